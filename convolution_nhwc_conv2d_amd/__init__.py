@@ -1,0 +1,269 @@
+"""Channels-last convolution forward on AMD MI355X (gfx950) -- Python binding.
+
+Thin ctypes marshalling over ``libcnhwc.so`` (declared in ``include/cnhwc.h``):
+torch supplies device memory and the stream; every step of the convolution runs
+in the library's HIP kernels.  There is no fallback: if the library is missing
+this import fails, and every library error raises :class:`CnhwcError`.
+
+    conv2d(x, w, stride, padding, dilation, *, algo, ws_limit, tile_batch, unfold_rows)
+    conv3d(x, w, stride, padding, dilation, *, algo, inner_algo, ws_limit, ...)
+    plan2d(...) / plan3d(...) -> Plan      (algorithm selection only; no GPU needed)
+
+Layouts: x [N,H,W,C] / [N,D,H,W,C]; w [O,KH,KW,C] / [O,KD,KH,KW,C];
+y [N,OH,OW,O] / [N,OD,OH,OW,O]; dtype float32, float16 or bfloat16 (x, w, y
+share it).
+
+``ws_limit`` is the working-set figure W the Winograd byte budget is derived
+from (budget = 3/4 W - input - output - transformed filter).  It defaults to the
+device's total memory, a fixed property of the device (never free memory).  For
+tests, the environment variables ``CNHWC_WS_LIMIT`` (bytes) and
+``CNHWC_TILE_BATCH`` are read here -- and only here -- and passed to the
+library as ordinary arguments (MLX PR "Bound winograd conv2d working set by
+tiling the batch", Testing: an injected budget and a forced tile size).
+"""
+import ctypes
+import os
+
+import torch  # noqa: F401  (load torch's HIP runtime first: the library then binds to it)
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libcnhwc.so")
+
+F32, F16, BF16 = 0, 1, 2
+_DTYPE_CODE = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}
+
+ALGOS = {"auto": 0, "winograd": 1, "implicit_gemm": 2, "unfold_gemm": 3, "small_kd": 4}
+ALGO_NAMES = {v: k for k, v in ALGOS.items()}
+
+STATUS = {0: "OK", 1: "INVALID_ARGUMENT", 2: "UNSUPPORTED", 3: "NOT_APPLICABLE", 4: "BUDGET",
+          5: "WORKSPACE_TOO_SMALL", 6: "PLAN_MISMATCH", 7: "HIP", 8: "INTERNAL"}
+
+
+class Desc(ctypes.Structure):
+    _fields_ = [("nd", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("n", ctypes.c_int64), ("d", ctypes.c_int64), ("h", ctypes.c_int64),
+                ("w", ctypes.c_int64), ("c", ctypes.c_int64), ("o", ctypes.c_int64),
+                ("kd", ctypes.c_int64), ("kh", ctypes.c_int64), ("kw", ctypes.c_int64),
+                ("stride", ctypes.c_int32 * 3), ("pad", ctypes.c_int32 * 3),
+                ("dil", ctypes.c_int32 * 3), ("groups", ctypes.c_int32)]
+
+
+class Opts(ctypes.Structure):
+    _fields_ = [("ws_limit_bytes", ctypes.c_uint64), ("force_algo", ctypes.c_int32),
+                ("force_inner_algo", ctypes.c_int32), ("force_tile_batch", ctypes.c_int64),
+                ("force_unfold_rows", ctypes.c_int64)]
+
+
+class Plan(ctypes.Structure):
+    _fields_ = [("algo", ctypes.c_int32), ("inner_algo", ctypes.c_int32),
+                ("out_d", ctypes.c_int64), ("out_h", ctypes.c_int64), ("out_w", ctypes.c_int64),
+                ("tile_batch", ctypes.c_int64), ("n_tiles", ctypes.c_int64),
+                ("tiles_per_image", ctypes.c_int64), ("unfold_rows", ctypes.c_int64),
+                ("n_chunks", ctypes.c_int64), ("own_bytes", ctypes.c_uint64),
+                ("budget_bytes", ctypes.c_uint64), ("scratch_per_element", ctypes.c_uint64),
+                ("workspace_bytes", ctypes.c_uint64), ("kernel_config", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("opts", Opts)]
+
+    @property
+    def algo_name(self):
+        return ALGO_NAMES[self.algo]
+
+    @property
+    def inner_algo_name(self):
+        return ALGO_NAMES[self.inner_algo]
+
+    def as_dict(self):
+        d = {f: getattr(self, f) for f, _ in self._fields_ if f not in ("opts", "reserved")}
+        d["algo"] = self.algo_name
+        d["inner_algo"] = self.inner_algo_name
+        d["opts"] = {f: getattr(self.opts, f) for f, _ in Opts._fields_}
+        return d
+
+    def __repr__(self):
+        return f"Plan({self.as_dict()})"
+
+
+class CnhwcError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        self.name = STATUS.get(status, str(status))
+        super().__init__(f"{where}: CNHWC_ERR_{self.name}")
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is not built; run `python -c 'import __graft_entry__ as g; g.build()'` "
+            "or `python convolution_nhwc_conv2d_amd/build.py` (needs hipcc for gfx950)")
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.POINTER
+    lib.cnhwc_abi_version.restype = ctypes.c_int
+    lib.cnhwc_status_string.restype = ctypes.c_char_p
+    lib.cnhwc_status_string.argtypes = [ctypes.c_int]
+    lib.cnhwc_conv_select.restype = ctypes.c_int
+    lib.cnhwc_conv_select.argtypes = [P(Desc), P(Opts), P(Plan)]
+    lib.cnhwc_winograd_tile_rule.restype = ctypes.c_int
+    lib.cnhwc_winograd_tile_rule.argtypes = [ctypes.c_uint64, ctypes.c_uint64, ctypes.c_uint64,
+                                             ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                             P(ctypes.c_int64), P(ctypes.c_uint64), P(ctypes.c_int32)]
+    for fn in (lib.cnhwc_conv2d_fwd, lib.cnhwc_conv3d_fwd):
+        fn.restype = ctypes.c_int
+        fn.argtypes = [P(Desc), P(Plan), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                       ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p]
+    if lib.cnhwc_abi_version() != 1:
+        raise ImportError("libcnhwc.so ABI version mismatch")
+    return lib
+
+
+lib = _load()
+
+EXPORTED = ("cnhwc_abi_version", "cnhwc_status_string", "cnhwc_conv_select",
+            "cnhwc_winograd_tile_rule", "cnhwc_conv2d_fwd", "cnhwc_conv3d_fwd")
+
+
+# ------------------------------------------------------------------ helpers
+
+def _tup(v, n):
+    if isinstance(v, int):
+        return (v,) * n
+    v = tuple(int(t) for t in v)
+    if len(v) != n:
+        raise ValueError(f"expected {n} values, got {v}")
+    return v
+
+
+def make_desc(x_shape, w_shape, stride=1, padding=0, dilation=1, dtype=torch.float32):
+    """Descriptor for a 2D (4-D shapes) or 3D (5-D shapes) channels-last conv."""
+    d = Desc()
+    if len(x_shape) == 4:
+        d.nd = 2
+        n, h, w, c = x_shape
+        o, kh, kw, c2 = w_shape
+        dd, kd = 1, 1
+        s, p, dl = (1,) + _tup(stride, 2), (0,) + _tup(padding, 2), (1,) + _tup(dilation, 2)
+    elif len(x_shape) == 5:
+        d.nd = 3
+        n, dd, h, w, c = x_shape
+        o, kd, kh, kw, c2 = w_shape
+        s, p, dl = _tup(stride, 3), _tup(padding, 3), _tup(dilation, 3)
+    else:
+        raise ValueError("x must be 4-D (NHWC) or 5-D (NDHWC)")
+    if c2 != c:
+        raise ValueError(f"channel mismatch: x has {c}, w has {c2}")
+    if dtype not in _DTYPE_CODE:
+        raise TypeError(f"unsupported dtype {dtype}")
+    d.dtype = _DTYPE_CODE[dtype]
+    d.n, d.d, d.h, d.w, d.c, d.o, d.kd, d.kh, d.kw = n, dd, h, w, c, o, kd, kh, kw
+    for i in range(3):
+        d.stride[i], d.pad[i], d.dil[i] = s[i], p[i], dl[i]
+    d.groups = 1
+    return d
+
+
+def default_ws_limit(device=None):
+    """W for the byte budget: CNHWC_WS_LIMIT if set, else the device's total memory."""
+    env = os.environ.get("CNHWC_WS_LIMIT")
+    if env:
+        return int(env)
+    if torch.cuda.is_available():
+        return int(torch.cuda.get_device_properties(device or 0).total_memory)
+    return 288 * 10**9  # MI355X HBM3E capacity, when planning without a device
+
+
+def make_opts(ws_limit=None, algo="auto", inner_algo="auto", tile_batch=None, unfold_rows=None,
+              device=None):
+    o = Opts()
+    o.ws_limit_bytes = int(ws_limit) if ws_limit is not None else default_ws_limit(device)
+    o.force_algo = ALGOS[algo]
+    o.force_inner_algo = ALGOS[inner_algo]
+    if tile_batch is None and os.environ.get("CNHWC_TILE_BATCH"):
+        tile_batch = int(os.environ["CNHWC_TILE_BATCH"])
+    o.force_tile_batch = int(tile_batch or 0)
+    o.force_unfold_rows = int(unfold_rows or 0)
+    return o
+
+
+def select(desc, opts):
+    """Run the library's planner; returns a Plan or raises CnhwcError."""
+    p = Plan()
+    st = lib.cnhwc_conv_select(ctypes.byref(desc), ctypes.byref(opts), ctypes.byref(p))
+    if st != 0:
+        raise CnhwcError(st, "cnhwc_conv_select")
+    return p
+
+
+def winograd_tile_rule(ws_limit, own_bytes, scratch_per_element, n, rows_per_element, force_tile=0):
+    """The Winograd batch-tiling rule alone: (tile_batch, budget_bytes, fallback)."""
+    t, b, f = ctypes.c_int64(), ctypes.c_uint64(), ctypes.c_int32()
+    st = lib.cnhwc_winograd_tile_rule(int(ws_limit), int(own_bytes), int(scratch_per_element), int(n),
+                                      int(rows_per_element), int(force_tile), ctypes.byref(t),
+                                      ctypes.byref(b), ctypes.byref(f))
+    if st != 0:
+        raise CnhwcError(st, "cnhwc_winograd_tile_rule")
+    return t.value, b.value, bool(f.value)
+
+
+def plan2d(x_shape, w_shape, stride=1, padding=0, dilation=1, dtype=torch.float32, **kw):
+    return select(make_desc(x_shape, w_shape, stride, padding, dilation, dtype), make_opts(**kw))
+
+
+def plan3d(x_shape, w_shape, stride=1, padding=0, dilation=1, dtype=torch.float32, **kw):
+    return select(make_desc(x_shape, w_shape, stride, padding, dilation, dtype), make_opts(**kw))
+
+
+def _check_tensor(t, name):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a GPU torch tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _run(fn, x, w, stride, padding, dilation, opts, out, workspace, plan):
+    _check_tensor(x, "x")
+    _check_tensor(w, "w")
+    if w.dtype != x.dtype or w.device != x.device:
+        raise TypeError("x and w must share dtype and device")
+    desc = make_desc(tuple(x.shape), tuple(w.shape), stride, padding, dilation, x.dtype)
+    if plan is None:
+        plan = select(desc, opts)
+    oshape = (x.shape[0],) + ((plan.out_d,) if desc.nd == 3 else ()) + (plan.out_h, plan.out_w, w.shape[0])
+    if out is None:
+        out = torch.empty(oshape, dtype=x.dtype, device=x.device)
+    else:
+        _check_tensor(out, "out")
+        if tuple(out.shape) != oshape or out.dtype != x.dtype:
+            raise ValueError("out has the wrong shape or dtype")
+    nbytes = int(plan.workspace_bytes)
+    if workspace is None and nbytes > 0:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=x.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    stream = torch.cuda.current_stream(x.device).cuda_stream
+    st = fn(ctypes.byref(desc), ctypes.byref(plan), x.data_ptr(), w.data_ptr(), out.data_ptr(),
+            ws_ptr, ws_len, stream)
+    if st != 0:
+        raise CnhwcError(st, fn.__name__)
+    return out
+
+
+def conv2d(x, w, stride=1, padding=0, dilation=1, *, algo="auto", ws_limit=None, tile_batch=None,
+           unfold_rows=None, out=None, workspace=None, plan=None):
+    """y[N,OH,OW,O] = channels-last conv2d of x[N,H,W,C] with w[O,KH,KW,C]."""
+    opts = make_opts(ws_limit, algo, "auto", tile_batch, unfold_rows, x.device if x.is_cuda else None)
+    return _run(lib.cnhwc_conv2d_fwd, x, w, stride, padding, dilation, opts, out, workspace, plan)
+
+
+def conv3d(x, w, stride=1, padding=0, dilation=1, *, algo="auto", inner_algo="auto", ws_limit=None,
+           tile_batch=None, unfold_rows=None, out=None, workspace=None, plan=None):
+    """y[N,OD,OH,OW,O] = channels-last conv3d of x[N,D,H,W,C] with w[O,KD,KH,KW,C]."""
+    opts = make_opts(ws_limit, algo, inner_algo, tile_batch, unfold_rows, x.device if x.is_cuda else None)
+    return _run(lib.cnhwc_conv3d_fwd, x, w, stride, padding, dilation, opts, out, workspace, plan)
+
+
+def direct_flops(x_shape, w_shape, plan):
+    """2*N*OD*OH*OW*O*C*KD*KH*KW: the metric's flop count (direct-equivalent)."""
+    o = w_shape[0]
+    k = 1
+    for v in w_shape[1:]:
+        k *= v
+    return 2 * x_shape[0] * plan.out_d * plan.out_h * plan.out_w * o * k

@@ -1,0 +1,220 @@
+// Forward entry points: argument and plan validation, then the launch
+// sequence of the planned algorithm on the caller's stream.  Nothing here
+// allocates, synchronises or falls back to another algorithm.
+//
+// Winograd (MLX PR "Bound winograd conv2d working set by tiling the batch",
+// Fix): filter transform once, then for each batch tile the input transform,
+// the 64 tile-position GEMMs and the output transform, all through the one
+// workspace.  Unfold (MLX PR "Use the explicit gemm for wide convs on neural
+// accelerators", Notes): per row chunk, unfold into the one buffer, then GEMM.
+// 3D (MLX PR "Decompose small kernel-depth 3D convs into 2D convs", Change):
+// per depth tap, a 2D conv on the frame view and the weight depth slice,
+// accumulated in fp32.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+
+#include "internal.hpp"
+
+namespace cnhwc {
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool overlaps(const void* a, uint64_t na, const void* b, uint64_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+cnhwc_status_t hip_status(int e) { return e == hipSuccess ? CNHWC_OK : CNHWC_ERR_HIP; }
+
+// One 2D conv (a full 2D call or one depth tap of a 3D call).
+//   x: [n][h][w][c] (dtype), w: rows of K = kh*kw*c elements at stride ldw,
+//   y: [n][oh][ow][o] (dtype), acc: fp32 rows of the same shape (epi != store).
+cnhwc_status_t run_2d(const cnhwc_conv_desc_t& d, const cnhwc_plan_t& p, int32_t algo,
+                      const void* x, const void* w, int64_t ldw, void* y, float* acc, int32_t epi,
+                      char* ws, void* stream) {
+  const uint64_t es = dtype_size(d.dtype);
+  const int64_t oh = p.out_h, ow = p.out_w;
+  const int64_t m_rows = d.n * oh * ow;
+  const int64_t k = d.kh * d.kw * d.c;
+
+  GemmParams g;
+  std::memset(&g, 0, sizeof(g));
+  g.dtype = d.dtype;
+  g.epi = epi;
+  g.config = p.kernel_config;
+  g.N = d.o;
+  g.h = d.h;
+  g.w = d.w;
+  g.c = d.c;
+  g.oh = oh;
+  g.ow = ow;
+  g.kh = d.kh;
+  g.kw = d.kw;
+  g.sh = d.stride[1];
+  g.sw = d.stride[2];
+  g.ph = d.pad[1];
+  g.pw = d.pad[2];
+  g.dh = d.dil[1];
+  g.dw = d.dil[2];
+  g.batch = 1;
+
+  if (algo == CNHWC_ALGO_IMPLICIT_GEMM) {
+    g.a_mode = kAImplicit;
+    g.M = m_rows;
+    g.K = k;
+    g.a = x;
+    g.b = w;
+    g.ldb = ldw;
+    g.out = y;
+    g.ldc = d.o;
+    g.acc = acc;
+    return hip_status(gemm_launch(g, stream));
+  }
+
+  if (algo == CNHWC_ALGO_UNFOLD_GEMM) {
+    const int64_t kp = unfold_kp(k, d.dtype);
+    const int64_t rows = p.unfold_rows;
+    for (int64_t m0 = 0; m0 < m_rows; m0 += rows) {
+      const int64_t r = m0 + rows <= m_rows ? rows : m_rows - m0;
+      int e = unfold_launch(d.dtype, x, d.h, d.w, d.c, oh, ow, d.kh, d.kw, d.stride[1],
+                            d.stride[2], d.pad[1], d.pad[2], d.dil[1], d.dil[2], m0, r, kp, ws,
+                            stream);
+      if (e != hipSuccess) return CNHWC_ERR_HIP;
+      g.a_mode = kADense;
+      g.M = r;
+      g.K = k;
+      g.a = ws;
+      g.lda = kp;
+      g.b = w;
+      g.ldb = ldw;
+      g.out = static_cast<char*>(y) + uint64_t(m0) * d.o * es;
+      g.ldc = d.o;
+      g.acc = acc ? acc + m0 * d.o : nullptr;
+      e = gemm_launch(g, stream);
+      if (e != hipSuccess) return CNHWC_ERR_HIP;
+    }
+    return CNHWC_OK;
+  }
+
+  if (algo == CNHWC_ALGO_WINOGRAD) {
+    const WinoLayout L = wino_layout(d, oh, ow, p.tile_batch);
+    float* U = reinterpret_cast<float*>(ws + L.off_u);
+    float* V = reinterpret_cast<float*>(ws + L.off_v);
+    float* Mt = reinterpret_cast<float*>(ws + L.off_m);
+    int e = wino_filter_launch(d.dtype, w, ldw, d.o, d.c, L.cs, U, stream);
+    if (e != hipSuccess) return CNHWC_ERR_HIP;
+    const uint64_t x_elem = uint64_t(d.h) * d.w * d.c * es;  // bytes of one image
+    const uint64_t y_elem = uint64_t(oh) * ow * d.o;         // elements of one output image
+    for (int64_t n0 = 0; n0 < d.n; n0 += p.tile_batch) {
+      const int64_t nb = n0 + p.tile_batch <= d.n ? p.tile_batch : d.n - n0;
+      e = wino_input_launch(d.dtype, static_cast<const char*>(x) + n0 * x_elem, nb, d.h, d.w, d.c,
+                            L.cs, d.pad[1], d.pad[2], L.tiles_h, L.tiles_w, V, int64_t(L.v_plane),
+                            stream);
+      if (e != hipSuccess) return CNHWC_ERR_HIP;
+      GemmParams q;
+      std::memset(&q, 0, sizeof(q));
+      q.dtype = CNHWC_F32;
+      q.a_mode = kADense;
+      q.epi = kEpiStore;
+      q.config = p.kernel_config;
+      q.M = nb * L.t;
+      q.N = d.o;
+      q.K = L.cs;
+      q.a = V;
+      q.lda = L.cs;
+      q.b = U;
+      q.ldb = L.cs;
+      q.out = Mt;
+      q.ldc = d.o;
+      q.batch = kWinoP;
+      q.stride_a = int64_t(L.v_plane);
+      q.stride_b = d.o * L.cs;
+      q.stride_out = int64_t(L.m_plane);
+      e = gemm_launch(q, stream);
+      if (e != hipSuccess) return CNHWC_ERR_HIP;
+      e = wino_output_launch(d.dtype, Mt, int64_t(L.m_plane), nb, oh, ow, d.o, L.tiles_h,
+                             L.tiles_w, static_cast<char*>(y) + n0 * y_elem * es,
+                             acc ? acc + n0 * y_elem : nullptr, epi, stream);
+      if (e != hipSuccess) return CNHWC_ERR_HIP;
+    }
+    return CNHWC_OK;
+  }
+  return CNHWC_ERR_INTERNAL;
+}
+
+cnhwc_status_t validate(const cnhwc_conv_desc_t* desc, const cnhwc_plan_t* plan, int nd,
+                        const void* x, const void* w, const void* y, const void* ws,
+                        uint64_t ws_bytes) {
+  if (!desc || !plan) return CNHWC_ERR_INVALID_ARGUMENT;
+  if (desc->nd != nd) return CNHWC_ERR_INVALID_ARGUMENT;
+  cnhwc_plan_t ref;
+  const cnhwc_status_t st = select_impl(desc, &plan->opts, &ref);
+  if (st != CNHWC_OK) return st;
+  if (!plan_equal(ref, *plan)) return CNHWC_ERR_PLAN_MISMATCH;
+  if (!x || !w || !y || !aligned16(x) || !aligned16(w) || !aligned16(y))
+    return CNHWC_ERR_INVALID_ARGUMENT;
+  const uint64_t es = dtype_size(desc->dtype);
+  const uint64_t xb = uint64_t(desc->n) * desc->d * desc->h * desc->w * desc->c * es;
+  const uint64_t yb = uint64_t(desc->n) * plan->out_d * plan->out_h * plan->out_w * desc->o * es;
+  if (overlaps(x, xb, y, yb)) return CNHWC_ERR_INVALID_ARGUMENT;
+  if (plan->workspace_bytes > 0) {
+    if (ws_bytes < plan->workspace_bytes) return CNHWC_ERR_WORKSPACE_TOO_SMALL;
+    if (!ws || !aligned16(ws)) return CNHWC_ERR_INVALID_ARGUMENT;
+    if (overlaps(ws, plan->workspace_bytes, y, yb) || overlaps(ws, plan->workspace_bytes, x, xb))
+      return CNHWC_ERR_INVALID_ARGUMENT;
+  }
+  return CNHWC_OK;
+}
+
+}  // namespace
+}  // namespace cnhwc
+
+extern "C" {
+
+cnhwc_status_t cnhwc_conv2d_fwd(const cnhwc_conv_desc_t* desc, const cnhwc_plan_t* plan,
+                                const void* x, const void* w, void* y, void* workspace,
+                                uint64_t workspace_bytes, void* hip_stream) {
+  using namespace cnhwc;
+  const cnhwc_status_t st = validate(desc, plan, 2, x, w, y, workspace, workspace_bytes);
+  if (st != CNHWC_OK) return st;
+  return run_2d(*desc, *plan, plan->algo, x, w, desc->kh * desc->kw * desc->c, y, nullptr,
+                kEpiStore, static_cast<char*>(workspace), hip_stream);
+}
+
+cnhwc_status_t cnhwc_conv3d_fwd(const cnhwc_conv_desc_t* desc, const cnhwc_plan_t* plan,
+                                const void* x, const void* w, void* y, void* workspace,
+                                uint64_t workspace_bytes, void* hip_stream) {
+  using namespace cnhwc;
+  const cnhwc_status_t st = validate(desc, plan, 3, x, w, y, workspace, workspace_bytes);
+  if (st != CNHWC_OK) return st;
+  if (plan->algo != CNHWC_ALGO_SMALL_KD) return CNHWC_ERR_INTERNAL;
+  const cnhwc_conv_desc_t& d = *desc;
+  const int64_t od = plan->out_d;
+  const cnhwc_conv_desc_t f = frame_desc(d, od);
+  const uint64_t es = dtype_size(d.dtype);
+  const uint64_t acc_bytes =
+      d.dtype == CNHWC_F32 ? 0 : align_up(uint64_t(od) * plan->out_h * plan->out_w * d.o * 4, 256);
+  char* ws = static_cast<char*>(workspace);
+  float* acc = d.dtype == CNHWC_F32 ? static_cast<float*>(y) : reinterpret_cast<float*>(ws);
+  char* inner_ws = ws ? ws + acc_bytes : nullptr;
+  const uint64_t frame_bytes = uint64_t(d.h) * d.w * d.c * es;
+  const int64_t k2 = d.kh * d.kw * d.c;
+  const int64_t ldw = d.kd * k2;  // weight [O][KD][KH][KW][C]: row stride of one depth slice
+  for (int64_t t = 0; t < d.kd; ++t) {
+    int32_t epi;
+    if (d.kd == 1) epi = kEpiStore;
+    else if (d.dtype == CNHWC_F32) epi = t == 0 ? kEpiStore : kEpiAccMid;
+    else epi = t == 0 ? kEpiAccFirst : (t == d.kd - 1 ? kEpiAccLast : kEpiAccMid);
+    const void* xt = static_cast<const char*>(x) + uint64_t(t) * frame_bytes;
+    const void* wt = static_cast<const char*>(w) + uint64_t(t) * k2 * es;
+    const cnhwc_status_t s =
+        run_2d(f, *plan, plan->inner_algo, xt, wt, ldw, y, acc, epi, inner_ws, hip_stream);
+    if (s != CNHWC_OK) return s;
+  }
+  return CNHWC_OK;
+}
+
+}  // extern "C"

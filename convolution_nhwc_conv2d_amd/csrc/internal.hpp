@@ -1,0 +1,129 @@
+// Internal declarations shared by the planner (select.cpp), the launch
+// sequencing (api.cpp) and the gfx950 kernels (*.hip).
+#pragma once
+#include <cstdint>
+#include <cstddef>
+
+#include "../../include/cnhwc.h"
+
+namespace cnhwc {
+
+inline uint64_t dtype_size(int dt) { return dt == CNHWC_F32 ? 4u : 2u; }
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline uint64_t align_up(uint64_t v, uint64_t a) { return (v + a - 1) / a * a; }
+
+// Winograd F(6x6,3x3): 8x8 input tiles at stride 6, 64 tile positions.
+constexpr int kWinoM = 6;
+constexpr int kWinoT = 8;
+constexpr int kWinoP = 64;
+
+// Channel stride of the transformed input/filter rows: C rounded up to a
+// multiple of 8 so every row is 32-byte aligned (pad channels are zero).
+inline int64_t wino_cs(int64_t c) { return (c + 7) / 8 * 8; }
+
+// ------------------------------------------------------------------ GEMM
+
+// GEMM tile configurations.  Each id fixes the tile shape, the MFMA form and
+// the K order, so the bits of an output row depend on (config, K, data) only,
+// never on the number of rows or on which launch the row is in.
+enum GemmConfig : int32_t {
+  kCfgNone = 0,
+  // fp32 operands, v_mfma_f32_32x32x2f32, BM=128, BK=32
+  kCfgF32_N32 = 1,
+  kCfgF32_N64 = 2,
+  kCfgF32_N96 = 3,
+  kCfgF32_N128 = 4,
+  // fp16/bf16 operands, v_mfma_f32_32x32x16_{f16,bf16}, BM=128, BK=64
+  kCfgH_N64 = 10,
+  kCfgH_N128 = 11,
+};
+
+// Pick the tile configuration from the element type and the output-channel
+// count (and nothing that depends on the batch or on tiling).
+int32_t pick_gemm_config(int dtype, int64_t n_cols);
+
+// Epilogue: how a GEMM / output-transform result r is written.
+enum EpiMode : int32_t {
+  kEpiStore = 0,     // y = round(r)
+  kEpiAccFirst = 1,  // acc = r                (fp32)
+  kEpiAccMid = 2,    // acc = acc + r          (fp32)
+  kEpiAccLast = 3,   // y = round(acc + r)
+};
+
+// A-operand source.
+enum AMode : int32_t {
+  kADense = 0,      // A[m][k] = a[m*lda + k]      (lda, K multiples of 16 B)
+  kAImplicit = 1,   // A[m][k] gathered from an NHWC image, k = (kh*KW + kw)*C + c
+};
+
+struct GemmParams {
+  int32_t dtype;         // element type of A, B and the output
+  int32_t a_mode;
+  int32_t epi;
+  int32_t config;
+  int64_t M, N, K;       // C[M x N] = A[M x K] * B[N x K]^T
+  const void* a;
+  int64_t lda;           // dense A row stride (elements)
+  // implicit-A geometry (input image [n][h][w][c])
+  int64_t h, w, c, oh, ow, kh, kw;
+  int32_t sh, sw, ph, pw, dh, dw;
+  const void* b;
+  int64_t ldb;           // B row stride (elements)
+  void* out;             // output rows, row stride ldc (elements of dtype)
+  int64_t ldc;
+  float* acc;            // fp32 accumulator rows (row stride ldc) for kEpiAcc*
+  // batched GEMM (Winograd tile positions): element offsets per batch index
+  int64_t batch;
+  int64_t stride_a, stride_b, stride_out;
+};
+
+int gemm_launch(const GemmParams& p, void* stream);  // returns hipError_t
+
+// ------------------------------------------------------------ Winograd
+
+// U[p][o][c] = (G g G^T)_p, g = w[o*ldo + (kh*3 + kw)*C + c]; zero for c >= C.
+int wino_filter_launch(int dtype, const void* w, int64_t ldo, int64_t o, int64_t c,
+                       int64_t cs, float* u, void* stream);
+
+// V[p][r][c] = (B^T d B)_p for tile r of nb images [nb][h][w][c] (8x8 tiles at
+// stride 6 starting at (-ph, -pw), zero outside); plane stride `plane`.
+int wino_input_launch(int dtype, const void* x, int64_t nb, int64_t h, int64_t w, int64_t c,
+                      int64_t cs, int32_t ph, int32_t pw, int64_t tiles_h, int64_t tiles_w,
+                      float* v, int64_t plane, void* stream);
+
+// Y = A^T M A per tile and output channel, cropped to [oh, ow]; epilogue mode.
+int wino_output_launch(int dtype, const float* m, int64_t plane, int64_t nb, int64_t oh,
+                       int64_t ow, int64_t o, int64_t tiles_h, int64_t tiles_w, void* y,
+                       float* acc, int32_t epi, void* stream);
+
+// ------------------------------------------------------------- Unfold
+
+// buf[r][k] for output rows m0..m0+rows-1 (k = (kh*KW + kw)*C + c, zero outside
+// the image and for k >= K), row stride kp elements.
+int unfold_launch(int dtype, const void* x, int64_t h, int64_t w, int64_t c, int64_t oh,
+                  int64_t ow, int64_t kh, int64_t kw, int32_t sh, int32_t sw, int32_t ph,
+                  int32_t pw, int32_t dh, int32_t dw, int64_t m0, int64_t rows, int64_t kp,
+                  void* buf, void* stream);
+
+// Unfold row stride: K rounded up to 16 bytes worth of elements.
+inline int64_t unfold_kp(int64_t k, int dtype) {
+  const int64_t v = 16 / (int64_t)dtype_size(dtype);
+  return (k + v - 1) / v * v;
+}
+
+// ------------------------------------------------------------ planner
+
+// Winograd workspace layout for a 2D conv and a tile size.
+struct WinoLayout {
+  int64_t tiles_h, tiles_w, t, cs;
+  uint64_t u_bytes, v_plane, m_plane;  // plane strides in elements
+  uint64_t off_u, off_v, off_m, total;
+};
+WinoLayout wino_layout(const cnhwc_conv_desc_t& d2, int64_t oh, int64_t ow, int64_t tile_batch);
+
+cnhwc_status_t select_impl(const cnhwc_conv_desc_t* desc, const cnhwc_select_opts_t* opts,
+                           cnhwc_plan_t* plan);
+bool plan_equal(const cnhwc_plan_t& a, const cnhwc_plan_t& b);
+cnhwc_conv_desc_t frame_desc(const cnhwc_conv_desc_t& d3, int64_t od);  // 3D -> per-tap 2D
+
+}  // namespace cnhwc

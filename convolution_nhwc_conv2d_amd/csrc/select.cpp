@@ -1,0 +1,318 @@
+// Algorithm selection and memory planning: a pure host function of the
+// convolution descriptor and the selection options.  No device call, no
+// allocation, no environment read, no dependence on free memory.
+//
+// Sources (MLX pull requests):
+//  - "Bound winograd conv2d working set by tiling the batch", Problem and Fix:
+//    the Winograd gate (C%32, O%32, C+O >= 256 for 3x3 stride 1), the budget
+//    3/4 of the working-set figure minus the conv's own tensors (input, output,
+//    transformed filter), batch tiles sized from it with one reused scratch
+//    set, the fallback to implicit GEMM when no element fits or tiles carry
+//    too few GEMM rows, and unchanged work when the whole batch fits.  Testing:
+//    the budget can be injected and a tile size forced (capped by the budget).
+//  - "Use the explicit gemm for wide convs on neural accelerators", intro and
+//    Notes: unfold+GEMM for wide output channels in half precision, placed
+//    after the Winograd branch; the unfold tiled against a fixed buffer cap.
+//    The closing review rejects dispatch on live memory, so none is used.
+//  - "Decompose small kernel-depth 3D convs into 2D convs", Change: the guard
+//    (idil 1, groups 1, N 1, KD <= 7, depth stride 1, dilation 1, depth pad 0,
+//    channels multiple of 16) and the per-tap 2D decomposition.
+#include <cstring>
+#include <algorithm>
+
+#include "internal.hpp"
+
+namespace cnhwc {
+
+namespace {
+
+int64_t out_extent(int64_t in, int64_t k, int64_t s, int64_t p, int64_t d) {
+  const int64_t span = in + 2 * p - d * (k - 1) - 1;
+  return span < 0 ? 0 : span / s + 1;
+}
+
+bool valid_dtype(int32_t dt) { return dt == CNHWC_F32 || dt == CNHWC_F16 || dt == CNHWC_BF16; }
+
+// floor(3/4 * w) without overflow.
+uint64_t three_quarters(uint64_t w) { return (w / 4) * 3 + ((w % 4) * 3) / 4; }
+
+// Bound on element counts so every byte size below fits comfortably in 63 bits.
+constexpr int64_t kMaxDim = int64_t(1) << 31;
+constexpr uint64_t kMaxElems = uint64_t(1) << 56;
+
+cnhwc_status_t check_desc(const cnhwc_conv_desc_t& d, int64_t out[3]) {
+  if (d.nd != 2 && d.nd != 3) return CNHWC_ERR_INVALID_ARGUMENT;
+  if (!valid_dtype(d.dtype)) return CNHWC_ERR_INVALID_ARGUMENT;
+  const int64_t dims[9] = {d.n, d.d, d.h, d.w, d.c, d.o, d.kd, d.kh, d.kw};
+  for (int64_t v : dims)
+    if (v < 1 || v > kMaxDim) return CNHWC_ERR_INVALID_ARGUMENT;
+  for (int i = 0; i < 3; ++i) {
+    if (d.stride[i] < 1 || d.pad[i] < 0 || d.dil[i] < 1) return CNHWC_ERR_INVALID_ARGUMENT;
+    if (d.stride[i] > (1 << 20) || d.pad[i] > (1 << 20) || d.dil[i] > (1 << 20))
+      return CNHWC_ERR_INVALID_ARGUMENT;
+  }
+  if (d.groups != 1) return d.groups < 1 ? CNHWC_ERR_INVALID_ARGUMENT : CNHWC_ERR_UNSUPPORTED;
+  if (d.nd == 2 && (d.d != 1 || d.kd != 1 || d.stride[0] != 1 || d.pad[0] != 0 || d.dil[0] != 1))
+    return CNHWC_ERR_INVALID_ARGUMENT;
+  out[0] = out_extent(d.d, d.kd, d.stride[0], d.pad[0], d.dil[0]);
+  out[1] = out_extent(d.h, d.kh, d.stride[1], d.pad[1], d.dil[1]);
+  out[2] = out_extent(d.w, d.kw, d.stride[2], d.pad[2], d.dil[2]);
+  if (out[0] < 1 || out[1] < 1 || out[2] < 1) return CNHWC_ERR_INVALID_ARGUMENT;
+  const double ex = double(d.n) * d.d * d.h * d.w * d.c;
+  const double ey = double(d.n) * out[0] * out[1] * out[2] * d.o;
+  const double ew = double(d.o) * d.kd * d.kh * d.kw * d.c;
+  if (ex > double(kMaxElems) || ey > double(kMaxElems) || ew > double(kMaxElems))
+    return CNHWC_ERR_INVALID_ARGUMENT;
+  return CNHWC_OK;
+}
+
+bool winograd_geometry(const cnhwc_conv_desc_t& d) {
+  return d.nd == 2 && d.kh == 3 && d.kw == 3 && d.stride[1] == 1 && d.stride[2] == 1 &&
+         d.dil[1] == 1 && d.dil[2] == 1;
+}
+
+// The channel/dtype gate AUTO applies on top of the geometry.  The pages' gate
+// is C%32, O%32, C+O >= 256; on MI355X Winograd is only taken automatically
+// for fp32 (fp16/bf16 implicit GEMM runs on the much faster half-precision
+// matrix cores; the Winograd transforms keep fp32 tensors).
+bool winograd_auto_gate(const cnhwc_conv_desc_t& d) {
+  return winograd_geometry(d) && d.c % 32 == 0 && d.o % 32 == 0 && d.c + d.o >= 256 &&
+         d.dtype == CNHWC_F32;
+}
+
+void tile_rule(uint64_t ws_limit, uint64_t own, uint64_t scratch, int64_t n, int64_t rows,
+               int64_t force_tile, int64_t* tile, uint64_t* budget, int32_t* fallback) {
+  const uint64_t q = three_quarters(ws_limit);
+  const uint64_t b = q > own ? q - own : 0;
+  const uint64_t fit = scratch ? b / scratch : 0;
+  int64_t t = fit > uint64_t(n) ? n : int64_t(fit);
+  if (force_tile > 0) t = std::min<int64_t>(t, force_tile);
+  *tile = t;
+  *budget = b;
+  *fallback = (t < 1) || (force_tile <= 0 && t < n && t * rows < CNHWC_MIN_TILE_ROWS);
+}
+
+cnhwc_status_t select_2d(const cnhwc_conv_desc_t& d, const int64_t out[3],
+                         const cnhwc_select_opts_t& o, int32_t force, cnhwc_plan_t* p) {
+  const uint64_t es = dtype_size(d.dtype);
+  const int64_t m_rows = d.n * out[1] * out[2];
+  const int64_t k = d.kh * d.kw * d.c;
+  p->out_d = 1;
+  p->out_h = out[1];
+  p->out_w = out[2];
+
+  if (force != CNHWC_ALGO_AUTO && force != CNHWC_ALGO_WINOGRAD &&
+      force != CNHWC_ALGO_IMPLICIT_GEMM && force != CNHWC_ALGO_UNFOLD_GEMM)
+    return force == CNHWC_ALGO_SMALL_KD ? CNHWC_ERR_NOT_APPLICABLE : CNHWC_ERR_INVALID_ARGUMENT;
+
+  // 1. Winograd (gate + budget), or forced.
+  const bool try_wino = force == CNHWC_ALGO_WINOGRAD ||
+                        (force == CNHWC_ALGO_AUTO && winograd_auto_gate(d));
+  if (force == CNHWC_ALGO_WINOGRAD && !winograd_geometry(d)) return CNHWC_ERR_NOT_APPLICABLE;
+  if (try_wino) {
+    const WinoLayout one = wino_layout(d, out[1], out[2], 1);
+    const uint64_t own = uint64_t(d.n) * d.h * d.w * d.c * es +
+                         uint64_t(m_rows) * d.o * es + one.u_bytes;
+    const uint64_t scratch = uint64_t(kWinoP) * one.t * (one.cs + d.o) * 4;  // V + M of one element
+    int64_t tb;
+    uint64_t budget;
+    int32_t fb;
+    tile_rule(o.ws_limit_bytes, own, scratch, d.n, one.t, o.force_tile_batch, &tb, &budget, &fb);
+    if (force == CNHWC_ALGO_WINOGRAD && tb < 1) return CNHWC_ERR_BUDGET;
+    if (force == CNHWC_ALGO_WINOGRAD || !fb) {
+      const WinoLayout lay = wino_layout(d, out[1], out[2], tb);
+      p->algo = p->inner_algo = CNHWC_ALGO_WINOGRAD;
+      p->tile_batch = tb;
+      p->n_tiles = ceil_div(d.n, tb);
+      p->tiles_per_image = lay.t;
+      p->own_bytes = own;
+      p->budget_bytes = budget;
+      p->scratch_per_element = scratch;
+      p->workspace_bytes = lay.total;
+      p->kernel_config = pick_gemm_config(CNHWC_F32, d.o);
+      return CNHWC_OK;
+    }
+  }
+
+  // 2. Unfold + GEMM for wide half-precision convs, or forced.
+  if (force == CNHWC_ALGO_UNFOLD_GEMM ||
+      (force == CNHWC_ALGO_AUTO && d.dtype != CNHWC_F32 && d.o >= CNHWC_UNFOLD_MIN_COUT)) {
+    const int64_t kp = unfold_kp(k, d.dtype);
+    int64_t rows = o.force_unfold_rows > 0
+                       ? o.force_unfold_rows
+                       : int64_t(CNHWC_UNFOLD_CAP_BYTES / (uint64_t(kp) * es));
+    rows = std::max<int64_t>(1, std::min<int64_t>(rows, m_rows));
+    p->algo = p->inner_algo = CNHWC_ALGO_UNFOLD_GEMM;
+    p->unfold_rows = rows;
+    p->n_chunks = ceil_div(m_rows, rows);
+    p->workspace_bytes = align_up(uint64_t(rows) * kp * es, 256);
+    p->kernel_config = pick_gemm_config(d.dtype, d.o);
+    return CNHWC_OK;
+  }
+
+  // 3. Implicit GEMM (scratch-free).
+  p->algo = p->inner_algo = CNHWC_ALGO_IMPLICIT_GEMM;
+  p->workspace_bytes = 0;
+  p->kernel_config = pick_gemm_config(d.dtype, d.o);
+  return CNHWC_OK;
+}
+
+cnhwc_status_t select_3d(const cnhwc_conv_desc_t& d, const int64_t out[3],
+                         const cnhwc_select_opts_t& o, cnhwc_plan_t* p) {
+  const bool forced = o.force_algo == CNHWC_ALGO_SMALL_KD;
+  if (o.force_algo != CNHWC_ALGO_AUTO && !forced) return CNHWC_ERR_NOT_APPLICABLE;
+  // Structural requirements of the decomposition itself.
+  const bool structural = d.n == 1 && d.stride[0] == 1 && d.dil[0] == 1 && d.pad[0] == 0;
+  // AUTO guard: also KD <= 7, dilation 1 everywhere, channels multiple of 16.
+  const bool guard = structural && d.kd <= 7 && d.dil[1] == 1 && d.dil[2] == 1 &&
+                     d.c % 16 == 0 && d.o % 16 == 0;
+  if (forced ? !structural : !guard)
+    return forced ? CNHWC_ERR_NOT_APPLICABLE : CNHWC_ERR_UNSUPPORTED;
+  const cnhwc_conv_desc_t f = frame_desc(d, out[0]);
+  int64_t fo[3];
+  cnhwc_status_t st = check_desc(f, fo);
+  if (st != CNHWC_OK) return st;
+  cnhwc_plan_t inner;
+  std::memset(&inner, 0, sizeof(inner));
+  st = select_2d(f, fo, o, o.force_inner_algo, &inner);
+  if (st != CNHWC_OK) return st;
+  *p = inner;
+  p->algo = CNHWC_ALGO_SMALL_KD;
+  p->inner_algo = inner.algo;
+  p->out_d = out[0];
+  const uint64_t acc = d.dtype == CNHWC_F32
+                           ? 0
+                           : align_up(uint64_t(out[0]) * out[1] * out[2] * d.o * 4, 256);
+  p->workspace_bytes = acc + inner.workspace_bytes;
+  return CNHWC_OK;
+}
+
+}  // namespace
+
+WinoLayout wino_layout(const cnhwc_conv_desc_t& d, int64_t oh, int64_t ow, int64_t tb) {
+  WinoLayout l{};
+  l.tiles_h = ceil_div(oh, kWinoM);
+  l.tiles_w = ceil_div(ow, kWinoM);
+  l.t = l.tiles_h * l.tiles_w;
+  l.cs = wino_cs(d.c);
+  const uint64_t rows = uint64_t(tb) * l.t;
+  l.u_bytes = uint64_t(kWinoP) * d.o * l.cs * 4;
+  l.v_plane = rows * l.cs;
+  l.m_plane = rows * d.o;
+  l.off_u = 0;
+  l.off_v = align_up(l.u_bytes, 256);
+  l.off_m = l.off_v + align_up(kWinoP * l.v_plane * 4, 256);
+  l.total = l.off_m + align_up(kWinoP * l.m_plane * 4, 256);
+  return l;
+}
+
+cnhwc_conv_desc_t frame_desc(const cnhwc_conv_desc_t& d3, int64_t od) {
+  cnhwc_conv_desc_t f = d3;
+  f.nd = 2;
+  f.n = od;
+  f.d = 1;
+  f.kd = 1;
+  f.stride[0] = 1;
+  f.pad[0] = 0;
+  f.dil[0] = 1;
+  return f;
+}
+
+int32_t pick_gemm_config(int dtype, int64_t n_cols) {
+  if (dtype == CNHWC_F32) {
+    if (n_cols <= 32) return kCfgF32_N32;
+    if (n_cols <= 64) return kCfgF32_N64;
+    // least padding waste over {128, 96, 64}; ties go to the wider tile
+    const int64_t cand[3] = {128, 96, 64};
+    const int32_t ids[3] = {kCfgF32_N128, kCfgF32_N96, kCfgF32_N64};
+    int best = 0;
+    int64_t best_waste = ceil_div(n_cols, cand[0]) * cand[0] - n_cols;
+    for (int i = 1; i < 3; ++i) {
+      const int64_t waste = ceil_div(n_cols, cand[i]) * cand[i] - n_cols;
+      if (waste < best_waste) { best = i; best_waste = waste; }
+    }
+    return ids[best];
+  }
+  return n_cols <= 64 ? kCfgH_N64 : kCfgH_N128;
+}
+
+bool plan_equal(const cnhwc_plan_t& a, const cnhwc_plan_t& b) {
+  return a.algo == b.algo && a.inner_algo == b.inner_algo && a.out_d == b.out_d &&
+         a.out_h == b.out_h && a.out_w == b.out_w && a.tile_batch == b.tile_batch &&
+         a.n_tiles == b.n_tiles && a.tiles_per_image == b.tiles_per_image &&
+         a.unfold_rows == b.unfold_rows && a.n_chunks == b.n_chunks &&
+         a.own_bytes == b.own_bytes && a.budget_bytes == b.budget_bytes &&
+         a.scratch_per_element == b.scratch_per_element &&
+         a.workspace_bytes == b.workspace_bytes && a.kernel_config == b.kernel_config &&
+         a.opts.ws_limit_bytes == b.opts.ws_limit_bytes &&
+         a.opts.force_algo == b.opts.force_algo &&
+         a.opts.force_inner_algo == b.opts.force_inner_algo &&
+         a.opts.force_tile_batch == b.opts.force_tile_batch &&
+         a.opts.force_unfold_rows == b.opts.force_unfold_rows;
+}
+
+cnhwc_status_t select_impl(const cnhwc_conv_desc_t* desc, const cnhwc_select_opts_t* opts,
+                           cnhwc_plan_t* plan) {
+  if (!desc || !opts || !plan) return CNHWC_ERR_INVALID_ARGUMENT;
+  if (opts->ws_limit_bytes == 0 || opts->force_tile_batch < 0 || opts->force_unfold_rows < 0)
+    return CNHWC_ERR_INVALID_ARGUMENT;
+  if (opts->force_algo < CNHWC_ALGO_AUTO || opts->force_algo > CNHWC_ALGO_SMALL_KD ||
+      opts->force_inner_algo < CNHWC_ALGO_AUTO || opts->force_inner_algo > CNHWC_ALGO_UNFOLD_GEMM)
+    return CNHWC_ERR_INVALID_ARGUMENT;
+  int64_t out[3];
+  cnhwc_status_t st = check_desc(*desc, out);
+  if (st != CNHWC_OK) return st;
+  cnhwc_plan_t p;
+  std::memset(&p, 0, sizeof(p));
+  if (desc->nd == 2) {
+    if (opts->force_inner_algo != CNHWC_ALGO_AUTO) return CNHWC_ERR_INVALID_ARGUMENT;
+    st = select_2d(*desc, out, *opts, opts->force_algo, &p);
+  } else {
+    st = select_3d(*desc, out, *opts, &p);
+  }
+  if (st != CNHWC_OK) return st;
+  p.opts = *opts;
+  *plan = p;
+  return CNHWC_OK;
+}
+
+}  // namespace cnhwc
+
+extern "C" {
+
+int cnhwc_abi_version(void) { return CNHWC_ABI_VERSION; }
+
+const char* cnhwc_status_string(cnhwc_status_t s) {
+  switch (s) {
+    case CNHWC_OK: return "ok";
+    case CNHWC_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case CNHWC_ERR_UNSUPPORTED: return "unsupported convolution";
+    case CNHWC_ERR_NOT_APPLICABLE: return "forced algorithm not applicable";
+    case CNHWC_ERR_BUDGET: return "forced Winograd does not fit the byte budget";
+    case CNHWC_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case CNHWC_ERR_PLAN_MISMATCH: return "plan does not match the descriptor";
+    case CNHWC_ERR_HIP: return "HIP launch error";
+    case CNHWC_ERR_INTERNAL: return "internal error";
+  }
+  return "unknown status";
+}
+
+cnhwc_status_t cnhwc_conv_select(const cnhwc_conv_desc_t* desc, const cnhwc_select_opts_t* opts,
+                                 cnhwc_plan_t* plan) {
+  return cnhwc::select_impl(desc, opts, plan);
+}
+
+cnhwc_status_t cnhwc_winograd_tile_rule(uint64_t ws_limit, uint64_t own_bytes,
+                                        uint64_t scratch_per_element, int64_t n,
+                                        int64_t rows_per_element, int64_t force_tile,
+                                        int64_t* tile_batch, uint64_t* budget_bytes,
+                                        int32_t* fallback) {
+  if (!tile_batch || !budget_bytes || !fallback || n < 1 || rows_per_element < 1 ||
+      scratch_per_element == 0 || force_tile < 0)
+    return CNHWC_ERR_INVALID_ARGUMENT;
+  cnhwc::tile_rule(ws_limit, own_bytes, scratch_per_element, n, rows_per_element, force_tile,
+                   tile_batch, budget_bytes, fallback);
+  return CNHWC_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,208 @@
+/*
+ * cnhwc.h -- C ABI of the channels-last convolution forward library for AMD
+ * MI355X (gfx950).
+ *
+ * The operations are the ones three MLX pull requests discuss for Metal; this
+ * library computes the same things with its own HIP kernels:
+ *
+ *   [tiling page]   MLX PR "Bound winograd conv2d working set by tiling the
+ *                   batch" -- sections Problem, Fix, Testing and the review
+ *                   comments (M4 Pro / M5 Max verification).
+ *   [explicit page] MLX PR "Use the explicit gemm for wide convs on neural
+ *                   accelerators" -- intro tables, Verified, Notes, the ResNet-50
+ *                   and memory follow-ups.
+ *   [3D page]       MLX PR "Decompose small kernel-depth 3D convs into 2D convs"
+ *                   -- sections Problem, Change, Results, Tests, Open questions.
+ *
+ * Operation.  Cross-correlation (no kernel flip), zero padding, groups = 1:
+ *   y[n,(od,)oh,ow,o] = sum_{(kd,)kh,kw,c} x[n,(id,)ih,iw,c] * w[o,(kd,)kh,kw,c]
+ *   with ih = oh*stride_h - pad_h + kh*dil_h (likewise w, d), x = 0 outside.
+ *   Output extent per dim: floor((in + 2*pad - dil*(k-1) - 1)/stride) + 1.
+ *
+ * Layouts (all dense, row-major, element type = desc.dtype):
+ *   x  [N,H,W,C]  (2D)   or [N,D,H,W,C]  (3D)     -- channels-last input
+ *   w  [O,KH,KW,C](2D)   or [O,KD,KH,KW,C](3D)    -- output channel outermost
+ *   y  [N,OH,OW,O](2D)   or [N,OD,OH,OW,O](3D)
+ * Arithmetic: products accumulate in fp32 for every dtype; the output is rounded
+ * once to the dtype, round-to-nearest-even.  Winograd keeps its transformed
+ * tensors in fp32 whatever the input dtype.
+ *
+ * Ownership and threading.  The caller owns x, w, y, the workspace and the
+ * stream; they must stay valid until the work queued on the stream completes.
+ * The library allocates no device memory, keeps no global state, never
+ * synchronises and reads no environment variable.  Every call is thread-safe.
+ * The forward calls only queue kernels on the given HIP stream (NULL = the
+ * default stream); device faults therefore surface at the caller's next
+ * synchronisation.
+ *
+ * Errors.  Every call returns a status.  The forward calls validate every
+ * argument and the plan before queueing any work; on any error nothing is
+ * queued and y is left untouched.  A forced algorithm that cannot run returns
+ * CNHWC_ERR_NOT_APPLICABLE (or CNHWC_ERR_BUDGET for Winograd over budget); the
+ * library never silently falls back to another algorithm -- only
+ * CNHWC_ALGO_AUTO selects, deterministically.  (The tiling page's Problem
+ * section is about the opposite behaviour: a failed command buffer whose error
+ * was dropped left an all-zero output.)
+ */
+#ifndef CNHWC_H_
+#define CNHWC_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CNHWC_ABI_VERSION 1
+
+/* Fewest GEMM rows (tile_batch * tiles_per_image) a Winograd batch tile may
+ * carry when the batch does not fit in one tile; below it AUTO falls back to
+ * implicit GEMM.  The tiling page (Fix) falls back when tiles carry too few
+ * GEMM rows to amortise their fixed cost but gives no number; this value is
+ * our reading. */
+#define CNHWC_MIN_TILE_ROWS 256
+
+/* Byte cap of one unfold chunk (rows * K * element size).  The explicit page
+ * (Notes) says the unfold is tiled against a buffer limit and reuses one
+ * buffer; the limit here is a fixed constant, never live memory. */
+#define CNHWC_UNFOLD_CAP_BYTES (256ull << 20)
+
+/* AUTO takes unfold+GEMM for fp16/bf16 2D convs with C_out >= this value that
+ * no earlier rule took (explicit page: the rule is on the output-channel count
+ * and only for half precision; the threshold is set from measurements on
+ * MI355X). */
+#define CNHWC_UNFOLD_MIN_COUT 512
+
+typedef enum { CNHWC_F32 = 0, CNHWC_F16 = 1, CNHWC_BF16 = 2 } cnhwc_dtype_t;
+
+typedef enum {
+  CNHWC_ALGO_AUTO = 0,
+  CNHWC_ALGO_WINOGRAD = 1,      /* 3x3 stride-1 dilation-1 2D only */
+  CNHWC_ALGO_IMPLICIT_GEMM = 2, /* any 2D conv; scratch-free */
+  CNHWC_ALGO_UNFOLD_GEMM = 3,   /* any 2D conv; unfold buffer in the workspace */
+  CNHWC_ALGO_SMALL_KD = 4       /* 3D as KD accumulated 2D convs */
+} cnhwc_algo_t;
+
+typedef enum {
+  CNHWC_OK = 0,
+  CNHWC_ERR_INVALID_ARGUMENT = 1,  /* bad descriptor, null/misaligned pointer */
+  CNHWC_ERR_UNSUPPORTED = 2,       /* valid conv outside what this library runs */
+  CNHWC_ERR_NOT_APPLICABLE = 3,    /* the forced algorithm cannot run this conv */
+  CNHWC_ERR_BUDGET = 4,            /* forced Winograd: not one element fits */
+  CNHWC_ERR_WORKSPACE_TOO_SMALL = 5,
+  CNHWC_ERR_PLAN_MISMATCH = 6,     /* plan != cnhwc_conv_select(desc, plan.opts) */
+  CNHWC_ERR_HIP = 7,               /* a kernel launch reported an error */
+  CNHWC_ERR_INTERNAL = 8
+} cnhwc_status_t;
+
+/* Convolution descriptor.  For nd == 2 set d = kd = 1, and index 0 of
+ * stride/pad/dil to 1/0/1.  Index order of the triples: depth, height, width. */
+typedef struct {
+  int32_t nd;        /* 2 or 3 */
+  int32_t dtype;     /* cnhwc_dtype_t: element type of x, w and y */
+  int64_t n, d, h, w, c, o, kd, kh, kw;
+  int32_t stride[3];
+  int32_t pad[3];
+  int32_t dil[3];
+  int32_t groups;    /* must be 1 */
+} cnhwc_conv_desc_t;
+
+/* Selection options.  The selection depends on these and the descriptor only,
+ * never on free memory (tiling page, review; explicit page, closing review). */
+typedef struct {
+  uint64_t ws_limit_bytes;   /* W: the device working-set figure, or an injected
+                                budget (tiling page, Testing).  Must be > 0.  The
+                                Winograd budget is floor(3/4 W) - own bytes. */
+  int32_t force_algo;        /* cnhwc_algo_t; AUTO = select */
+  int32_t force_inner_algo;  /* SMALL_KD only: per-tap 2D algorithm; AUTO = select */
+  int64_t force_tile_batch;  /* Winograd: 0 = budget rule; else min(value, budget tile) */
+  int64_t force_unfold_rows; /* Unfold: 0 = the fixed byte cap; else rows per chunk */
+} cnhwc_select_opts_t;
+
+/* A plan: a plain value, a pure function of (descriptor, options). */
+typedef struct {
+  int32_t algo;              /* resolved algorithm, never AUTO */
+  int32_t inner_algo;        /* SMALL_KD: per-tap 2D algorithm; else == algo */
+  int64_t out_d, out_h, out_w;
+  int64_t tile_batch;        /* Winograd: batch elements per tile (3D: frames) */
+  int64_t n_tiles;           /* Winograd: number of batch tiles */
+  int64_t tiles_per_image;   /* Winograd: ceil(OH/6) * ceil(OW/6) */
+  int64_t unfold_rows;       /* Unfold: output rows per chunk */
+  int64_t n_chunks;          /* Unfold: number of chunks */
+  uint64_t own_bytes;        /* Winograd: bytes of x + y + transformed filter */
+  uint64_t budget_bytes;     /* Winograd: floor(3/4 W) - own, 0 if negative */
+  uint64_t scratch_per_element; /* Winograd: V + M bytes of one batch element */
+  uint64_t workspace_bytes;  /* bytes the forward call needs in `workspace` */
+  int32_t kernel_config;     /* GEMM tile configuration id */
+  int32_t reserved;
+  cnhwc_select_opts_t opts;  /* the options this plan was made from */
+} cnhwc_plan_t;
+
+/* Returns CNHWC_ABI_VERSION. */
+int cnhwc_abi_version(void);
+
+/* Human-readable name of a status (static storage; never NULL). */
+const char* cnhwc_status_string(cnhwc_status_t s);
+
+/* Algorithm selection and memory planning (host only, no device call).
+ *
+ * AUTO, 2D, in order (tiling page, Problem and Fix; explicit page, Notes):
+ *  1. Winograd when KH = KW = 3, stride 1, dilation 1, C % 32 == 0,
+ *     O % 32 == 0, C + O >= 256 and dtype == F32, and the budget rule admits
+ *     it: tile = min(N, floor(budget / scratch_per_element)); fall back if
+ *     tile < 1, or if tile < N and tile * tiles_per_image < CNHWC_MIN_TILE_ROWS.
+ *  2. Unfold + GEMM for F16/BF16 with O >= CNHWC_UNFOLD_MIN_COUT.
+ *  3. Implicit GEMM.
+ * AUTO, 3D (3D page, Change): SMALL_KD when N == 1, KD <= 7, depth stride 1,
+ *   dilation 1 in every dim, depth pad 0, C % 16 == 0 and O % 16 == 0; the
+ *   per-tap 2D algorithm is AUTO-selected on the [OD,H,W,C] frame conv.  Any
+ *   other 3D conv returns CNHWC_ERR_UNSUPPORTED.
+ * Forcing: WINOGRAD needs only 3x3/stride 1/dilation 1 (the channel gates are
+ *   skipped); a forced tile size is capped by the budget tile (tiling page,
+ *   Testing).  SMALL_KD needs N == 1, depth stride 1, depth dilation 1, depth
+ *   pad 0.
+ * Returns OK and fills *plan, or an error (plan untouched). */
+cnhwc_status_t cnhwc_conv_select(const cnhwc_conv_desc_t* desc, const cnhwc_select_opts_t* opts,
+                                 cnhwc_plan_t* plan);
+
+/* The Winograd batch-tiling rule alone, as select applies it (tiling page,
+ * Fix): budget = floor(3/4 * ws_limit) - own (0 if negative);
+ * tile = min(n, floor(budget / scratch_per_element)); with force_tile > 0,
+ * tile = min(force_tile, that).  *tile_batch = 0 means "does not fit";
+ * *fallback = 1 when AUTO would fall back to implicit GEMM (tile < 1, or
+ * tile < n with tile * rows_per_element < CNHWC_MIN_TILE_ROWS and no forced
+ * tile).  Exposed so callers can evaluate the rule with other buffer sets. */
+cnhwc_status_t cnhwc_winograd_tile_rule(uint64_t ws_limit, uint64_t own_bytes,
+                                        uint64_t scratch_per_element, int64_t n,
+                                        int64_t rows_per_element, int64_t force_tile,
+                                        int64_t* tile_batch, uint64_t* budget_bytes,
+                                        int32_t* fallback);
+
+/* 2D forward: y = conv2d(x, w) with the given plan (from cnhwc_conv_select on
+ * this desc; re-derived and compared, CNHWC_ERR_PLAN_MISMATCH otherwise).
+ * x, w, y: device pointers, 16-byte aligned, layouts above, not overlapping y.
+ * workspace: device pointer, 16-byte aligned, >= plan.workspace_bytes (may be
+ * NULL when that is 0); contents on entry are ignored, on exit undefined.
+ * hip_stream: a hipStream_t (NULL = default stream).
+ * Winograd runs the batch in plan.n_tiles tiles of plan.tile_batch elements
+ * (the last may be shorter) through one workspace; the result is bit-identical
+ * for every tile size (tiling page, Testing).  Unfold runs plan.n_chunks row
+ * chunks through one buffer (explicit page, Notes). */
+cnhwc_status_t cnhwc_conv2d_fwd(const cnhwc_conv_desc_t* desc, const cnhwc_plan_t* plan,
+                                const void* x, const void* w, void* y, void* workspace,
+                                uint64_t workspace_bytes, void* hip_stream);
+
+/* 3D forward (nd == 3), same conventions.  SMALL_KD (3D page, Change): for each
+ * depth tap kd, the frames x[0, kd:kd+OD] (a pointer offset) and the weight
+ * slice w[:, kd] (a strided view) form a 2D conv with batch OD, computed by the
+ * plan's inner algorithm and accumulated in fp32 (in y itself for F32, in the
+ * workspace otherwise); the last tap rounds into y once.  KD == 1 gives the
+ * same bits as conv2d on the [D,H,W,C] frames. */
+cnhwc_status_t cnhwc_conv3d_fwd(const cnhwc_conv_desc_t* desc, const cnhwc_plan_t* plan,
+                                const void* x, const void* w, void* y, void* workspace,
+                                uint64_t workspace_bytes, void* hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CNHWC_H_ */

@@ -1,0 +1,169 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Cases follow the workloads of the MLX pages: the small fp32 3x3 conv, the
+half-precision filter/stride/dilation/padding grid with aligned and unaligned
+channels (MLX PR "Use the explicit gemm for wide convs on neural accelerators",
+Verified), the fp32 Winograd workload at reduced batch and size (MLX PR "Bound
+winograd conv2d working set by tiling the batch"), and the 3D decomposition
+(MLX PR "Decompose small kernel-depth 3D convs into 2D convs", Tests).
+"""
+import numpy as np
+import pytest
+import torch
+
+import conv_workloads as cw
+import oracle
+from gpu_util import TOL, bits, check_parity, gather_rows, poisoned, to_oracle
+
+pytestmark = pytest.mark.gpu
+
+cn = pytest.importorskip("convolution_nhwc_conv2d_amd")
+
+
+def _dev(t):
+    return t.to("cuda")
+
+
+def _run_case(case, algo, rows=None, **kw):
+    w = case.weight()
+    x = case.input()
+    xg, wg = _dev(x), _dev(w)
+    fn = cn.conv2d if case.nd == 2 else cn.conv3d
+    y = fn(xg, wg, **case.conv_kwargs(), algo=algo, **kw)
+    torch.cuda.synchronize()
+    yr, den = oracle.conv(to_oracle(x), to_oracle(w), **case.conv_kwargs(), rows=rows)
+    yg = gather_rows(y, rows) if rows is not None else y.cpu()
+    return check_parity(yg, yr, den, y.dtype, f"{case.name}/{algo}"), y
+
+
+# ------------------------------------------------------------ small fp32 conv
+
+@pytest.mark.parametrize("algo", ["winograd", "implicit_gemm", "unfold_gemm", "auto"])
+def test_small_fp32_all_algorithms(algo):
+    case = cw.small_fp32()
+    err, y = _run_case(case, algo)
+    assert err < 2e-5
+    p = cn.plan2d(case.x_shape(), case.w_shape(), **case.conv_kwargs())
+    assert p.algo_name == "implicit_gemm"  # C+O = 64 < 256: AUTO does not take Winograd
+
+
+# ------------------------------------------------------- half geometry grid
+
+GRID = [(dt, c) for dt in ("f16", "bf16") for c in (128, 120)]
+
+
+@pytest.mark.parametrize("dtype,c_in", GRID)
+def test_half_geometry_grid(dtype, c_in):
+    for case in cw.half_geometry_grid(dtype, c_in):
+        x, w = case.input(), case.weight()
+        yr, den = oracle.conv(to_oracle(x), to_oracle(w), **case.conv_kwargs())
+        for algo in ("implicit_gemm", "unfold_gemm"):
+            y = cn.conv2d(_dev(x), _dev(w), **case.conv_kwargs(), algo=algo)
+            check_parity(y.cpu(), yr, den, y.dtype, f"{case.name}/{algo}")
+
+
+@pytest.mark.parametrize("k,s,d,p", [(3, 1, 1, 1), (5, 2, 1, 2), (7, 2, 2, 0), (1, 2, 1, 0), (3, 2, 2, 2)])
+def test_fp32_geometry(k, s, d, p):
+    h = (16 - 1) * s + d * (k - 1) + 1 - 2 * p
+    for c_in in (64, 30):
+        case = cw.ConvCase(f"f32_k{k}s{s}d{d}p{p}_c{c_in}", 2, h, h + 1, c_in, 48, k, k, (s, s), (p, p), (d, d),
+                           "f32", "uniform", "normal", None, 9, k * 100 + c_in)
+        x, w = case.input(), case.weight()
+        yr, den = oracle.conv(to_oracle(x), to_oracle(w), **case.conv_kwargs())
+        for algo in ("implicit_gemm", "unfold_gemm"):
+            y = cn.conv2d(_dev(x), _dev(w), **case.conv_kwargs(), algo=algo)
+            check_parity(y.cpu(), yr, den, y.dtype, f"{case.name}/{algo}")
+
+
+# ------------------------------------------- integer data: exact in every dtype
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("algo", ["implicit_gemm", "unfold_gemm", "winograd"])
+def test_integer_data_bit_exact(dtype, algo):
+    # entries in {-1,0,1}, K = 3*3*24 = 216 <= 256: every partial sum is an
+    # integer of magnitude <= 216, exact in fp32/fp16/bf16 -> results must equal
+    # the oracle exactly (Winograd only for fp32-exact transforms: excluded)
+    if algo == "winograd":
+        pytest.skip("Winograd transforms use fractional coefficients: not exact by construction")
+    case = cw.ConvCase("ternary", 2, 13, 11, 24, 40, 3, 3, (1, 1), (1, 1), (1, 1), dtype, "ternary", "ternary",
+                       1.0, 21, 0)
+    x, w = case.input(), case.weight()
+    y = cn.conv2d(_dev(x), _dev(w), **case.conv_kwargs(), algo=algo)
+    yr, _ = oracle.conv(to_oracle(x), to_oracle(w), **case.conv_kwargs())
+    assert np.array_equal(y.cpu().double().numpy(), yr)
+
+
+# --------------------------------------------------------- Winograd tiling
+
+def _wino_case(n=5, h=40, w=44, c=64, o=96):
+    return cw.ConvCase(f"wino_{n}x{h}x{w}_{c}to{o}", n, h, w, c, o, 3, 3, (1, 1), (1, 1), (1, 1),
+                       "f32", "uniform", "normal", (1.0 / (9 * c)) ** 0.5, 2, 77)
+
+
+def test_winograd_parity_fp32():
+    case = _wino_case()
+    err, _ = _run_case(case, "winograd")
+    assert err < 2e-5
+
+
+@pytest.mark.parametrize("tile", [1, 2, 3, 4])
+def test_winograd_tiled_bit_identical_to_untiled(tile):
+    case = _wino_case()
+    x, w = _dev(case.input()), _dev(case.weight())
+    full = cn.conv2d(x, w, 1, 1, 1, algo="winograd")
+    p = cn.plan2d(tuple(x.shape), tuple(w.shape), 1, 1, 1, algo="winograd", tile_batch=tile)
+    assert p.tile_batch == tile and p.n_tiles == -(-case.n // tile)
+    tiled = cn.conv2d(x, w, 1, 1, 1, algo="winograd", tile_batch=tile, out=poisoned(full.shape, full.dtype))
+    assert torch.equal(bits(tiled), bits(full))
+
+
+def test_winograd_budget_injection_tiles_and_falls_back():
+    # T = 16*17 = 272 tiles per image: a 2-element tile carries 544 GEMM rows,
+    # above the MIN_TILE_ROWS floor, so the budget rule tiles instead of falling back
+    case = _wino_case(n=6, h=96, w=100, c=128, o=128)
+    x, w = _dev(case.input()), _dev(case.weight())
+    full = cn.conv2d(x, w, 1, 1, 1)
+    assert cn.plan2d(tuple(x.shape), tuple(w.shape), 1, 1, 1).algo_name == "winograd"
+    base = cn.plan2d(tuple(x.shape), tuple(w.shape), 1, 1, 1, ws_limit=10**12)
+    # a W leaving room for exactly two elements
+    need = base.own_bytes + 2 * base.scratch_per_element
+    wl = -(-need * 4 // 3) + 8
+    p = cn.plan2d(tuple(x.shape), tuple(w.shape), 1, 1, 1, ws_limit=wl)
+    assert p.algo_name == "winograd" and p.tile_batch == 2 and p.n_tiles == 3
+    tiled = cn.conv2d(x, w, 1, 1, 1, ws_limit=wl)
+    assert torch.equal(bits(tiled), bits(full))
+    # 1 MB -> implicit GEMM fallback: correct but not bit-identical in general
+    p = cn.plan2d(tuple(x.shape), tuple(w.shape), 1, 1, 1, ws_limit=2**20)
+    assert p.algo_name == "implicit_gemm"
+    fb = cn.conv2d(x, w, 1, 1, 1, ws_limit=2**20)
+    yr, den = oracle.conv(to_oracle(case.input()), to_oracle(case.weight()), 1, 1, 1)
+    check_parity(fb.cpu(), yr, den, torch.float32, "fallback")
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_winograd_half_precision_forced(dtype):
+    case = cw.ConvCase(f"wino_{dtype}", 2, 20, 23, 64, 64, 3, 3, (1, 1), (1, 1), (1, 1), dtype, "normal",
+                       "normal", None, 3, 5)
+    err, _ = _run_case(case, "winograd")
+    assert err < 1e-2
+
+
+# ---------------------------------------------------------------- 3D
+
+@pytest.mark.parametrize("kd", [1, 2, 3, 5])
+@pytest.mark.parametrize("inner", ["auto", "implicit_gemm", "winograd", "unfold_gemm"])
+def test_conv3d_small_kd(kd, inner):
+    case = cw.ConvCase(f"c3d_kd{kd}", 1, 9, 10, 32, 48, 3, 3, (1, 1, 1), (0, 1, 1), (1, 1, 1), "bf16",
+                       "normal", "normal", None, 5, kd, nd=3, d=kd + 4, kd=kd)
+    err, _ = _run_case(case, "auto", inner_algo=inner) if inner != "auto" else _run_case(case, "auto")
+    assert err < 1e-2
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+def test_conv3d_kd1_bit_identical_to_conv2d(dtype):
+    case = cw.ConvCase("c3d_kd1", 1, 12, 12, 32, 32, 3, 3, (1, 1, 1), (0, 1, 1), (1, 1, 1), dtype,
+                       "normal", "normal", None, 5, 99, nd=3, d=6, kd=1)
+    x, w = _dev(case.input()), _dev(case.weight())
+    y3 = cn.conv3d(x, w, 1, (0, 1, 1), 1)
+    y2 = cn.conv2d(x[0], w[:, 0].contiguous(), 1, 1, 1)
+    assert torch.equal(bits(y3[0]), bits(y2))

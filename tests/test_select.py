@@ -1,0 +1,292 @@
+"""Planner tests (host logic only, no GPU): cnhwc_conv_select and the Winograd
+batch-tiling rule, including the memory figures printed on MLX PR "Bound
+winograd conv2d working set by tiling the batch" (tests/golden/tiling_page_memory.txt).
+"""
+import ctypes
+import math
+import os
+
+import pytest
+import torch
+
+import convolution_nhwc_conv2d_amd as cn
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "tiling_page_memory.txt")
+GB = 1e9
+
+
+def _golden():
+    rows = {"m4pro": [], "m2max": [], "m5max_elements": None, "m5max_peak": None}
+    for line in open(GOLDEN):
+        line = line.split("#")[0].split()
+        if not line:
+            continue
+        if line[0] == "m4pro":
+            rows["m4pro"].append((int(line[1]), float(line[2]), float(line[3])))
+        elif line[0] == "m2max":
+            rows["m2max"].append((int(line[1]), float(line[2]), float(line[3])))
+        elif line[0] == "m5max_elements":
+            rows["m5max_elements"] = int(line[1])
+        elif line[0] == "m5max_peak":
+            rows["m5max_peak"] = (float(line[1]), float(line[2]))
+    return rows
+
+
+# ---- the buffer set the tiling page describes for MLX's Winograd (Problem):
+# padded input + input-transform GEMM operand V + GEMM result M per element,
+# and the conv's own tensors x, y, transformed filter U (Fix).
+def _mlx_buffers(h, w, c, o, m):
+    """Bytes per batch element for F(m x m, 3x3) (fp32): x, y, pad, V, M; and U."""
+    t = m + 2
+    th, tw = math.ceil(h / m), math.ceil(w / m)
+    tiles = th * tw
+    x = h * w * c * 4
+    y = h * w * o * 4
+    pad = (th * m + 2) * (tw * m + 2) * c * 4  # padded to whole tiles plus the 2-pixel halo
+    v = t * t * tiles * c * 4
+    mm = t * t * tiles * o * 4
+    u = t * t * o * c * 4
+    return x, y, pad, v, mm, u, tiles
+
+
+def test_golden_untiled_peaks_single_out_f6x3():
+    """The control peaks (no tiling) are reproduced only by 8x8 tiles at stride 6."""
+    g = _golden()
+    for m, expect in ((6, True), (4, False), (2, False)):
+        x, y, pad, v, mm, u, _ = _mlx_buffers(512, 512, 192, 96, m)
+        ok = all(round((n * (x + y + pad + v + mm) + u) / GB, 1) == peak for n, peak, _ in g["m4pro"])
+        assert ok == expect, m
+    x, y, pad, v, mm, u, _ = _mlx_buffers(512, 512, 192, 96, 6)
+    for n, untiled, _ in g["m2max"]:
+        assert round((n * (x + y + pad + v + mm) + u) / GB) == untiled
+
+
+def test_golden_tiled_peaks_follow_the_budget_rule():
+    """Some single working-set figure W gives all four printed M4 Pro tiled peaks
+    through the rule tile = min(N, floor((3/4 W - own) / scratch))."""
+    g = _golden()
+    x, y, pad, v, mm, u, tiles = _mlx_buffers(512, 512, 192, 96, 6)
+    scratch = pad + v + mm
+    hits = []
+    for wmb in range(39000, 42000, 5):
+        wl = wmb * 10**6
+        tiles_ok = []
+        for n, _, tiled in g["m4pro"]:
+            own = n * (x + y) + u
+            tb, _, fb = cn.winograd_tile_rule(wl, own, scratch, n, tiles)
+            if fb or round((own + tb * scratch) / GB, 1) != tiled:
+                break
+            tiles_ok.append(tb)
+        else:
+            hits.append((wl, tuple(tiles_ok)))
+    assert hits, "no W reproduces the printed tiled peaks"
+    assert {t for _, t in hits} == {(27, 24, 20, 14)}
+    assert 40.1e9 < min(w for w, _ in hits) and max(w for w, _ in hits) < 40.4e9
+    # M2 Max, batch 80: the printed tiled peak is the tile of 45 elements
+    for n, _, tiled in g["m2max"]:
+        own = n * (x + y) + u
+        assert [tb for tb in range(1, n) if round((own + tb * scratch) / GB) == tiled] == [45]
+
+
+def test_golden_injected_512mb_case():
+    """N=16, 128x128, 192->96 is the shape whose output has the printed element
+    count; at an injected 512 MB budget the rule gives one-element tiles and the
+    printed 0.36 GB peak, and at 1 MB it falls back."""
+    g = _golden()
+    assert 16 * 128 * 128 * 96 == g["m5max_elements"]
+    x, y, pad, v, mm, u, tiles = _mlx_buffers(128, 128, 192, 96, 6)
+    own = 16 * (x + y) + u
+    untiled = 16 * (x + y + pad + v + mm) + u
+    assert round(untiled / GB, 2) == g["m5max_peak"][0]
+    for wl in (512 * 10**6, 512 * 2**20):
+        tb, _, fb = cn.winograd_tile_rule(wl, own, pad + v + mm, 16, tiles)
+        assert (tb, fb) == (1, False)
+        assert round((own + tb * (pad + v + mm)) / GB, 2) == g["m5max_peak"][1]
+    tb, _, fb = cn.winograd_tile_rule(2**20, own, pad + v + mm, 16, tiles)
+    assert fb and tb == 0
+
+
+# ------------------------------------------------------------ our own plans
+
+def _p(xs, ws, stride=1, pad=1, dil=1, dtype=torch.float32, **kw):
+    return cn.plan2d(xs, ws, stride, pad, dil, dtype, **kw)
+
+
+C2W = (96, 3, 3, 192)
+
+
+def test_wide_fp32_full_budget_is_untiled_winograd():
+    p = _p((40, 512, 512, 192), C2W, ws_limit=288 * 10**9)
+    assert p.algo_name == "winograd" and p.tile_batch == 40 and p.n_tiles == 1
+    assert p.tiles_per_image == 86 * 86
+    assert p.scratch_per_element == 64 * 7396 * (192 + 96) * 4
+    assert p.own_bytes == 40 * 512 * 512 * (192 + 96) * 4 + 64 * 96 * 192 * 4
+    assert p.workspace_bytes >= 64 * 96 * 192 * 4 + 40 * p.scratch_per_element
+    assert p.budget_bytes == 288 * 10**9 // 4 * 3 - p.own_bytes
+
+
+@pytest.mark.parametrize("n", [8, 32, 40, 64])
+@pytest.mark.parametrize("wl", [512 * 10**6, 512 * 2**20, 10**6, 2**20])
+def test_wide_fp32_small_budgets_fall_back(n, wl):
+    p = _p((n, 512, 512, 192), C2W, ws_limit=wl)
+    assert p.algo_name == "implicit_gemm" and p.workspace_bytes == 0
+
+
+@pytest.mark.parametrize("n", [32, 40, 48, 64])
+def test_wide_fp32_m4pro_class_budget_tiles(n):
+    wl = 40_200_000_000
+    p = _p((n, 512, 512, 192), C2W, ws_limit=wl)
+    own = n * 512 * 512 * (192 + 96) * 4 + 64 * 96 * 192 * 4
+    scratch = 64 * 7396 * (192 + 96) * 4
+    tb = min(n, (wl * 3 // 4 - own) // scratch)
+    assert p.algo_name == "winograd" and p.tile_batch == tb and p.n_tiles == -(-n // tb)
+
+
+def test_page_shape_512mib_tiles_our_scratch():
+    p = _p((16, 128, 128, 192), C2W, ws_limit=512 * 2**20)
+    assert p.algo_name == "winograd" and p.tile_batch == 2 and p.n_tiles == 8
+    assert _p((16, 128, 128, 192), C2W, ws_limit=2**20).algo_name == "implicit_gemm"
+
+
+def test_forced_tile_is_capped_by_budget_and_leaves_short_final_tile():
+    p = _p((40, 512, 512, 192), C2W, ws_limit=40_200_000_000, tile_batch=1000)
+    q = _p((40, 512, 512, 192), C2W, ws_limit=40_200_000_000)
+    assert p.tile_batch == q.tile_batch
+    p = _p((40, 512, 512, 192), C2W, tile_batch=3)
+    assert p.tile_batch == 3 and p.n_tiles == 14  # 13 tiles of 3 and a final tile of 1
+    p = _p((40, 512, 512, 192), C2W, tile_batch=7)
+    assert p.tile_batch == 7 and p.n_tiles == 6
+
+
+def test_min_tile_rows_fallback_for_spatially_tiny_convs():
+    # the page's 256 x 4x4, 64 -> 192 conv: one 6x6 tile per image
+    xs, ws = (256, 4, 4, 64), (192, 3, 3, 64)
+    assert _p(xs, ws).algo_name == "winograd"  # whole batch fits: unchanged
+    full = _p(xs, ws, ws_limit=10**12)
+    wl = -(-(full.own_bytes + 100 * full.scratch_per_element) * 4 // 3)
+    p = _p(xs, ws, ws_limit=wl)
+    assert p.algo_name == "implicit_gemm"  # 100 one-tile elements = 100 rows < 256
+    p = _p(xs, ws, ws_limit=wl, tile_batch=50)
+    assert p.algo_name == "winograd" and p.tile_batch == 50  # a forced tile bypasses the floor
+
+
+@pytest.mark.parametrize("c,o,dtype,expect", [
+    (192, 96, torch.float32, "winograd"), (160, 96, torch.float32, "winograd"),
+    (128, 96, torch.float32, "implicit_gemm"), (200, 96, torch.float32, "implicit_gemm"),
+    (192, 100, torch.float32, "implicit_gemm"), (256, 256, torch.float16, "implicit_gemm"),
+    (256, 512, torch.float16, "unfold_gemm"), (256, 1024, torch.bfloat16, "unfold_gemm"),
+    (256, 4096, torch.float32, "winograd")])
+def test_auto_gate(c, o, dtype, expect):
+    assert _p((2, 32, 32, c), (o, 3, 3, c), dtype=dtype).algo_name == expect
+
+
+def test_winograd_gate_needs_3x3_stride1_dilation1():
+    for xs, ws, s, d in (((1, 32, 32, 192), (96, 3, 3, 192), 2, 1), ((1, 32, 32, 192), (96, 3, 3, 192), 1, 2),
+                         ((1, 32, 32, 192), (96, 5, 5, 192), 1, 1)):
+        assert _p(xs, ws, s, 1, d).algo_name == "implicit_gemm"
+        with pytest.raises(cn.CnhwcError) as e:
+            _p(xs, ws, s, 1, d, algo="winograd")
+        assert e.value.name == "NOT_APPLICABLE"
+
+
+def test_forced_winograd_over_budget():
+    with pytest.raises(cn.CnhwcError) as e:
+        _p((8, 512, 512, 192), C2W, algo="winograd", ws_limit=2**20)
+    assert e.value.name == "BUDGET"
+
+
+def test_unfold_rows_cap_and_forced_rows():
+    xs, ws = (16, 32, 32, 256), (1024, 3, 3, 256)
+    p = _p(xs, ws, dtype=torch.float16)
+    k = 9 * 256
+    assert p.algo_name == "unfold_gemm"
+    assert p.unfold_rows == min(16 * 1024, (256 << 20) // (k * 2))
+    assert p.workspace_bytes >= p.unfold_rows * k * 2
+    p = _p(xs, ws, dtype=torch.float16, unfold_rows=1000)
+    assert p.unfold_rows == 1000 and p.n_chunks == 17  # 16 x 1000 + a short chunk of 384
+
+
+def test_kernel_config_depends_on_channels_and_dtype_only():
+    a = _p((40, 512, 512, 192), C2W)
+    b = _p((1, 64, 64, 192), C2W, algo="winograd")
+    c = _p((40, 512, 512, 192), C2W, ws_limit=40_200_000_000)
+    assert a.kernel_config == b.kernel_config == c.kernel_config
+
+
+def test_select_is_deterministic_bytes():
+    d = cn.make_desc((40, 512, 512, 192), C2W, 1, 1, 1, torch.float32)
+    o = cn.make_opts(ws_limit=40_200_000_000)
+    a, b = cn.select(d, o), cn.select(d, o)
+    assert ctypes.string_at(ctypes.addressof(a), ctypes.sizeof(a)) == \
+        ctypes.string_at(ctypes.addressof(b), ctypes.sizeof(b))
+
+
+@pytest.mark.parametrize("xs,ws,s,p,d,err", [
+    ((1, 2, 2, 8), (8, 5, 5, 8), 1, 0, 1, "INVALID_ARGUMENT"),   # output extent < 1
+    ((1, 8, 8, 8), (8, 3, 3, 8), 0, 0, 1, "INVALID_ARGUMENT"),   # stride 0
+    ((1, 8, 8, 8), (8, 3, 3, 8), 1, -1, 1, "INVALID_ARGUMENT"),  # negative pad
+    ((0, 8, 8, 8), (8, 3, 3, 8), 1, 0, 1, "INVALID_ARGUMENT"),   # empty batch
+])
+def test_invalid_descriptors(xs, ws, s, p, d, err):
+    with pytest.raises(cn.CnhwcError) as e:
+        _p(xs, ws, s, p, d)
+    assert e.value.name == err
+
+
+def test_invalid_opts_and_groups():
+    d = cn.make_desc((1, 8, 8, 8), (8, 3, 3, 8), 1, 1, 1)
+    with pytest.raises(cn.CnhwcError) as e:
+        cn.select(d, cn.make_opts(ws_limit=0))
+    assert e.value.name == "INVALID_ARGUMENT"
+    d.groups = 2
+    with pytest.raises(cn.CnhwcError) as e:
+        cn.select(d, cn.make_opts())
+    assert e.value.name == "UNSUPPORTED"
+
+
+# ------------------------------------------------------------------- 3D
+
+X3, W3 = (1, 41, 60, 104, 256), (256, 3, 3, 3, 256)
+
+
+def test_3d_video_shapes_take_small_kd():
+    for t, h, w, c, o in ((17, 64, 64, 256, 256), (41, 60, 104, 256, 256), (41, 120, 208, 512, 512)):
+        p = cn.plan3d((1, t, h, w, c), (o, 3, 3, 3, c), 1, (0, 1, 1), 1, torch.bfloat16)
+        assert p.algo_name == "small_kd" and p.out_d == t - 2
+        assert p.inner_algo_name in ("implicit_gemm", "unfold_gemm")
+        assert p.workspace_bytes >= (t - 2) * h * w * o * 4  # fp32 accumulator
+
+
+@pytest.mark.parametrize("change", ["n2", "kd9", "stride_d", "dil_h", "pad_d", "c_mod16", "o_mod16"])
+def test_3d_guard_each_clause(change):
+    xs, ws = list(X3), list(W3)
+    s, p, d = [1, 1, 1], [0, 1, 1], [1, 1, 1]
+    if change == "n2":
+        xs[0] = 2
+    elif change == "kd9":
+        ws[1] = 9
+    elif change == "stride_d":
+        s[0] = 2
+    elif change == "dil_h":
+        d[1] = 2
+    elif change == "pad_d":
+        p[0] = 1
+    elif change == "c_mod16":
+        xs[-1] = ws[-1] = 250
+    elif change == "o_mod16":
+        ws[0] = 250
+    with pytest.raises(cn.CnhwcError) as e:
+        cn.plan3d(tuple(xs), tuple(ws), s, p, d, torch.bfloat16)
+    assert e.value.name == "UNSUPPORTED"
+    structural = change in ("n2", "stride_d", "pad_d")
+    if structural:
+        with pytest.raises(cn.CnhwcError) as e:
+            cn.plan3d(tuple(xs), tuple(ws), s, p, d, torch.bfloat16, algo="small_kd")
+        assert e.value.name == "NOT_APPLICABLE"
+    else:  # forcing the decomposition only needs its structural conditions
+        assert cn.plan3d(tuple(xs), tuple(ws), s, p, d, torch.bfloat16, algo="small_kd").algo_name == "small_kd"
+
+
+def test_3d_forced_inner_winograd():
+    p = cn.plan3d(X3, W3, 1, (0, 1, 1), 1, torch.bfloat16, inner_algo="winograd")
+    assert p.inner_algo_name == "winograd" and p.tile_batch == 39
