@@ -1,0 +1,252 @@
+#!/usr/bin/env python3
+"""Benchmark of the channels-last conv forward hot path on one MI355X.
+
+Workload (default): the fp32 conv2d the Winograd-tiling MLX PR ("Bound
+winograd conv2d working set by tiling the batch", Testing) reports on --
+N=40 x 512x512, C=192 -> O=96, 3x3, stride 1, pad 1, x ~ U[-1,1],
+w ~ N(0, 1/(9C)), seeded and synthetic.  One step is one full forward call
+(plan selection, then every kernel of the selected algorithm: for this
+workload the Winograd filter transform, input transform, 64 tile-position
+GEMMs and output transform, over the batch tiles the byte budget allows).
+
+Metric: direct-equivalent TFLOP/s = 2*N*OH*OW*O*C*KH*KW / time per step, with
+inputs resident in HBM.  Per-kernel durations come from hipEvents the library
+records on the launch stream between kernels during the timed steps; the
+dominant kernel is reported against its roofline (algorithmic flops or bytes
+per launch / average launch time).  The CPU baseline times the fp64 oracle on
+a bounded sample of output pixels of the same workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--batch N]
+                       [--ws-limit BYTES] [--tile-batch T] [--no-cpu-baseline]
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK = {  # MI355X published peaks
+    "hbm_gbs": 8000.0,
+    "mfma_tflops": {"f32": 157.3, "f16": 2500.0, "bf16": 2500.0},
+}
+PAGE_BASELINE_TFLOPS = 11.2  # the page's ~310 ms Winograd time on this workload, direct-equivalent (M2 Max)
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--batch", type=int, default=40)
+    ap.add_argument("--ws-limit", type=int, default=None)
+    ap.add_argument("--tile-batch", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    return ap.parse_args()
+
+
+def csrc_hash():
+    """Hash of the kernel sources (decides whether stored traffic counters still apply)."""
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "convolution_nhwc_conv2d_amd", "csrc")
+    for f in sorted(os.listdir(d)):
+        if f.endswith((".hip", ".hpp", ".h", ".cpp")):
+            h.update(f.encode())
+            h.update(open(os.path.join(d, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def kernel_work(kind, plan, case, es):
+    """Algorithmic work of one launch of a kernel kind for this plan:
+    (bound, amount, unit).  Flops for GEMM stages, HBM bytes for transforms."""
+    n, h, w, c, o = plan.tile_batch, case.h, case.w, case.c, case.o
+    cs = (c + 7) // 8 * 8
+    rows = n * plan.tiles_per_image
+    if kind == "wino_gemm":
+        return "mfma", 2.0 * 64 * rows * c * o, "flop"
+    if kind == "wino_input":
+        return "hbm", float(n * h * w * c * es + 64 * rows * cs * 4), "byte"
+    if kind == "wino_output":
+        return "hbm", float(64 * rows * o * 4 + n * plan.out_h * plan.out_w * o * es), "byte"
+    if kind == "wino_filter":
+        return "hbm", float(o * 9 * c * es + 64 * o * cs * 4), "byte"
+    if kind == "implicit_gemm":
+        m = case.n * plan.out_h * plan.out_w
+        return "mfma", 2.0 * m * o * case.kh * case.kw * c, "flop"
+    return None, None, None
+
+
+def load_traffic(workload_key, kind):
+    """HBM traffic per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        data = json.load(open(path))
+    except ValueError:
+        return None
+    ent = data.get(workload_key, {}).get(kind)
+    if not ent or ent.get("csrc_hash") != csrc_hash():
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def cpu_baseline(case, seconds):
+    """Time the fp64 oracle on a seeded sample of output pixels (all O channels)."""
+    import numpy as np
+    import oracle
+    import conv_workloads as cw
+    threads = len(os.sched_getaffinity(0))
+    w = case.weight().numpy()
+    per = case.h * case.w  # output pixels per batch element (3x3, s1, p1: OH=H, OW=W)
+    kw = case.conv_kwargs()
+    x1 = case.input([0]).numpy()
+    calib = cw.sample_rows(per, 4096, 11)
+    t0 = time.perf_counter()
+    oracle.conv(x1, w, **kw, rows=calib, threads=threads)
+    rate = calib.size / (time.perf_counter() - t0)
+    # the sample: seeded output pixels spread over the first `elems` batch elements
+    count = int(max(4096, rate * seconds))
+    elems = min(case.n, -(-count // per))
+    count = min(count, elems * per)
+    xs = case.input(list(range(elems))).numpy()
+    rows = cw.sample_rows(elems * per, count, 12)
+    t0 = time.perf_counter()
+    oracle.conv(xs, w, **kw, rows=rows, threads=threads)
+    dt = time.perf_counter() - t0
+    flops = 2.0 * count * case.o * case.kh * case.kw * case.c
+    cpu = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{count} seeded output pixels (x {case.o} channels) of batch elements 0..{elems - 1}, "
+                      f"fp64 direct correlation, {dt:.2f} s wall; CPU {cpu}",
+            "seconds": dt, "outputs_per_s": count * case.o / dt}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(each GPU would run the same plan on its own share of the batch).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import conv_workloads as cw
+    import convolution_nhwc_conv2d_amd as cn
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    case = cw.wide_fp32(args.batch)
+    log(f"[bench] generating {case.name} inputs")
+    t0 = time.perf_counter()
+    w = case.weight().to(dev)
+    x = torch.empty(case.x_shape(), dtype=torch.float32, device=dev)
+    for i in range(case.n):
+        x[i].copy_(case.element(i))
+    torch.cuda.synchronize()
+    log(f"[bench] inputs resident in HBM ({time.perf_counter() - t0:.1f} s)")
+
+    ws_limit = args.ws_limit if args.ws_limit is not None else cn.default_ws_limit(dev)
+    plan = cn.plan2d(tuple(x.shape), tuple(w.shape), 1, 1, 1, torch.float32, ws_limit=ws_limit,
+                     tile_batch=args.tile_batch)
+    log(f"[bench] plan {plan}")
+    out = torch.empty((case.n, plan.out_h, plan.out_w, case.o), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(1, plan.workspace_bytes), dtype=torch.uint8, device=dev)
+
+    def step(timer=None):
+        cn.conv2d(x, w, 1, 1, 1, plan=plan, out=out, workspace=ws, timer=timer)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] warmup {args.warmup} done; timing {args.steps} steps")
+    timer = cn.KernelTimer()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(timer)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    ms = dt * 1e3 / args.steps
+    flops = cn.direct_flops(tuple(x.shape), tuple(w.shape), plan)
+    value = flops / (ms / 1e3) / 1e12
+    log(f"[bench] {ms:.3f} ms/step, {value:.2f} TFLOP/s direct-equivalent")
+
+    per_kind = {}
+    for kind, kms in timer.durations():
+        e = per_kind.setdefault(kind, [0, 0.0])
+        e[0] += 1
+        e[1] += kms
+    timer.close()
+    stages = {}
+    for kind, (cnt, tot) in per_kind.items():
+        bound, work, unit = kernel_work(kind, plan, case, 4)
+        avg = tot / cnt
+        ent = {"launches": cnt, "avg_ms": avg, "share": tot / (ms * args.steps)}
+        if bound == "mfma":
+            ent.update(bound="mfma", achieved=work / (avg / 1e3) / 1e12, peak=PEAK["mfma_tflops"]["f32"],
+                       unit="TFLOP/s", work_per_launch=work)
+            ent["frac"] = ent["achieved"] / ent["peak"]
+        elif bound == "hbm":
+            ent.update(bound="hbm", achieved=work / (avg / 1e3) / 1e9, peak=PEAK["hbm_gbs"], unit="GB/s",
+                       work_per_launch=work)
+            ent["frac"] = ent["achieved"] / ent["peak"]
+        stages[kind] = ent
+    dom = max(stages, key=lambda k: stages[k]["avg_ms"] * stages[k]["launches"])
+    d = stages[dom]
+    workload_key = f"fp32_{case.n}x512x512_192to96_{plan.algo_name}_tb{plan.tile_batch}"
+    traffic = load_traffic(workload_key, dom)
+    roofline = {"bound": d.get("bound"), "achieved": d.get("achieved"), "peak": d.get("peak"),
+                "unit": d.get("unit"), "frac": d.get("frac"), "traffic": traffic, "kernel": dom,
+                "avg_ms": d["avg_ms"], "work_per_launch": d.get("work_per_launch")}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a bounded sample")
+        cpu = cpu_baseline(case, args.cpu_seconds)
+        log(f"[bench] oracle {cpu['value']:.4f} TFLOP/s on {cpu['cores']} threads")
+
+    line = {
+        "metric": "conv fwd TFLOP/s (2*N*OH*OW*O*C*KH*KW/s) and % of roofline",
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": value / PAGE_BASELINE_TFLOPS,
+        "dtype": "f32",
+        "data": "synthetic (seeded numpy PCG64: x ~ U[-1,1], w ~ N(0, 1/(9C)))",
+        "config": {"workload": f"conv2d fp32 NHWC N={case.n}, 512x512, C=192 -> O=96, 3x3, stride 1, pad 1",
+                   "algo": plan.algo_name, "tile_batch": plan.tile_batch, "n_tiles": plan.n_tiles,
+                   "ws_limit_bytes": int(ws_limit), "workspace_bytes": int(plan.workspace_bytes),
+                   "parallelism": "single GPU"},
+        "roofline": roofline,
+        "stages": stages,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -110,6 +110,13 @@ def _load():
         fn.restype = ctypes.c_int
         fn.argtypes = [P(Desc), P(Plan), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                        ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p]
+    for fn in (lib.cnhwc_conv2d_fwd_timed, lib.cnhwc_conv3d_fwd_timed):
+        fn.restype = ctypes.c_int
+        fn.argtypes = [P(Desc), P(Plan), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                       ctypes.c_void_p, ctypes.c_uint64, ctypes.c_void_p, P(ctypes.c_void_p),
+                       ctypes.c_int32, P(ctypes.c_int32)]
+    lib.cnhwc_launch_count.restype = ctypes.c_int64
+    lib.cnhwc_launch_count.argtypes = [P(Desc), P(Plan)]
     if lib.cnhwc_abi_version() != 1:
         raise ImportError("libcnhwc.so ABI version mismatch")
     return lib
@@ -118,7 +125,11 @@ def _load():
 lib = _load()
 
 EXPORTED = ("cnhwc_abi_version", "cnhwc_status_string", "cnhwc_conv_select",
-            "cnhwc_winograd_tile_rule", "cnhwc_conv2d_fwd", "cnhwc_conv3d_fwd")
+            "cnhwc_winograd_tile_rule", "cnhwc_conv2d_fwd", "cnhwc_conv3d_fwd",
+            "cnhwc_launch_count", "cnhwc_conv2d_fwd_timed", "cnhwc_conv3d_fwd_timed")
+
+KERNEL_KINDS = {0: "end", 1: "wino_filter", 2: "wino_input", 3: "wino_gemm", 4: "wino_output",
+                5: "implicit_gemm", 6: "unfold", 7: "unfold_gemm"}
 
 
 # ------------------------------------------------------------------ helpers
@@ -218,7 +229,7 @@ def _check_tensor(t, name):
         raise ValueError(f"{name} must be contiguous")
 
 
-def _run(fn, x, w, stride, padding, dilation, opts, out, workspace, plan):
+def _run(fn, x, w, stride, padding, dilation, opts, out, workspace, plan, timer=None):
     _check_tensor(x, "x")
     _check_tensor(w, "w")
     if w.dtype != x.dtype or w.device != x.device:
@@ -239,25 +250,102 @@ def _run(fn, x, w, stride, padding, dilation, opts, out, workspace, plan):
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
     stream = torch.cuda.current_stream(x.device).cuda_stream
-    st = fn(ctypes.byref(desc), ctypes.byref(plan), x.data_ptr(), w.data_ptr(), out.data_ptr(),
-            ws_ptr, ws_len, stream)
+    if timer is None:
+        st = fn(ctypes.byref(desc), ctypes.byref(plan), x.data_ptr(), w.data_ptr(), out.data_ptr(),
+                ws_ptr, ws_len, stream)
+    else:
+        n = lib.cnhwc_launch_count(ctypes.byref(desc), ctypes.byref(plan)) + 1
+        ev, kinds = timer.slots(n)
+        st = fn(ctypes.byref(desc), ctypes.byref(plan), x.data_ptr(), w.data_ptr(), out.data_ptr(),
+                ws_ptr, ws_len, stream, ev, n, kinds)
+        if st == 0:
+            timer.recorded(n)
     if st != 0:
         raise CnhwcError(st, fn.__name__)
     return out
 
 
+class _Hip:
+    """The HIP runtime torch already loaded (same SONAME), for event timing only."""
+    _lib = None
+
+    @classmethod
+    def get(cls):
+        if cls._lib is None:
+            h = ctypes.CDLL("libamdhip64.so.7")
+            h.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+            h.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            h.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+            h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+            cls._lib = h
+        return cls._lib
+
+
+class KernelTimer:
+    """Per-kernel durations of forward calls, from hipEvents the library records
+    on the launch stream right before each kernel (cnhwc_conv*_fwd_timed).
+
+    Pass as ``timer=`` to conv2d/conv3d; after a synchronize, ``durations()``
+    returns [(kind_name, ms), ...] for every kernel of every timed call."""
+
+    def __init__(self):
+        self._pending = []   # (events array, kinds array, n)
+        self._pool = []
+
+    def slots(self, n):
+        hip = _Hip.get()
+        ev = (ctypes.c_void_p * n)()
+        for i in range(n):
+            if self._pool:
+                ev[i] = self._pool.pop()
+            else:
+                e = ctypes.c_void_p()
+                if hip.hipEventCreate(ctypes.byref(e)) != 0:
+                    raise RuntimeError("hipEventCreate failed")
+                ev[i] = e
+        kinds = (ctypes.c_int32 * n)()
+        self._cur = (ev, kinds)
+        return ev, kinds
+
+    def recorded(self, n):
+        ev, kinds = self._cur
+        self._pending.append((ev, kinds, n))
+
+    def durations(self):
+        hip = _Hip.get()
+        out = []
+        for ev, kinds, n in self._pending:
+            hip.hipEventSynchronize(ev[n - 1])
+            for i in range(n - 1):
+                ms = ctypes.c_float()
+                if hip.hipEventElapsedTime(ctypes.byref(ms), ev[i], ev[i + 1]) != 0:
+                    raise RuntimeError("hipEventElapsedTime failed")
+                out.append((KERNEL_KINDS[kinds[i]], float(ms.value)))
+            self._pool.extend(ev[i] for i in range(n))
+        self._pending = []
+        return out
+
+    def close(self):
+        hip = _Hip.get()
+        for e in self._pool:
+            hip.hipEventDestroy(e)
+        self._pool = []
+
+
 def conv2d(x, w, stride=1, padding=0, dilation=1, *, algo="auto", ws_limit=None, tile_batch=None,
-           unfold_rows=None, out=None, workspace=None, plan=None):
+           unfold_rows=None, out=None, workspace=None, plan=None, timer=None):
     """y[N,OH,OW,O] = channels-last conv2d of x[N,H,W,C] with w[O,KH,KW,C]."""
     opts = make_opts(ws_limit, algo, "auto", tile_batch, unfold_rows, x.device if x.is_cuda else None)
-    return _run(lib.cnhwc_conv2d_fwd, x, w, stride, padding, dilation, opts, out, workspace, plan)
+    fn = lib.cnhwc_conv2d_fwd_timed if timer is not None else lib.cnhwc_conv2d_fwd
+    return _run(fn, x, w, stride, padding, dilation, opts, out, workspace, plan, timer)
 
 
 def conv3d(x, w, stride=1, padding=0, dilation=1, *, algo="auto", inner_algo="auto", ws_limit=None,
-           tile_batch=None, unfold_rows=None, out=None, workspace=None, plan=None):
+           tile_batch=None, unfold_rows=None, out=None, workspace=None, plan=None, timer=None):
     """y[N,OD,OH,OW,O] = channels-last conv3d of x[N,D,H,W,C] with w[O,KD,KH,KW,C]."""
     opts = make_opts(ws_limit, algo, inner_algo, tile_batch, unfold_rows, x.device if x.is_cuda else None)
-    return _run(lib.cnhwc_conv3d_fwd, x, w, stride, padding, dilation, opts, out, workspace, plan)
+    fn = lib.cnhwc_conv3d_fwd_timed if timer is not None else lib.cnhwc_conv3d_fwd
+    return _run(fn, x, w, stride, padding, dilation, opts, out, workspace, plan, timer)
 
 
 def direct_flops(x_shape, w_shape, plan):

@@ -29,12 +29,34 @@ bool overlaps(const void* a, uint64_t na, const void* b, uint64_t nb) {
 
 cnhwc_status_t hip_status(int e) { return e == hipSuccess ? CNHWC_OK : CNHWC_ERR_HIP; }
 
+// Optional event recording between kernel launches (timed entry points).
+struct Recorder {
+  void* const* events = nullptr;
+  int32_t* kinds = nullptr;
+  int32_t n = 0;
+  hipStream_t stream = nullptr;
+  void mark(int32_t kind) {
+    if (!events) return;
+    hipEventRecord(reinterpret_cast<hipEvent_t>(events[n]), stream);
+    if (kinds) kinds[n] = kind;
+    ++n;
+  }
+};
+
+// Kernels launched by one 2D conv with this plan.
+int64_t launches_2d(const cnhwc_plan_t& p, int32_t algo) {
+  if (algo == CNHWC_ALGO_IMPLICIT_GEMM) return 1;
+  if (algo == CNHWC_ALGO_UNFOLD_GEMM) return 2 * p.n_chunks;
+  if (algo == CNHWC_ALGO_WINOGRAD) return 1 + 3 * p.n_tiles;
+  return -1;
+}
+
 // One 2D conv (a full 2D call or one depth tap of a 3D call).
 //   x: [n][h][w][c] (dtype), w: rows of K = kh*kw*c elements at stride ldw,
 //   y: [n][oh][ow][o] (dtype), acc: fp32 rows of the same shape (epi != store).
 cnhwc_status_t run_2d(const cnhwc_conv_desc_t& d, const cnhwc_plan_t& p, int32_t algo,
                       const void* x, const void* w, int64_t ldw, void* y, float* acc, int32_t epi,
-                      char* ws, void* stream) {
+                      char* ws, void* stream, Recorder& rec) {
   const uint64_t es = dtype_size(d.dtype);
   const int64_t oh = p.out_h, ow = p.out_w;
   const int64_t m_rows = d.n * oh * ow;
@@ -71,6 +93,7 @@ cnhwc_status_t run_2d(const cnhwc_conv_desc_t& d, const cnhwc_plan_t& p, int32_t
     g.out = y;
     g.ldc = d.o;
     g.acc = acc;
+    rec.mark(CNHWC_KERNEL_IMPLICIT_GEMM);
     return hip_status(gemm_launch(g, stream));
   }
 
@@ -79,6 +102,7 @@ cnhwc_status_t run_2d(const cnhwc_conv_desc_t& d, const cnhwc_plan_t& p, int32_t
     const int64_t rows = p.unfold_rows;
     for (int64_t m0 = 0; m0 < m_rows; m0 += rows) {
       const int64_t r = m0 + rows <= m_rows ? rows : m_rows - m0;
+      rec.mark(CNHWC_KERNEL_UNFOLD);
       int e = unfold_launch(d.dtype, x, d.h, d.w, d.c, oh, ow, d.kh, d.kw, d.stride[1],
                             d.stride[2], d.pad[1], d.pad[2], d.dil[1], d.dil[2], m0, r, kp, ws,
                             stream);
@@ -93,6 +117,7 @@ cnhwc_status_t run_2d(const cnhwc_conv_desc_t& d, const cnhwc_plan_t& p, int32_t
       g.out = static_cast<char*>(y) + uint64_t(m0) * d.o * es;
       g.ldc = d.o;
       g.acc = acc ? acc + m0 * d.o : nullptr;
+      rec.mark(CNHWC_KERNEL_UNFOLD_GEMM);
       e = gemm_launch(g, stream);
       if (e != hipSuccess) return CNHWC_ERR_HIP;
     }
@@ -104,12 +129,14 @@ cnhwc_status_t run_2d(const cnhwc_conv_desc_t& d, const cnhwc_plan_t& p, int32_t
     float* U = reinterpret_cast<float*>(ws + L.off_u);
     float* V = reinterpret_cast<float*>(ws + L.off_v);
     float* Mt = reinterpret_cast<float*>(ws + L.off_m);
+    rec.mark(CNHWC_KERNEL_WINO_FILTER);
     int e = wino_filter_launch(d.dtype, w, ldw, d.o, d.c, L.cs, U, stream);
     if (e != hipSuccess) return CNHWC_ERR_HIP;
     const uint64_t x_elem = uint64_t(d.h) * d.w * d.c * es;  // bytes of one image
     const uint64_t y_elem = uint64_t(oh) * ow * d.o;         // elements of one output image
     for (int64_t n0 = 0; n0 < d.n; n0 += p.tile_batch) {
       const int64_t nb = n0 + p.tile_batch <= d.n ? p.tile_batch : d.n - n0;
+      rec.mark(CNHWC_KERNEL_WINO_INPUT);
       e = wino_input_launch(d.dtype, static_cast<const char*>(x) + n0 * x_elem, nb, d.h, d.w, d.c,
                             L.cs, d.pad[1], d.pad[2], L.tiles_h, L.tiles_w, V, int64_t(L.v_plane),
                             stream);
@@ -133,8 +160,10 @@ cnhwc_status_t run_2d(const cnhwc_conv_desc_t& d, const cnhwc_plan_t& p, int32_t
       q.stride_a = int64_t(L.v_plane);
       q.stride_b = d.o * L.cs;
       q.stride_out = int64_t(L.m_plane);
+      rec.mark(CNHWC_KERNEL_WINO_GEMM);
       e = gemm_launch(q, stream);
       if (e != hipSuccess) return CNHWC_ERR_HIP;
+      rec.mark(CNHWC_KERNEL_WINO_OUTPUT);
       e = wino_output_launch(d.dtype, Mt, int64_t(L.m_plane), nb, oh, ow, d.o, L.tiles_h,
                              L.tiles_w, static_cast<char*>(y) + n0 * y_elem * es,
                              acc ? acc + n0 * y_elem : nullptr, epi, stream);
@@ -169,28 +198,37 @@ cnhwc_status_t validate(const cnhwc_conv_desc_t* desc, const cnhwc_plan_t* plan,
   return CNHWC_OK;
 }
 
-}  // namespace
-}  // namespace cnhwc
-
-extern "C" {
-
-cnhwc_status_t cnhwc_conv2d_fwd(const cnhwc_conv_desc_t* desc, const cnhwc_plan_t* plan,
-                                const void* x, const void* w, void* y, void* workspace,
-                                uint64_t workspace_bytes, void* hip_stream) {
-  using namespace cnhwc;
-  const cnhwc_status_t st = validate(desc, plan, 2, x, w, y, workspace, workspace_bytes);
-  if (st != CNHWC_OK) return st;
-  return run_2d(*desc, *plan, plan->algo, x, w, desc->kh * desc->kw * desc->c, y, nullptr,
-                kEpiStore, static_cast<char*>(workspace), hip_stream);
+// Kernels a whole forward call launches (3D: all taps).
+int64_t plan_launch_count(const cnhwc_conv_desc_t& d, const cnhwc_plan_t& p) {
+  if (p.algo == CNHWC_ALGO_SMALL_KD) {
+    const int64_t per = launches_2d(p, p.inner_algo);
+    return per < 0 ? -1 : per * d.kd;
+  }
+  return launches_2d(p, p.algo);
 }
 
-cnhwc_status_t cnhwc_conv3d_fwd(const cnhwc_conv_desc_t* desc, const cnhwc_plan_t* plan,
-                                const void* x, const void* w, void* y, void* workspace,
-                                uint64_t workspace_bytes, void* hip_stream) {
-  using namespace cnhwc;
+// 2D forward body shared by the plain and timed entry points.
+cnhwc_status_t fwd2d(const cnhwc_conv_desc_t* desc, const cnhwc_plan_t* plan, const void* x,
+                     const void* w, void* y, void* workspace, uint64_t workspace_bytes,
+                     void* stream, Recorder& rec) {
+  const cnhwc_status_t st = validate(desc, plan, 2, x, w, y, workspace, workspace_bytes);
+  if (st != CNHWC_OK) return st;
+  if (rec.events && plan_launch_count(*desc, *plan) + 1 > rec.n) return CNHWC_ERR_INVALID_ARGUMENT;
+  rec.n = 0;
+  const cnhwc_status_t s = run_2d(*desc, *plan, plan->algo, x, w, desc->kh * desc->kw * desc->c, y,
+                                  nullptr, kEpiStore, static_cast<char*>(workspace), stream, rec);
+  if (s == CNHWC_OK) rec.mark(CNHWC_KERNEL_END);
+  return s;
+}
+
+cnhwc_status_t fwd3d(const cnhwc_conv_desc_t* desc, const cnhwc_plan_t* plan, const void* x,
+                     const void* w, void* y, void* workspace, uint64_t workspace_bytes,
+                     void* stream, Recorder& rec) {
   const cnhwc_status_t st = validate(desc, plan, 3, x, w, y, workspace, workspace_bytes);
   if (st != CNHWC_OK) return st;
   if (plan->algo != CNHWC_ALGO_SMALL_KD) return CNHWC_ERR_INTERNAL;
+  if (rec.events && plan_launch_count(*desc, *plan) + 1 > rec.n) return CNHWC_ERR_INVALID_ARGUMENT;
+  rec.n = 0;
   const cnhwc_conv_desc_t& d = *desc;
   const int64_t od = plan->out_d;
   const cnhwc_conv_desc_t f = frame_desc(d, od);
@@ -211,10 +249,64 @@ cnhwc_status_t cnhwc_conv3d_fwd(const cnhwc_conv_desc_t* desc, const cnhwc_plan_
     const void* xt = static_cast<const char*>(x) + uint64_t(t) * frame_bytes;
     const void* wt = static_cast<const char*>(w) + uint64_t(t) * k2 * es;
     const cnhwc_status_t s =
-        run_2d(f, *plan, plan->inner_algo, xt, wt, ldw, y, acc, epi, inner_ws, hip_stream);
+        run_2d(f, *plan, plan->inner_algo, xt, wt, ldw, y, acc, epi, inner_ws, stream, rec);
     if (s != CNHWC_OK) return s;
   }
+  rec.mark(CNHWC_KERNEL_END);
   return CNHWC_OK;
+}
+
+}  // namespace
+}  // namespace cnhwc
+
+extern "C" {
+
+int64_t cnhwc_launch_count(const cnhwc_conv_desc_t* desc, const cnhwc_plan_t* plan) {
+  using namespace cnhwc;
+  if (!desc || !plan) return -1;
+  cnhwc_plan_t ref;
+  if (select_impl(desc, &plan->opts, &ref) != CNHWC_OK || !plan_equal(ref, *plan)) return -1;
+  return plan_launch_count(*desc, *plan);
+}
+
+cnhwc_status_t cnhwc_conv2d_fwd(const cnhwc_conv_desc_t* desc, const cnhwc_plan_t* plan,
+                                const void* x, const void* w, void* y, void* workspace,
+                                uint64_t workspace_bytes, void* hip_stream) {
+  cnhwc::Recorder rec;
+  return cnhwc::fwd2d(desc, plan, x, w, y, workspace, workspace_bytes, hip_stream, rec);
+}
+
+cnhwc_status_t cnhwc_conv3d_fwd(const cnhwc_conv_desc_t* desc, const cnhwc_plan_t* plan,
+                                const void* x, const void* w, void* y, void* workspace,
+                                uint64_t workspace_bytes, void* hip_stream) {
+  cnhwc::Recorder rec;
+  return cnhwc::fwd3d(desc, plan, x, w, y, workspace, workspace_bytes, hip_stream, rec);
+}
+
+cnhwc_status_t cnhwc_conv2d_fwd_timed(const cnhwc_conv_desc_t* desc, const cnhwc_plan_t* plan,
+                                      const void* x, const void* w, void* y, void* workspace,
+                                      uint64_t workspace_bytes, void* hip_stream,
+                                      void* const* events, int32_t n_events, int32_t* kinds) {
+  if (!events || n_events < 1) return CNHWC_ERR_INVALID_ARGUMENT;
+  cnhwc::Recorder rec;
+  rec.events = events;
+  rec.kinds = kinds;
+  rec.n = n_events;
+  rec.stream = reinterpret_cast<hipStream_t>(hip_stream);
+  return cnhwc::fwd2d(desc, plan, x, w, y, workspace, workspace_bytes, hip_stream, rec);
+}
+
+cnhwc_status_t cnhwc_conv3d_fwd_timed(const cnhwc_conv_desc_t* desc, const cnhwc_plan_t* plan,
+                                      const void* x, const void* w, void* y, void* workspace,
+                                      uint64_t workspace_bytes, void* hip_stream,
+                                      void* const* events, int32_t n_events, int32_t* kinds) {
+  if (!events || n_events < 1) return CNHWC_ERR_INVALID_ARGUMENT;
+  cnhwc::Recorder rec;
+  rec.events = events;
+  rec.kinds = kinds;
+  rec.n = n_events;
+  rec.stream = reinterpret_cast<hipStream_t>(hip_stream);
+  return cnhwc::fwd3d(desc, plan, x, w, y, workspace, workspace_bytes, hip_stream, rec);
 }
 
 }  // extern "C"

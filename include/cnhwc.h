@@ -202,6 +202,39 @@ cnhwc_status_t cnhwc_conv3d_fwd(const cnhwc_conv_desc_t* desc, const cnhwc_plan_
                                 const void* x, const void* w, void* y, void* workspace,
                                 uint64_t workspace_bytes, void* hip_stream);
 
+/* Kinds of the kernels a forward call launches (for the timed variants). */
+typedef enum {
+  CNHWC_KERNEL_END = 0,          /* the event after the last kernel */
+  CNHWC_KERNEL_WINO_FILTER = 1,  /* Winograd filter transform (once per call, per 3D tap) */
+  CNHWC_KERNEL_WINO_INPUT = 2,   /* Winograd input transform (per batch tile) */
+  CNHWC_KERNEL_WINO_GEMM = 3,    /* the 64 tile-position GEMMs of one batch tile */
+  CNHWC_KERNEL_WINO_OUTPUT = 4,  /* Winograd output transform (per batch tile) */
+  CNHWC_KERNEL_IMPLICIT_GEMM = 5,
+  CNHWC_KERNEL_UNFOLD = 6,       /* one unfold chunk */
+  CNHWC_KERNEL_UNFOLD_GEMM = 7   /* the dense GEMM of one unfold chunk */
+} cnhwc_kernel_kind_t;
+
+/* Number of kernels a forward call with this plan launches (3D: over all
+ * taps), or -1 if the plan is invalid for the descriptor. */
+int64_t cnhwc_launch_count(const cnhwc_conv_desc_t* desc, const cnhwc_plan_t* plan);
+
+/* Timed variants, for measurement: identical work to cnhwc_conv2d_fwd /
+ * cnhwc_conv3d_fwd, and in addition hipEventRecord(events[i], stream) right
+ * before the i-th kernel launch and once after the last one, with kinds[i] =
+ * its cnhwc_kernel_kind_t (CNHWC_KERNEL_END for the final event).  events:
+ * n_events hipEvent_t handles created by the caller; n_events must be at least
+ * cnhwc_launch_count() + 1 (CNHWC_ERR_INVALID_ARGUMENT otherwise, nothing
+ * queued).  kinds may be NULL.  Elapsed time between events i and i+1 is the
+ * duration of kernel i on the stream. */
+cnhwc_status_t cnhwc_conv2d_fwd_timed(const cnhwc_conv_desc_t* desc, const cnhwc_plan_t* plan,
+                                      const void* x, const void* w, void* y, void* workspace,
+                                      uint64_t workspace_bytes, void* hip_stream,
+                                      void* const* events, int32_t n_events, int32_t* kinds);
+cnhwc_status_t cnhwc_conv3d_fwd_timed(const cnhwc_conv_desc_t* desc, const cnhwc_plan_t* plan,
+                                      const void* x, const void* w, void* y, void* workspace,
+                                      uint64_t workspace_bytes, void* hip_stream,
+                                      void* const* events, int32_t n_events, int32_t* kinds);
+
 #ifdef __cplusplus
 }
 #endif

@@ -16,7 +16,7 @@ HEADER = os.path.join(ROOT, "include", "cnhwc.h")
 
 
 def test_every_declared_function_is_exported():
-    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", " ", open(HEADER).read(), flags=re.S)  # drop comments
     names = set(re.findall(r"^\s*(?:[\w\s\*]+?)\b(cnhwc_\w+)\s*\(", text, re.M))
     assert names == set(cn.EXPORTED)
     for n in names:
