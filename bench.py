@@ -51,6 +51,9 @@ def parse():
     ap.add_argument("--tile-batch", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--suite", default=None,
+                    help="instead of the headline line, time other workloads: "
+                         "comma list of small,wide,sweep,resnet,video or 'all' (one JSON line each)")
     return ap.parse_args()
 
 
@@ -139,8 +142,125 @@ def cpu_baseline(case, seconds):
             "seconds": dt, "outputs_per_s": count * case.o / dt}
 
 
+def _time_call(fn, reps=10, warmup=2):
+    """Average ms per call of fn() on the current stream (torch events)."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        fn()
+    b.record()
+    b.synchronize()
+    return a.elapsed_time(b) / reps
+
+
+def _kernel_split(fn, reps=3):
+    """Per-kernel-kind average ms of fn(timer) over reps calls."""
+    import convolution_nhwc_conv2d_amd as cn
+    import torch
+    t = cn.KernelTimer()
+    for _ in range(reps):
+        fn(t)
+    torch.cuda.synchronize()
+    agg = {}
+    for kind, ms in t.durations():
+        agg[kind] = agg.get(kind, 0.0) + ms / reps
+    t.close()
+    return agg
+
+
+def run_suite(names):
+    """Time the other workloads of the pages; one JSON line per measurement."""
+    import torch
+    import conv_workloads as cw
+    import convolution_nhwc_conv2d_amd as cn
+    dev = torch.device("cuda:0")
+
+    def emit(d):
+        print(json.dumps(d), flush=True)
+
+    def measure(case, algo="auto", inner=None, **kw):
+        x = case.input().to(dev)
+        w = case.weight().to(dev)
+        fn = cn.conv2d if case.nd == 2 else cn.conv3d
+        extra = dict(kw)
+        if inner:
+            extra["inner_algo"] = inner
+        y = fn(x, w, **case.conv_kwargs(), algo=algo, **extra)
+        plan = (cn.plan2d if case.nd == 2 else cn.plan3d)(tuple(x.shape), tuple(w.shape), **case.conv_kwargs(),
+                                                          dtype=x.dtype, algo=algo, **extra)
+        ws = torch.empty(max(1, plan.workspace_bytes), dtype=torch.uint8, device=dev)
+        call = lambda timer=None: fn(x, w, **case.conv_kwargs(), plan=plan, out=y, workspace=ws, timer=timer)
+        ms = _time_call(call)
+        split = _kernel_split(call)
+        flops = cn.direct_flops(tuple(x.shape), tuple(w.shape), plan)
+        return {"workload": case.name, "dtype": case.dtype, "algo": plan.algo_name,
+                "inner_algo": plan.inner_algo_name, "ms": ms, "tflops": flops / ms / 1e9,
+                "kernels_ms": split, "flops": flops}
+
+    if "small" in names:
+        for algo in ("winograd", "implicit_gemm", "unfold_gemm", "auto"):
+            r = measure(cw.small_fp32(), algo)
+            r["suite"] = "small_fp32"
+            emit(r)
+    if "wide" in names:
+        for n in (8, 32, 40, 64):
+            case = cw.wide_fp32(n)
+            for wl in (None, 40_200_000_000, 512 * 10**6):
+                kw = {} if wl is None else {"ws_limit": wl}
+                r = measure(case, **kw)
+                r.update(suite="wide_fp32", ws_limit=wl)
+                emit(r)
+    if "sweep" in names:
+        for dt in ("f16", "bf16"):
+            for c_out in (128, 256, 512, 1024, 2048, 4096):
+                for n in (1, 4, 16, 64):
+                    case = cw.cout_axis(dt, c_out, n)
+                    res = {a: measure(case, a) for a in ("implicit_gemm", "unfold_gemm")}
+                    emit({"suite": "half_cout_axis", "dtype": dt, "c_out": c_out, "m": n * 1024,
+                          "implicit_ms": res["implicit_gemm"]["ms"], "unfold_ms": res["unfold_gemm"]["ms"],
+                          "implicit_tflops": res["implicit_gemm"]["tflops"],
+                          "unfold_tflops": res["unfold_gemm"]["tflops"],
+                          "unfold_over_implicit": res["implicit_gemm"]["ms"] / res["unfold_gemm"]["ms"]})
+            for c_in in (128, 256, 512, 1024):
+                case = cw.cout_axis(dt, 1024, 16, c_in)
+                res = {a: measure(case, a) for a in ("implicit_gemm", "unfold_gemm")}
+                emit({"suite": "half_k_axis", "dtype": dt, "k": 9 * c_in, "c_out": 1024, "m": 16384,
+                      "implicit_tflops": res["implicit_gemm"]["tflops"],
+                      "unfold_tflops": res["unfold_gemm"]["tflops"],
+                      "unfold_over_implicit": res["implicit_gemm"]["ms"] / res["unfold_gemm"]["ms"]})
+    if "resnet" in names:
+        for batch in (1, 8):
+            stages = {}
+            for case, mult, stage in cw.resnet50_layers(batch):
+                r = measure(case)
+                s_ = stages.setdefault(stage, {"ms": 0.0, "flops": 0.0})
+                s_["ms"] += r["ms"] * mult
+                s_["flops"] += r["flops"] * mult
+                emit({"suite": "resnet50_layer", "batch": batch, "layer": case.name, "mult": mult,
+                      "algo": r["algo"], "ms": r["ms"], "tflops": r["tflops"], "kernels_ms": r["kernels_ms"]})
+            tot_ms = sum(v["ms"] for v in stages.values())
+            tot_fl = sum(v["flops"] for v in stages.values())
+            emit({"suite": "resnet50_stack", "batch": batch, "dtype": "f16", "total_ms": tot_ms,
+                  "tflops": tot_fl / tot_ms / 1e9, "stages_ms": {k: v["ms"] for k, v in stages.items()}})
+    if "video" in names:
+        for shape in cw.VIDEO3D_SHAPES:
+            case = cw.video3d(*shape)
+            for inner in ("auto", "implicit_gemm", "unfold_gemm"):
+                r = measure(case, inner=None if inner == "auto" else inner)
+                r["suite"] = "video3d"
+                emit(r)
+
+
 def main():
     args = parse()
+    if args.suite:
+        names = {"small", "wide", "sweep", "resnet", "video"} if args.suite == "all" else set(args.suite.split(","))
+        run_suite(names)
+        return
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
               "(each GPU would run the same plan on its own share of the batch).", file=sys.stderr)

@@ -112,8 +112,9 @@ def small_fp32(seed: int = 1) -> ConvCase:
 
 def wide_fp32(n: int, h: int = 512, w: int = 512, c: int = 192, o: int = 96, seed: int = 2) -> ConvCase:
     """The fp32 Winograd-tiling workload: n x 512x512, 192->96, 3x3, s1, p1."""
+    # the case index does not depend on n: element i is the same for every batch size
     return ConvCase(f"fp32_{n}x{h}x{w}_{c}to{o}", n, h, w, c, o, 3, 3, (1, 1), (1, 1), (1, 1),
-                    "f32", "uniform", "normal", 1.0 / math.sqrt(9 * c), seed, n)
+                    "f32", "uniform", "normal", 1.0 / math.sqrt(9 * c), seed, 0)
 
 
 def half_geometry_grid(dtype: str, c_in: int, seed: int = 3) -> List[ConvCase]:

@@ -13,13 +13,18 @@
 // [O][KD][KH][KW][C] for the 3D decomposition of MLX PR "Decompose small
 // kernel-depth 3D convs into 2D convs", Change): already K-contiguous.
 //
-// Design: 256 threads (4 wavefronts of 64), a BM x BN workgroup tile, BK-deep
-// K chunks staged through double-buffered LDS (16-byte global loads along K,
-// padded LDS rows so the 16-byte fragment reads are bank-conflict free), next
-// chunk prefetched into registers while the matrix cores work on the current
-// one.  fp32 uses v_mfma_f32_32x32x2f32 and fp16/bf16 v_mfma_f32_32x32x16_*.
-// The K order of every output element is fixed by the configuration alone, so
-// results never depend on M, on the launch a row is in, or on the grid.
+// Design: 256 threads (4 wavefronts of 64) own a BM x BN output tile.  K is
+// consumed in chunks of 128 bytes per row (32 fp32 or 64 fp16/bf16).  Each
+// chunk travels global -> registers (16-byte loads along K) -> LDS -> MFMA
+// fragments.  Two register staging sets keep the loads of chunk k+2 in flight
+// while the matrix cores consume chunk k, so global latency is covered by two
+// chunks of MFMA work; LDS is double buffered with one barrier per chunk.
+// LDS rows are 128 bytes with the 16-byte chunk index XOR-swizzled by the row,
+// so both the staging stores and the fragment reads are bank-conflict free
+// without padding.  fp32 uses v_mfma_f32_32x32x2f32 (a 16-byte LDS read feeds
+// four of them), fp16/bf16 v_mfma_f32_32x32x16_*.  The K order of every output
+// element is fixed by the configuration alone, so results never depend on M,
+// on the launch a row is in, or on the grid.
 #include <hip/hip_runtime.h>
 
 #include "internal.hpp"
@@ -28,35 +33,57 @@
 namespace cnhwc {
 namespace {
 
-template <int BM_, int BN_, int BK_, int WM_, int WN_, bool HALF_>
+template <int BM_, int BN_, int WM_, int WN_, bool HALF_, int NSETS_>
 struct TileCfg {
-  static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_;
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
   static constexpr bool HALF = HALF_;
+  static constexpr int BK = HALF_ ? 64 : 32;  // 128 bytes of K per row
+  static constexpr int NSETS = NSETS_;        // register staging sets (prefetch depth)
 };
 
 // A-operand gather modes (kernel template argument).
-constexpr int kLoadDense = 0;     // dense rows, 16-byte vectors
-constexpr int kLoadImplicit = 1;  // NHWC gather, 16-byte vectors (C % VE == 0)
-constexpr int kLoadScalar = 2;    // NHWC gather element by element (any C), scalar B
+constexpr int kLoadDense = 0;        // dense rows, 16-byte vectors
+constexpr int kLoadImplicit = 1;     // NHWC gather, 16-byte vectors (C % VE == 0)
+constexpr int kLoadScalar = 2;       // NHWC gather element by element (any C), scalar B
 constexpr int kLoadDenseScalar = 3;  // dense rows element by element, scalar B
+
+// 16 zero bytes: masked lanes load from here, so the operand loads need no
+// branches (padding taps, rows past M, K past the end).
+// Global-address-space pointers keep the loads global_load (a generic pointer
+// would turn them into flat loads, which also count against the LDS counter).
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+__device__ u32x4 g_zero16 = {0u, 0u, 0u, 0u};
+typedef const u32x4 __attribute__((address_space(1)))* gvec_ptr;
+template <typename T>
+__device__ __forceinline__ gvec_ptr gvec(const T* p) {
+  return (gvec_ptr)(p);
+}
+
+// Physical 16-byte chunk of logical chunk c in LDS row r (8 chunks per row).
+__device__ __forceinline__ int swz(int r, int c) { return (c ^ r ^ (r >> 3)) & 7; }
+
+template <int NA, int NB>
+struct Stage {
+  u32x4 a[NA];
+  u32x4 b[NB];
+};
 
 template <class Cfg, int LOAD, bool BF16>
 __global__ __launch_bounds__(256) void gemm_kernel(const GemmParams p) {
   using E = typename std::conditional<Cfg::HALF, uint16_t, float>::type;
   constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, WM = Cfg::WM, WN = Cfg::WN;
-  constexpr int VE = 16 / sizeof(E);          // elements per 16-byte vector
-  constexpr int KV = BK / VE;                 // vectors per tile row
-  constexpr int LDSK = BK + VE;               // padded LDS row (elements)
-  constexpr int ROW_STEP = 256 / KV;          // rows covered by one pass of 256 threads
-  constexpr int A_VEC = BM / ROW_STEP;
-  constexpr int B_VEC = BN / ROW_STEP;
+  constexpr int VE = 16 / sizeof(E);  // elements per 16-byte chunk
+  constexpr int ROWE = BK;            // elements per LDS row (128 bytes)
+  constexpr int A_VEC = BM / 32;      // 8 threads per row, 32 rows per pass of 256 threads
+  constexpr int B_VEC = BN / 32;
   constexpr int WAVES_N = BN / WN;
   constexpr int FM = WM / 32, FN = WN / 32;
-  static_assert(BM % ROW_STEP == 0 && BN % ROW_STEP == 0, "tile rows");
+  static_assert(BK * sizeof(E) == 128, "128-byte rows");
+  static_assert(BM % 32 == 0 && BN % 32 == 0, "tile rows");
   static_assert((BM / WM) * (BN / WN) == 4, "four wavefronts");
 
-  __shared__ __attribute__((aligned(16))) E lds_a[2][BM * LDSK];
-  __shared__ __attribute__((aligned(16))) E lds_b[2][BN * LDSK];
+  __shared__ __attribute__((aligned(16))) E lds_a[2][BM * ROWE];
+  __shared__ __attribute__((aligned(16))) E lds_b[2][BN * ROWE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -70,36 +97,44 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmParams p) {
   const E* __restrict__ B = reinterpret_cast<const E*>(p.b) + bz * p.stride_b;
   const int64_t M = p.M, N = p.N, K = p.K;
 
-  const int kv = tid % KV;
-  const int row0 = tid / KV;
+  const int kv = tid & 7;   // this thread's 16-byte chunk within a row
+  const int row0 = tid >> 3;
 
   // ---- per-thread A-row state (rows are fixed for the whole K loop)
-  int64_t a_base[A_VEC];   // dense: row offset; implicit: image offset of pixel (n, 0, 0)
+  // dense: a_off = row offset, -1 past M.  implicit: a_off = element offset of
+  // the row's window origin (oh*sh - ph, ow*sw - pw) in image n (may be
+  // negative: only used once the tap is known to be inside the image).
+  int64_t a_off[A_VEC];
   int32_t a_ih0[A_VEC], a_iw0[A_VEC];
 #pragma unroll
   for (int j = 0; j < A_VEC; ++j) {
-    const int64_t m = m0 + row0 + j * ROW_STEP;
+    const int64_t m = m0 + row0 + j * 32;
     if (LOAD == kLoadDense || LOAD == kLoadDenseScalar) {
-      a_base[j] = m < M ? m * p.lda : -1;
+      a_off[j] = m < M ? m * p.lda : -1;
       a_ih0[j] = a_iw0[j] = 0;
+    } else if (m < M) {
+      const int64_t hw = p.oh * p.ow;
+      const int64_t n = m / hw;
+      const int64_t r = m - n * hw;
+      const int64_t oh = r / p.ow;
+      const int64_t ow = r - oh * p.ow;
+      a_ih0[j] = int32_t(oh * p.sh - p.ph);
+      a_iw0[j] = int32_t(ow * p.sw - p.pw);
+      a_off[j] = n * p.h * p.w * p.c + (int64_t(a_ih0[j]) * p.w + a_iw0[j]) * p.c;
     } else {
-      if (m < M) {
-        const int64_t hw = p.oh * p.ow;
-        const int64_t n = m / hw;
-        const int64_t r = m - n * hw;
-        const int64_t oh = r / p.ow;
-        const int64_t ow = r - oh * p.ow;
-        a_base[j] = n * p.h * p.w * p.c;
-        a_ih0[j] = int32_t(oh * p.sh - p.ph);
-        a_iw0[j] = int32_t(ow * p.sw - p.pw);
-      } else {
-        a_base[j] = 0;
-        a_ih0[j] = -0x40000000;  // every tap out of range -> zeros
-        a_iw0[j] = -0x40000000;
-      }
+      a_off[j] = 0;
+      a_ih0[j] = -0x40000000;  // every tap out of range -> zeros
+      a_iw0[j] = -0x40000000;
     }
   }
-  // ---- K-position state of this thread's vector slot (implicit, vector path)
+  // B rows
+  int64_t b_off[B_VEC];
+#pragma unroll
+  for (int j = 0; j < B_VEC; ++j) {
+    const int64_t n = n0 + row0 + j * 32;
+    b_off[j] = n < N ? n * p.ldb : -1;
+  }
+  // ---- K position of the next chunk to load (implicit vector path)
   int32_t k_c = 0, k_kh = 0, k_kw = 0;
   if (LOAD == kLoadImplicit) {
     const int64_t k0 = int64_t(kv) * VE;
@@ -108,83 +143,99 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmParams p) {
     k_kh = int32_t(tap / p.kw);
     k_kw = int32_t(tap - int64_t(k_kh) * p.kw);
   }
-
-  uint4 ra[A_VEC], rb[B_VEC];
-
-  auto load_chunk = [&](int64_t kbase) {
-    const int64_t kk = kbase + int64_t(kv) * VE;
-    // A
-#pragma unroll
-    for (int j = 0; j < A_VEC; ++j) {
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (LOAD == kLoadDense) {
-        if (a_base[j] >= 0 && kk < K) v = *reinterpret_cast<const uint4*>(A + a_base[j] + kk);
-      } else if (LOAD == kLoadImplicit) {
-        const int32_t ih = a_ih0[j] + k_kh * p.dh;
-        const int32_t iw = a_iw0[j] + k_kw * p.dw;
-        if (k_kh < p.kh && uint32_t(ih) < uint32_t(p.h) && uint32_t(iw) < uint32_t(p.w))
-          v = *reinterpret_cast<const uint4*>(A + a_base[j] + (int64_t(ih) * p.w + iw) * p.c + k_c);
-      } else if (LOAD == kLoadDenseScalar) {
-        E e[VE];
-#pragma unroll
-        for (int t = 0; t < VE; ++t)
-          e[t] = (a_base[j] >= 0 && kk + t < K) ? A[a_base[j] + kk + t] : E(0);
-        v = *reinterpret_cast<const uint4*>(e);
-      } else {
-        E e[VE];
-#pragma unroll
-        for (int t = 0; t < VE; ++t) {
-          e[t] = E(0);
-          const int64_t k = kk + t;
-          if (k < K) {
-            const int64_t tap = k / p.c;
-            const int64_t c = k - tap * p.c;
-            const int64_t kh = tap / p.kw;
-            const int64_t kw = tap - kh * p.kw;
-            const int64_t ih = a_ih0[j] + kh * p.dh;
-            const int64_t iw = a_iw0[j] + kw * p.dw;
-            if (ih >= 0 && ih < p.h && iw >= 0 && iw < p.w)
-              e[t] = A[a_base[j] + (ih * p.w + iw) * p.c + c];
-          }
-        }
-        v = *reinterpret_cast<const uint4*>(e);
-      }
-      ra[j] = v;
-    }
-    // B
-#pragma unroll
-    for (int j = 0; j < B_VEC; ++j) {
-      const int64_t n = n0 + row0 + j * ROW_STEP;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (LOAD == kLoadDense || LOAD == kLoadImplicit) {
-        if (n < N && kk < K) v = *reinterpret_cast<const uint4*>(B + n * p.ldb + kk);
-      } else {
-        E e[VE];
-#pragma unroll
-        for (int t = 0; t < VE; ++t) e[t] = (n < N && kk + t < K) ? B[n * p.ldb + kk + t] : E(0);
-        v = *reinterpret_cast<const uint4*>(e);
-      }
-      rb[j] = v;
-    }
-  };
-
   auto advance_k = [&]() {
     if (LOAD == kLoadImplicit) {
       k_c += BK;
       while (k_c >= p.c) {
         k_c -= int32_t(p.c);
-        if (++k_kw == p.kw) { k_kw = 0; ++k_kh; }
+        if (++k_kw == p.kw) {
+          k_kw = 0;
+          ++k_kh;
+        }
       }
     }
   };
 
-  auto store_chunk = [&](int buf) {
+  const gvec_ptr zero = gvec(&g_zero16);
+  using St = Stage<A_VEC, B_VEC>;
+  auto load_chunk = [&](int64_t kbase, St& st) {
+    const int64_t kk = kbase + int64_t(kv) * VE;
+    const bool k_in = kk < K;
+    if constexpr (LOAD == kLoadDense) {
 #pragma unroll
-    for (int j = 0; j < A_VEC; ++j)
-      *reinterpret_cast<uint4*>(&lds_a[buf][(row0 + j * ROW_STEP) * LDSK + kv * VE]) = ra[j];
+      for (int j = 0; j < A_VEC; ++j) {
+        const gvec_ptr ptr = (a_off[j] >= 0 && k_in) ? gvec(A + a_off[j] + kk) : zero;
+        st.a[j] = *ptr;
+      }
+    } else if constexpr (LOAD == kLoadImplicit) {
+      // one tap for the whole chunk slot: shared offset, per-row bounds
+      const int32_t dhh = k_kh * p.dh, dww = k_kw * p.dw;
+      const int64_t tap_off = (int64_t(dhh) * p.w + dww) * p.c + k_c;
+      const bool tap_in = k_kh < p.kh;
 #pragma unroll
-    for (int j = 0; j < B_VEC; ++j)
-      *reinterpret_cast<uint4*>(&lds_b[buf][(row0 + j * ROW_STEP) * LDSK + kv * VE]) = rb[j];
+      for (int j = 0; j < A_VEC; ++j) {
+        const bool ok = tap_in && uint32_t(a_ih0[j] + dhh) < uint32_t(p.h) &&
+                        uint32_t(a_iw0[j] + dww) < uint32_t(p.w);
+        const gvec_ptr ptr = ok ? gvec(A + a_off[j] + tap_off) : zero;
+        st.a[j] = *ptr;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < A_VEC; ++j) {
+        E e[VE];
+        if (LOAD == kLoadDenseScalar) {
+#pragma unroll
+          for (int t = 0; t < VE; ++t)
+            e[t] = (a_off[j] >= 0 && kk + t < K) ? A[a_off[j] + kk + t] : E(0);
+        } else {
+#pragma unroll
+          for (int t = 0; t < VE; ++t) {
+            e[t] = E(0);
+            const int64_t k = kk + t;
+            if (k < K) {
+              const int64_t tap = k / p.c;
+              const int64_t c = k - tap * p.c;
+              const int64_t kh = tap / p.kw;
+              const int64_t kw = tap - kh * p.kw;
+              const int64_t dh_ = kh * p.dh, dw_ = kw * p.dw;
+              const int64_t ih = a_ih0[j] + dh_;
+              const int64_t iw = a_iw0[j] + dw_;
+              if (ih >= 0 && ih < p.h && iw >= 0 && iw < p.w)
+                e[t] = A[a_off[j] + (dh_ * p.w + dw_) * p.c + c];
+            }
+          }
+        }
+        st.a[j] = *reinterpret_cast<const u32x4*>(e);
+      }
+    }
+    if constexpr (LOAD == kLoadDense || LOAD == kLoadImplicit) {
+#pragma unroll
+      for (int j = 0; j < B_VEC; ++j) {
+        const gvec_ptr ptr = (b_off[j] >= 0 && k_in) ? gvec(B + b_off[j] + kk) : zero;
+        st.b[j] = *ptr;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < B_VEC; ++j) {
+        E e[VE];
+#pragma unroll
+        for (int t = 0; t < VE; ++t) e[t] = (b_off[j] >= 0 && kk + t < K) ? B[b_off[j] + kk + t] : E(0);
+        st.b[j] = *reinterpret_cast<const u32x4*>(e);
+      }
+    }
+  };
+
+  auto store_chunk = [&](int buf, const St& st) {
+#pragma unroll
+    for (int j = 0; j < A_VEC; ++j) {
+      const int r = row0 + j * 32;
+      *reinterpret_cast<u32x4*>(&lds_a[buf][r * ROWE + swz(r, kv) * VE]) = st.a[j];
+    }
+#pragma unroll
+    for (int j = 0; j < B_VEC; ++j) {
+      const int r = row0 + j * 32;
+      *reinterpret_cast<u32x4*>(&lds_b[buf][r * ROWE + swz(r, kv) * VE]) = st.b[j];
+    }
   };
 
   v16f acc[FM][FN];
@@ -199,62 +250,112 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmParams p) {
   const int brow = wn * WN + (lane & 31);
   const int khalf = lane >> 5;
 
+  // One K chunk = 4 fragment steps; step kq reads logical 16-byte chunk
+  // 2*kq + khalf of the lane's A and B rows.  Fragments are software
+  // pipelined: step kq+1's LDS reads are issued before step kq's MFMAs (two
+  // fragment register sets; the scheduling barriers keep the compiler from
+  // sinking the reads next to their first use).
+  struct Frags {
+    uint4 a[FM];
+    uint4 b[FN];
+  };
+  auto read_frags = [&](const E* la, const E* lb, int kq, Frags& f) {
+    const int cl = 2 * kq + khalf;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int r = arow + i * 32;
+      f.a[i] = *reinterpret_cast<const uint4*>(la + r * ROWE + swz(r, cl) * VE);
+    }
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int r = brow + j * 32;
+      f.b[j] = *reinterpret_cast<const uint4*>(lb + r * ROWE + swz(r, cl) * VE);
+    }
+  };
+  auto mma = [&](const Frags& f) {
+    if constexpr (!Cfg::HALF) {
+      // lane half h holds k = 8kq + 4h + s; sub-step s pairs k = 8kq + s with 8kq + 4 + s
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(__builtin_bit_cast(v4f, f.a[i])[s],
+                                                             __builtin_bit_cast(v4f, f.b[j])[s],
+                                                             acc[i][j], 0, 0, 0);
+    } else {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = mfma_32x32x16<BF16>(f.a[i], f.b[j], acc[i][j]);
+    }
+  };
   auto compute = [&](int buf) {
     const E* la = lds_a[buf];
     const E* lb = lds_b[buf];
-    if constexpr (!Cfg::HALF) {
-      // 8 K values per step: lane half h holds k = 4h..4h+3 of the step; MFMA
-      // sub-step s pairs k = s (h=0) with k = 4 + s (h=1).
-#pragma unroll
-      for (int kq = 0; kq < BK / 8; ++kq) {
-        v4f af[FM], bf[FN];
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-          af[i] = *reinterpret_cast<const v4f*>(la + (arow + i * 32) * LDSK + kq * 8 + khalf * 4);
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          bf[j] = *reinterpret_cast<const v4f*>(lb + (brow + j * 32) * LDSK + kq * 8 + khalf * 4);
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-#pragma unroll
-          for (int i = 0; i < FM; ++i)
-#pragma unroll
-            for (int j = 0; j < FN; ++j)
-              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[i][s], bf[j][s], acc[i][j], 0, 0, 0);
-      }
-    } else {
-      // 16 K values per MFMA: lane half h holds k = 8h..8h+7.
-#pragma unroll
-      for (int kq = 0; kq < BK / 16; ++kq) {
-        uint4 af[FM], bf[FN];
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-          af[i] = *reinterpret_cast<const uint4*>(la + (arow + i * 32) * LDSK + kq * 16 + khalf * 8);
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          bf[j] = *reinterpret_cast<const uint4*>(lb + (brow + j * 32) * LDSK + kq * 16 + khalf * 8);
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-          for (int j = 0; j < FN; ++j) acc[i][j] = mfma_32x32x16<BF16>(af[i], bf[j], acc[i][j]);
-      }
-    }
+    Frags f0, f1;
+    read_frags(la, lb, 0, f0);
+    read_frags(la, lb, 1, f1);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(f0);
+    __builtin_amdgcn_sched_barrier(0);
+    read_frags(la, lb, 2, f0);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(f1);
+    __builtin_amdgcn_sched_barrier(0);
+    read_frags(la, lb, 3, f1);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(f0);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(f1);
   };
 
   const int64_t nk = (K + BK - 1) / BK;
-  load_chunk(0);
-  store_chunk(0);
-  __syncthreads();
-  for (int64_t kc = 0; kc < nk; ++kc) {
-    const int cur = int(kc & 1);
-    const bool more = kc + 1 < nk;
-    if (more) {
-      advance_k();
-      load_chunk((kc + 1) * BK);
-    }
-    compute(cur);
-    if (more) store_chunk(cur ^ 1);
+  if constexpr (Cfg::NSETS == 1) {
+    // ---- main loop, one staging set: chunk k+1 in flight while chunk k computes
+    St s0;
+    load_chunk(0, s0);
+    store_chunk(0, s0);
     __syncthreads();
+    for (int64_t kc = 0; kc < nk; ++kc) {
+      const int cur = int(kc & 1);
+      const bool more = kc + 1 < nk;
+      if (more) {
+        advance_k();
+        load_chunk((kc + 1) * BK, s0);
+      }
+      compute(cur);
+      if (more) store_chunk(cur ^ 1, s0);
+      __syncthreads();
+    }
+  } else {
+  // ---- main loop, two staging sets: chunk k+2 in flight while chunk k computes
+  St s0, s1;
+  load_chunk(0, s0);
+  store_chunk(0, s0);
+  if (nk > 1) {
+    advance_k();
+    load_chunk(BK, s1);
+  }
+  __syncthreads();
+  for (int64_t kc = 0; kc < nk; kc += 2) {
+    if (kc + 2 < nk) {
+      advance_k();
+      load_chunk((kc + 2) * BK, s0);
+    }
+    compute(0);
+    if (kc + 1 < nk) store_chunk(1, s1);
+    __syncthreads();
+    if (kc + 1 >= nk) break;
+    if (kc + 3 < nk) {
+      advance_k();
+      load_chunk((kc + 3) * BK, s1);
+    }
+    compute(1);
+    if (kc + 2 < nk) store_chunk(0, s0);
+    __syncthreads();
+  }
   }
 
   // ---- epilogue: D[row][col] of a 32x32 block sits in lane l, register r at
@@ -289,8 +390,7 @@ template <class Cfg, bool BF16>
 hipError_t launch_cfg(const GemmParams& p, hipStream_t s) {
   const dim3 grid(unsigned((p.M + Cfg::BM - 1) / Cfg::BM), unsigned((p.N + Cfg::BN - 1) / Cfg::BN),
                   unsigned(p.batch));
-  const int es = Cfg::HALF ? 2 : 4;
-  const int ve = 16 / es;
+  const int ve = Cfg::HALF ? 8 : 4;
   const bool bvec = p.ldb % ve == 0 && p.K % ve == 0;
   if (p.a_mode == kADense) {
     if (bvec && p.lda % ve == 0)
@@ -305,25 +405,27 @@ hipError_t launch_cfg(const GemmParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <class Cfg>
+hipError_t launch_half(const GemmParams& p, hipStream_t s) {
+  return p.dtype == CNHWC_BF16 ? launch_cfg<Cfg, true>(p, s) : launch_cfg<Cfg, false>(p, s);
+}
+
 }  // namespace
 
 int gemm_launch(const GemmParams& p, void* stream) {
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (p.M <= 0 || p.N <= 0) return hipSuccess;
-  const bool bf = p.dtype == CNHWC_BF16;
   const bool f32cfg = p.config >= kCfgF32_N32 && p.config <= kCfgF32_N128;
   if (f32cfg != (p.dtype == CNHWC_F32)) return hipErrorInvalidValue;
   switch (p.config) {
-    case kCfgF32_N32: return launch_cfg<TileCfg<128, 32, 32, 32, 32, false>, false>(p, s);
-    case kCfgF32_N64: return launch_cfg<TileCfg<128, 64, 32, 32, 64, false>, false>(p, s);
-    case kCfgF32_N96: return launch_cfg<TileCfg<128, 96, 32, 32, 96, false>, false>(p, s);
-    case kCfgF32_N128: return launch_cfg<TileCfg<128, 128, 32, 32, 128, false>, false>(p, s);
-    case kCfgH_N64:
-      return bf ? launch_cfg<TileCfg<128, 64, 64, 32, 64, true>, true>(p, s)
-                : launch_cfg<TileCfg<128, 64, 64, 32, 64, true>, false>(p, s);
-    case kCfgH_N128:
-      return bf ? launch_cfg<TileCfg<128, 128, 64, 64, 64, true>, true>(p, s)
-                : launch_cfg<TileCfg<128, 128, 64, 64, 64, true>, false>(p, s);
+    case kCfgF32_N32: return launch_cfg<TileCfg<128, 32, 32, 32, false, 2>, false>(p, s);
+    case kCfgF32_N64: return launch_cfg<TileCfg<128, 64, 32, 64, false, 1>, false>(p, s);
+    case kCfgF32_N96: return launch_cfg<TileCfg<128, 96, 32, 96, false, 1>, false>(p, s);
+    case kCfgF32_N128: return launch_cfg<TileCfg<128, 128, 32, 128, false, 1>, false>(p, s);
+    case kCfgH_128x64: return launch_half<TileCfg<128, 64, 32, 64, true, 2>>(p, s);
+    case kCfgH_128x128: return launch_half<TileCfg<128, 128, 64, 64, true, 1>>(p, s);
+    case kCfgH_256x128: return launch_half<TileCfg<256, 128, 128, 64, true, 1>>(p, s);
+    case kCfgH_128x256: return launch_half<TileCfg<128, 256, 64, 128, true, 1>>(p, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -4,7 +4,7 @@
 #include <cstdint>
 #include <cstddef>
 
-#include "../../include/cnhwc.h"
+#include "cnhwc.h"
 
 namespace cnhwc {
 
@@ -33,14 +33,18 @@ enum GemmConfig : int32_t {
   kCfgF32_N64 = 2,
   kCfgF32_N96 = 3,
   kCfgF32_N128 = 4,
-  // fp16/bf16 operands, v_mfma_f32_32x32x16_{f16,bf16}, BM=128, BK=64
-  kCfgH_N64 = 10,
-  kCfgH_N128 = 11,
+  // fp16/bf16 operands, v_mfma_f32_32x32x16_{f16,bf16}, BK=64; BM x BN
+  kCfgH_128x64 = 10,
+  kCfgH_128x128 = 11,
+  kCfgH_256x128 = 12,
+  kCfgH_128x256 = 13,
 };
 
-// Pick the tile configuration from the element type and the output-channel
-// count (and nothing that depends on the batch or on tiling).
-int32_t pick_gemm_config(int dtype, int64_t n_cols);
+// Pick the tile configuration.  fp32: from the output-channel count only (the
+// Winograd GEMM's configuration must not depend on the batch or its tiling).
+// fp16/bf16: from the GEMM shape (rows M of the whole conv, columns N), by a
+// simple occupancy model over the 256 compute units.
+int32_t pick_gemm_config(int dtype, int64_t m_rows, int64_t n_cols);
 
 // Epilogue: how a GEMM / output-transform result r is written.
 enum EpiMode : int32_t {

@@ -129,7 +129,7 @@ cnhwc_status_t select_2d(const cnhwc_conv_desc_t& d, const int64_t out[3],
       p->budget_bytes = budget;
       p->scratch_per_element = scratch;
       p->workspace_bytes = lay.total;
-      p->kernel_config = pick_gemm_config(CNHWC_F32, d.o);
+      p->kernel_config = pick_gemm_config(CNHWC_F32, 0, d.o);
       return CNHWC_OK;
     }
   }
@@ -146,14 +146,14 @@ cnhwc_status_t select_2d(const cnhwc_conv_desc_t& d, const int64_t out[3],
     p->unfold_rows = rows;
     p->n_chunks = ceil_div(m_rows, rows);
     p->workspace_bytes = align_up(uint64_t(rows) * kp * es, 256);
-    p->kernel_config = pick_gemm_config(d.dtype, d.o);
+    p->kernel_config = pick_gemm_config(d.dtype, m_rows, d.o);
     return CNHWC_OK;
   }
 
   // 3. Implicit GEMM (scratch-free).
   p->algo = p->inner_algo = CNHWC_ALGO_IMPLICIT_GEMM;
   p->workspace_bytes = 0;
-  p->kernel_config = pick_gemm_config(d.dtype, d.o);
+  p->kernel_config = pick_gemm_config(d.dtype, m_rows, d.o);
   return CNHWC_OK;
 }
 
@@ -218,7 +218,7 @@ cnhwc_conv_desc_t frame_desc(const cnhwc_conv_desc_t& d3, int64_t od) {
   return f;
 }
 
-int32_t pick_gemm_config(int dtype, int64_t n_cols) {
+int32_t pick_gemm_config(int dtype, int64_t m_rows, int64_t n_cols) {
   if (dtype == CNHWC_F32) {
     if (n_cols <= 32) return kCfgF32_N32;
     if (n_cols <= 64) return kCfgF32_N64;
@@ -233,7 +233,26 @@ int32_t pick_gemm_config(int dtype, int64_t n_cols) {
     }
     return ids[best];
   }
-  return n_cols <= 64 ? kCfgH_N64 : kCfgH_N128;
+  // Half precision: estimated time = (waves of workgroups over the CUs) x
+  // (cost of one wave).  A wave of slots costs BM*BN*occupancy/efficiency:
+  // `occ` workgroups share a CU, `eff` is the measured relative throughput of
+  // the tile shape on MI355X (128x128 at two workgroups per CU is the fastest
+  // on every large conv of the sweep; the 256-wide tiles need one CU each and
+  // lose about 20%; 128x64 is for problems too small to fill the chip).
+  struct Cand { int32_t id; int64_t bm, bn, occ; double eff; };
+  const Cand cands[4] = {{kCfgH_128x128, 128, 128, 2, 1.00}, {kCfgH_128x256, 128, 256, 1, 0.85},
+                         {kCfgH_256x128, 256, 128, 1, 0.80}, {kCfgH_128x64, 128, 64, 2, 0.70}};
+  constexpr int64_t kCUs = 256;
+  int32_t best = kCfgH_128x128;
+  double best_t = 1e300;
+  for (const Cand& c : cands) {
+    const int64_t tiles = ceil_div(m_rows, c.bm) * ceil_div(n_cols, c.bn);
+    const int64_t slots = kCUs * c.occ;
+    const int64_t waves = ceil_div(tiles, slots);
+    const double t = double(waves) * double(c.bm * c.bn * c.occ) / c.eff;
+    if (t < best_t) { best_t = t; best = c.id; }
+  }
+  return best;
 }
 
 bool plan_equal(const cnhwc_plan_t& a, const cnhwc_plan_t& b) {

@@ -174,7 +174,7 @@ def test_min_tile_rows_fallback_for_spatially_tiny_convs():
     (192, 96, torch.float32, "winograd"), (160, 96, torch.float32, "winograd"),
     (128, 96, torch.float32, "implicit_gemm"), (200, 96, torch.float32, "implicit_gemm"),
     (192, 100, torch.float32, "implicit_gemm"), (256, 256, torch.float16, "implicit_gemm"),
-    (256, 512, torch.float16, "unfold_gemm"), (256, 1024, torch.bfloat16, "unfold_gemm"),
+    (256, 512, torch.float16, "implicit_gemm"), (256, 4096, torch.bfloat16, "implicit_gemm"),
     (256, 4096, torch.float32, "winograd")])
 def test_auto_gate(c, o, dtype, expect):
     assert _p((2, 32, 32, c), (o, 3, 3, c), dtype=dtype).algo_name == expect
@@ -197,12 +197,12 @@ def test_forced_winograd_over_budget():
 
 def test_unfold_rows_cap_and_forced_rows():
     xs, ws = (16, 32, 32, 256), (1024, 3, 3, 256)
-    p = _p(xs, ws, dtype=torch.float16)
+    p = _p(xs, ws, dtype=torch.float16, algo="unfold_gemm")
     k = 9 * 256
     assert p.algo_name == "unfold_gemm"
     assert p.unfold_rows == min(16 * 1024, (256 << 20) // (k * 2))
     assert p.workspace_bytes >= p.unfold_rows * k * 2
-    p = _p(xs, ws, dtype=torch.float16, unfold_rows=1000)
+    p = _p(xs, ws, dtype=torch.float16, algo="unfold_gemm", unfold_rows=1000)
     assert p.unfold_rows == 1000 and p.n_chunks == 17  # 16 x 1000 + a short chunk of 384
 
 
