@@ -51,6 +51,12 @@ def parse():
     ap.add_argument("--tile-batch", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--calib-copy", type=int, default=0,
+                    help="also run one plain device copy of this many bytes (fp32 -> fp32) before the "
+                         "timed work, as the known-size reference for HBM traffic counters")
+    ap.add_argument("--traffic-from", nargs=2, default=None, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="parse two rocprofv3 --pmc counter CSVs (FETCH_SIZE, WRITE_SIZE) of a run made "
+                         "with --calib-copy, write profiles/traffic.json, print it and exit")
     ap.add_argument("--suite", default=None,
                     help="instead of the headline line, time other workloads: "
                          "comma list of small,wide,sweep,resnet,video or 'all' (one JSON line each)")
@@ -140,6 +146,53 @@ def cpu_baseline(case, seconds):
             "sample": f"{count} seeded output pixels (x {case.o} channels) of batch elements 0..{elems - 1}, "
                       f"fp64 direct correlation, {dt:.2f} s wall; CPU {cpu}",
             "seconds": dt, "outputs_per_s": count * case.o / dt}
+
+
+def traffic_from(fetch_csv, write_csv, calib_bytes, workload_key):
+    """Per-launch HBM bytes of each kernel kind from two rocprofv3 --pmc runs,
+    each counter scaled so that the plain copy of `calib_bytes` reads (writes)
+    exactly `calib_bytes`.  Kernel kinds are recognised by kernel name."""
+    import csv
+    kinds = {"wino_input_kernel": "wino_input", "wino_output_kernel": "wino_output",
+             "wino_filter_kernel": "wino_filter", "wino_gemm_resident_kernel": "wino_gemm",
+             "gemm_kernel": "gemm", "unfold_": "unfold"}
+
+    def load(path, counter):
+        per = {}
+        for row in csv.DictReader(open(path)):
+            if row.get("Counter_Name") != counter:
+                continue
+            name = row.get("Kernel_Name", "")
+            kind = next((v for k, v in kinds.items() if k in name), None)
+            if kind is None and ("copy" in name.lower() or "elementwise" in name.lower()):
+                kind = "copy"
+            if kind is None:
+                continue
+            per.setdefault(kind, []).append(float(row["Counter_Value"]))
+        return per
+
+    f = load(fetch_csv, "FETCH_SIZE")
+    w = load(write_csv, "WRITE_SIZE")
+    kib = calib_bytes / 1024.0
+    ffac = kib / max(f["copy"]) if f.get("copy") else None
+    wfac = kib / max(w["copy"]) if w.get("copy") else None
+    out = {"calib_copy_bytes": calib_bytes, "fetch_scale": ffac, "write_scale": wfac,
+           "csrc_hash": csrc_hash(), "kernels": {}}
+    for kind in set(f) | set(w):
+        if kind == "copy":
+            continue
+        fk = sum(f.get(kind, [0])) / max(1, len(f.get(kind, [0])))
+        wk = sum(w.get(kind, [0])) / max(1, len(w.get(kind, [0])))
+        out["kernels"][kind] = {"fetch_kib_raw": fk, "write_kib_raw": wk,
+                                "bytes_per_launch": (fk * (ffac or 1) + wk * (wfac or 1)) * 1024.0,
+                                "csrc_hash": csrc_hash()}
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    data = json.load(open(path)) if os.path.exists(path) else {}
+    data[workload_key] = out["kernels"]
+    data[workload_key + ":calibration"] = {k: v for k, v in out.items() if k != "kernels"}
+    with open(path, "w") as fh:
+        json.dump(data, fh, indent=1, sort_keys=True)
+    return out
 
 
 def _time_call(fn, reps=10, warmup=2):
@@ -257,6 +310,10 @@ def run_suite(names):
 
 def main():
     args = parse()
+    if args.traffic_from:
+        key = f"fp32_{args.batch}x512x512_192to96"
+        print(json.dumps(traffic_from(args.traffic_from[0], args.traffic_from[1], args.calib_copy, key), indent=1))
+        return
     if args.suite:
         names = {"small", "wide", "sweep", "resnet", "video"} if args.suite == "all" else set(args.suite.split(","))
         run_suite(names)
@@ -294,6 +351,13 @@ def main():
     def step(timer=None):
         cn.conv2d(x, w, 1, 1, 1, plan=plan, out=out, workspace=ws, timer=timer)
 
+    if args.calib_copy:
+        src = torch.ones(args.calib_copy // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log(f"[bench] calibration copy of {args.calib_copy} bytes done")
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -332,8 +396,7 @@ def main():
         stages[kind] = ent
     dom = max(stages, key=lambda k: stages[k]["avg_ms"] * stages[k]["launches"])
     d = stages[dom]
-    workload_key = f"fp32_{case.n}x512x512_192to96_{plan.algo_name}_tb{plan.tile_batch}"
-    traffic = load_traffic(workload_key, dom)
+    traffic = load_traffic(f"fp32_{case.n}x512x512_192to96", dom)
     roofline = {"bound": d.get("bound"), "achieved": d.get("achieved"), "peak": d.get("peak"),
                 "unit": d.get("unit"), "frac": d.get("frac"), "traffic": traffic, "kernel": dom,
                 "avg_ms": d["avg_ms"], "work_per_launch": d.get("work_per_launch")}

@@ -141,27 +141,32 @@ cnhwc_status_t run_2d(const cnhwc_conv_desc_t& d, const cnhwc_plan_t& p, int32_t
                             L.cs, d.pad[1], d.pad[2], L.tiles_h, L.tiles_w, V, int64_t(L.v_plane),
                             stream);
       if (e != hipSuccess) return CNHWC_ERR_HIP;
-      GemmParams q;
-      std::memset(&q, 0, sizeof(q));
-      q.dtype = CNHWC_F32;
-      q.a_mode = kADense;
-      q.epi = kEpiStore;
-      q.config = p.kernel_config;
-      q.M = nb * L.t;
-      q.N = d.o;
-      q.K = L.cs;
-      q.a = V;
-      q.lda = L.cs;
-      q.b = U;
-      q.ldb = L.cs;
-      q.out = Mt;
-      q.ldc = d.o;
-      q.batch = kWinoP;
-      q.stride_a = int64_t(L.v_plane);
-      q.stride_b = d.o * L.cs;
-      q.stride_out = int64_t(L.m_plane);
       rec.mark(CNHWC_KERNEL_WINO_GEMM);
-      e = gemm_launch(q, stream);
+      if (p.kernel_config == kCfgWinoResident) {
+        e = wino_gemm_resident_launch(V, U, Mt, nb * L.t, d.o, L.cs, int64_t(L.v_plane),
+                                      int64_t(L.m_plane), stream);
+      } else {
+        GemmParams q;
+        std::memset(&q, 0, sizeof(q));
+        q.dtype = CNHWC_F32;
+        q.a_mode = kADense;
+        q.epi = kEpiStore;
+        q.config = p.kernel_config;
+        q.M = nb * L.t;
+        q.N = d.o;
+        q.K = L.cs;
+        q.a = V;
+        q.lda = L.cs;
+        q.b = U;
+        q.ldb = L.cs;
+        q.out = Mt;
+        q.ldc = d.o;
+        q.batch = kWinoP;
+        q.stride_a = int64_t(L.v_plane);
+        q.stride_b = d.o * L.cs;
+        q.stride_out = int64_t(L.m_plane);
+        e = gemm_launch(q, stream);
+      }
       if (e != hipSuccess) return CNHWC_ERR_HIP;
       rec.mark(CNHWC_KERNEL_WINO_OUTPUT);
       e = wino_output_launch(d.dtype, Mt, int64_t(L.m_plane), nb, oh, ow, d.o, L.tiles_h,

@@ -38,6 +38,8 @@ enum GemmConfig : int32_t {
   kCfgH_128x128 = 11,
   kCfgH_256x128 = 12,
   kCfgH_128x256 = 13,
+  // Winograd tile-position GEMMs: persistent fp32 kernel with U_p resident in LDS
+  kCfgWinoResident = 20,
 };
 
 // Pick the tile configuration.  fp32: from the output-channel count only (the
@@ -82,6 +84,12 @@ struct GemmParams {
 };
 
 int gemm_launch(const GemmParams& p, void* stream);  // returns hipError_t
+
+// Persistent Winograd GEMM (all 64 positions): M_p[rows][o] = V_p[rows][cs] * U_p[o][cs]^T.
+// Applicable when U_p fits in LDS (cs <= 192, o <= 96).
+bool wino_gemm_resident_ok(int64_t cs, int64_t o);
+int wino_gemm_resident_launch(const float* v, const float* u, float* m, int64_t rows, int64_t o,
+                              int64_t cs, int64_t v_plane, int64_t m_plane, void* stream);
 
 // ------------------------------------------------------------ Winograd
 

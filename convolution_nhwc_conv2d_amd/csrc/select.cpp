@@ -129,7 +129,9 @@ cnhwc_status_t select_2d(const cnhwc_conv_desc_t& d, const int64_t out[3],
       p->budget_bytes = budget;
       p->scratch_per_element = scratch;
       p->workspace_bytes = lay.total;
-      p->kernel_config = pick_gemm_config(CNHWC_F32, 0, d.o);
+      // the GEMM configuration depends on (C, O) only, never on the batch tiling
+      p->kernel_config = wino_gemm_resident_ok(lay.cs, d.o) ? int32_t(kCfgWinoResident)
+                                                            : pick_gemm_config(CNHWC_F32, 0, d.o);
       return CNHWC_OK;
     }
   }
