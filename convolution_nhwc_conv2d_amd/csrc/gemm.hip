@@ -13,7 +13,8 @@
 // [O][KD][KH][KW][C] for the 3D decomposition of MLX PR "Decompose small
 // kernel-depth 3D convs into 2D convs", Change): already K-contiguous.
 //
-// Design: 256 threads (4 wavefronts of 64) own a BM x BN output tile.  K is
+// Design: one wavefront per WM x WN sub-tile (4 or 8 per workgroup) of a BM x
+// BN output tile.  K is
 // consumed in chunks of 128 bytes per row (32 fp32 or 64 fp16/bf16).  Each
 // chunk travels global -> registers (16-byte loads along K) -> LDS -> MFMA
 // fragments.  Two register staging sets keep the loads of chunk k+2 in flight
@@ -36,6 +37,7 @@ namespace {
 template <int BM_, int BN_, int WM_, int WN_, bool HALF_, int NSETS_>
 struct TileCfg {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+  static constexpr int NT = 64 * (BM_ / WM_) * (BN_ / WN_);  // threads: one wavefront per WM x WN
   static constexpr bool HALF = HALF_;
   static constexpr int BK = HALF_ ? 64 : 32;  // 128 bytes of K per row
   static constexpr int NSETS = NSETS_;        // register staging sets (prefetch depth)
@@ -69,18 +71,19 @@ struct Stage {
 };
 
 template <class Cfg, int LOAD, bool BF16>
-__global__ __launch_bounds__(256) void gemm_kernel(const GemmParams p) {
+__global__ __launch_bounds__(Cfg::NT) void gemm_kernel(const GemmParams p) {
   using E = typename std::conditional<Cfg::HALF, uint16_t, float>::type;
   constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, WM = Cfg::WM, WN = Cfg::WN;
   constexpr int VE = 16 / sizeof(E);  // elements per 16-byte chunk
   constexpr int ROWE = BK;            // elements per LDS row (128 bytes)
-  constexpr int A_VEC = BM / 32;      // 8 threads per row, 32 rows per pass of 256 threads
-  constexpr int B_VEC = BN / 32;
+  constexpr int NT = Cfg::NT;
+  constexpr int RP = NT / 8;          // rows per pass: 8 threads per 128-byte row
+  constexpr int A_VEC = BM / RP;
+  constexpr int B_VEC = BN / RP;
   constexpr int WAVES_N = BN / WN;
   constexpr int FM = WM / 32, FN = WN / 32;
   static_assert(BK * sizeof(E) == 128, "128-byte rows");
-  static_assert(BM % 32 == 0 && BN % 32 == 0, "tile rows");
-  static_assert((BM / WM) * (BN / WN) == 4, "four wavefronts");
+  static_assert(BM % RP == 0 && BN % RP == 0, "tile rows");
 
   __shared__ __attribute__((aligned(16))) E lds_a[2][BM * ROWE];
   __shared__ __attribute__((aligned(16))) E lds_b[2][BN * ROWE];
@@ -108,7 +111,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmParams p) {
   int32_t a_ih0[A_VEC], a_iw0[A_VEC];
 #pragma unroll
   for (int j = 0; j < A_VEC; ++j) {
-    const int64_t m = m0 + row0 + j * 32;
+    const int64_t m = m0 + row0 + j * RP;
     if (LOAD == kLoadDense || LOAD == kLoadDenseScalar) {
       a_off[j] = m < M ? m * p.lda : -1;
       a_ih0[j] = a_iw0[j] = 0;
@@ -131,7 +134,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmParams p) {
   int64_t b_off[B_VEC];
 #pragma unroll
   for (int j = 0; j < B_VEC; ++j) {
-    const int64_t n = n0 + row0 + j * 32;
+    const int64_t n = n0 + row0 + j * RP;
     b_off[j] = n < N ? n * p.ldb : -1;
   }
   // ---- K position of the next chunk to load (implicit vector path)
@@ -228,12 +231,12 @@ __global__ __launch_bounds__(256) void gemm_kernel(const GemmParams p) {
   auto store_chunk = [&](int buf, const St& st) {
 #pragma unroll
     for (int j = 0; j < A_VEC; ++j) {
-      const int r = row0 + j * 32;
+      const int r = row0 + j * RP;
       *reinterpret_cast<u32x4*>(&lds_a[buf][r * ROWE + swz(r, kv) * VE]) = st.a[j];
     }
 #pragma unroll
     for (int j = 0; j < B_VEC; ++j) {
-      const int r = row0 + j * 32;
+      const int r = row0 + j * RP;
       *reinterpret_cast<u32x4*>(&lds_b[buf][r * ROWE + swz(r, kv) * VE]) = st.b[j];
     }
   };
@@ -394,13 +397,13 @@ hipError_t launch_cfg(const GemmParams& p, hipStream_t s) {
   const bool bvec = p.ldb % ve == 0 && p.K % ve == 0;
   if (p.a_mode == kADense) {
     if (bvec && p.lda % ve == 0)
-      hipLaunchKernelGGL((gemm_kernel<Cfg, kLoadDense, BF16>), grid, dim3(256), 0, s, p);
+      hipLaunchKernelGGL((gemm_kernel<Cfg, kLoadDense, BF16>), grid, dim3(Cfg::NT), 0, s, p);
     else
-      hipLaunchKernelGGL((gemm_kernel<Cfg, kLoadDenseScalar, BF16>), grid, dim3(256), 0, s, p);
+      hipLaunchKernelGGL((gemm_kernel<Cfg, kLoadDenseScalar, BF16>), grid, dim3(Cfg::NT), 0, s, p);
   } else if (p.c % ve == 0 && bvec) {
-    hipLaunchKernelGGL((gemm_kernel<Cfg, kLoadImplicit, BF16>), grid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL((gemm_kernel<Cfg, kLoadImplicit, BF16>), grid, dim3(Cfg::NT), 0, s, p);
   } else {
-    hipLaunchKernelGGL((gemm_kernel<Cfg, kLoadScalar, BF16>), grid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL((gemm_kernel<Cfg, kLoadScalar, BF16>), grid, dim3(Cfg::NT), 0, s, p);
   }
   return hipGetLastError();
 }

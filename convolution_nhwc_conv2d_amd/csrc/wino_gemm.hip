@@ -10,16 +10,20 @@
 //    wavefronts never synchronise again;
 //  - each wavefront owns 32-row blocks (all O columns) and streams its own rows
 //    of V_p straight from global memory into MFMA operand registers, 32 K
-//    values per chunk, the next chunk's loads in flight while the current one
-//    feeds the matrix cores (v_mfma_f32_32x32x2f32);
+//    values per chunk, the loads of the chunk two steps ahead in flight while
+//    the current one feeds the matrix cores (v_mfma_f32_32x32x2f32);
 //  - a finished block's result is stored after the next chunk's loads are
 //    issued; a wavefront that waits on its stores is covered by the other
 //    wavefront sharing its SIMD.
 // MFMA k assignment: in chunk kc, step q (0..3), sub-step s (0..3), lanes of
 // half h (0/1) supply k = 32*kc + 16*h + 4*q + s.  Each lane thus reads 64
 // contiguous bytes of its row per chunk.  The order depends on C and O only,
-// so batch tiling never changes a bit.
+// so batch tiling never changes a bit.  K = C must be a multiple of 32 (at most
+// 192) so a block's chunks unroll completely and every LDS and global address
+// is a per-block base plus an immediate offset.
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 
 #include "internal.hpp"
 #include "device_common.hpp"
@@ -41,32 +45,31 @@ __device__ __forceinline__ gvec_ptr gvec(const T* p) {
 
 __device__ __forceinline__ int swz(int r, int c) { return (c ^ r ^ (r >> 3)) & 7; }
 
-template <int BN>
+template <int BN, int NCH>
 __global__ __launch_bounds__(kResThreads) void wino_gemm_resident_kernel(
     const float* __restrict__ V, const float* __restrict__ U, float* __restrict__ Mout,
-    int64_t rows, int64_t O, int64_t Cs, int64_t v_plane, int64_t m_plane, int32_t wg_per_p) {
+    int64_t rows, int64_t O, int64_t v_plane, int64_t m_plane, int32_t wg_per_p) {
   constexpr int FN = BN / 32;
-  __shared__ __attribute__((aligned(16))) float lds_u[kResMaxChunks * BN * 32];
+  constexpr int64_t Cs = 32 * NCH;  // K, a whole number of 32-wide chunks
+  __shared__ __attribute__((aligned(16))) float lds_u[NCH * BN * 32];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int p = int(blockIdx.x) / wg_per_p;
   const int part = int(blockIdx.x) - p * wg_per_p;
-  const int nch = int((Cs + 31) / 32);
   const float* __restrict__ A = V + int64_t(p) * v_plane;
   const float* __restrict__ B = U + int64_t(p) * O * Cs;
   float* __restrict__ C = Mout + int64_t(p) * m_plane;
   const gvec_ptr zero = gvec(&g_res_zero16);
 
   // ---- U_p -> LDS, [chunk][row][32 floats], 16-byte pieces swizzled by row;
-  // zeros past O or C.  Every thread takes part, then the one barrier.
-  for (int idx = tid; idx < nch * BN * 8; idx += kResThreads) {
+  // zeros past O.  Every thread takes part, then the one barrier.
+  for (int idx = tid; idx < NCH * BN * 8; idx += kResThreads) {
     const int kc = idx / (BN * 8);
     const int r = (idx >> 3) % BN;
     const int v = idx & 7;
-    const int64_t k = int64_t(kc) * 32 + v * 4;
-    const gvec_ptr src = (r < O && k < Cs) ? gvec(B + r * Cs + k) : zero;
+    const gvec_ptr src = r < O ? gvec(B + r * Cs + kc * 32 + v * 4) : zero;
     *reinterpret_cast<u32x4*>(&lds_u[(kc * BN + r) * 32 + swz(r, v) * 4]) = *src;
   }
   __syncthreads();
@@ -84,111 +87,130 @@ __global__ __launch_bounds__(kResThreads) void wino_gemm_resident_kernel(
   const int i = lane & 31;  // row within the block / column within a 32-column group
   const int h = lane >> 5;  // k half
 
-  // A operand of one chunk: 4 x 16 bytes of row (blk*32 + i), k = 32kc + 16h + 4q
-  auto load_a = [&](int64_t blk, int kc, u32x4 (&a)[4]) {
-    const int64_t m = blk * 32 + i;
-    const int64_t k0 = int64_t(kc) * 32 + h * 16;
-    const float* row = A + m * Cs;
+  // LDS byte offsets of this lane's B pieces (step q, column group j) within a chunk
+  int boff[4][FN];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int64_t k = k0 + 4 * q;
-      const gvec_ptr src = (m < rows && k < Cs) ? gvec(row + k) : zero;
-      a[q] = *src;
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int r = i + 32 * j;
+      boff[q][j] = (r * 32 + swz(r, 4 * h + q) * 4) * 4;
     }
+  const char* lu = reinterpret_cast<const char*>(lds_u);
+
+  // Row pointer of a block: rows past the end are clamped to the last row (in
+  // bounds; their results are never stored, and rows do not mix in the MFMA).
+  auto rowptr = [&](int64_t blk) {
+    int64_t m = blk * 32 + i;
+    m = m < rows ? m : rows - 1;
+    return A + m * Cs + 16 * h;
+  };
+  // A operand of chunk kc: 4 x 16 bytes at k = 32kc + 16h + 4q
+  auto load_a = [&](const float* rp, int kc, u32x4 (&a)[4]) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) a[q] = *gvec(rp + kc * 32 + 4 * q);
   };
 
   v16f acc[FN];
-#pragma unroll
-  for (int j = 0; j < FN; ++j)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[j][r] = 0.0f;
-
-  // one chunk: B fragments from the resident U_p, 4 steps x 4 sub-steps x FN MFMAs
-  auto compute = [&](const u32x4 (&a)[4], int kc) {
-    const float* lu = lds_u + kc * BN * 32;
+  // one chunk: B fragments from the resident U_p, 4 steps x 4 sub-steps x FN MFMAs;
+  // the block's first MFMA per accumulator starts from zero
+  auto compute = [&](const u32x4 (&a)[4], int kc, bool first_chunk) {
+    const char* base = lu + kc * BN * 128;
     u32x4 b0[FN], b1[FN];
     auto read_b = [&](int q, u32x4 (&b)[FN]) {
-      const int cl = 4 * h + q;  // logical 16-byte piece of the 128-byte row slice
 #pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int r = i + 32 * j;
-        b[j] = *reinterpret_cast<const u32x4*>(lu + r * 32 + swz(r, cl) * 4);
-      }
+      for (int j = 0; j < FN; ++j) b[j] = *reinterpret_cast<const u32x4*>(base + boff[q][j]);
     };
-    auto mma = [&](const u32x4& av, const u32x4 (&b)[FN]) {
+    auto mma = [&](const u32x4& av, const u32x4 (&b)[FN], bool zero_start) {
 #pragma unroll
       for (int s = 0; s < 4; ++s)
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
+        for (int j = 0; j < FN; ++j) {
+          const v16f cin = (zero_start && s == 0) ? v16f{} : acc[j];
           acc[j] = __builtin_amdgcn_mfma_f32_32x32x2f32(__builtin_bit_cast(v4f, av)[s],
-                                                        __builtin_bit_cast(v4f, b[j])[s], acc[j], 0,
-                                                        0, 0);
+                                                        __builtin_bit_cast(v4f, b[j])[s], cin, 0, 0, 0);
+        }
     };
     read_b(0, b0);
     read_b(1, b1);
     __builtin_amdgcn_sched_barrier(0);
-    mma(a[0], b0);
+    mma(a[0], b0, first_chunk);
     __builtin_amdgcn_sched_barrier(0);
     read_b(2, b0);
     __builtin_amdgcn_sched_barrier(0);
-    mma(a[1], b1);
+    mma(a[1], b1, false);
     __builtin_amdgcn_sched_barrier(0);
     read_b(3, b1);
     __builtin_amdgcn_sched_barrier(0);
-    mma(a[2], b0);
+    mma(a[2], b0, false);
     __builtin_amdgcn_sched_barrier(0);
-    mma(a[3], b1);
+    mma(a[3], b1, false);
   };
 
   // D[row][col] of a 32x32 block: lane l, register r -> row 8*(r/4) + 4*(l/32) + r%4, col l%32
-  auto store_block = [&](const v16f (&res)[FN], int64_t blk) {
+  auto store_block = [&](int64_t blk) {
+    float* cp = C + (blk * 32 + h * 4) * O + i;
+    const bool full = blk * 32 + 32 <= rows;
 #pragma unroll
     for (int j = 0; j < FN; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int64_t row = blk * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
-        const int64_t col = j * 32 + i;
-        if (row < rows && col < O) C[row * O + col] = res[j][r];
+        const int rr = (r >> 2) * 8 + (r & 3);
+        if (32 * j + i < O && (full || blk * 32 + h * 4 + rr < rows)) cp[rr * O + 32 * j] = acc[j][r];
       }
   };
 
-  // (blk, kc): the chunk being computed; (lblk, lkc): the next chunk to load.
-  // Unrolled by two so the two operand register sets stay static.
-  int64_t blk = first, lblk = first, left = nmine;  // `left`: blocks not yet finished
-  int kc = 0, lkc = 0;
-  auto step = [&](const u32x4 (&cur)[4], u32x4 (&nxt)[4]) -> bool {
-    if (++lkc == nch) {
-      lkc = 0;
-      lblk += kResWaves;
-    }
-    const bool more = !(left == 1 && kc == nch - 1);
-    if (more) load_a(lblk, lkc, nxt);
-    compute(cur, kc);
-    if (kc == nch - 1) {
-      store_block(acc, blk);
+  // Blocks in order.  Three operand sets: chunk c of a block lives in set
+  // (c + PAR) % 3, and the loads of the chunk two steps ahead (possibly in the
+  // next block) are issued before each chunk's MFMAs.
+  u32x4 a0[4], a1[4], a2[4];
+  auto set = [&](int k) -> u32x4 (&)[4] { return k == 0 ? a0 : (k == 1 ? a1 : a2); };
+  int64_t b = 0;
+  const float* rp = rowptr(first);
+  const float* rpn = nmine > 1 ? rowptr(first + kResWaves) : rp;
+  load_a(rp, 0, a0);
+  if (NCH > 1) load_a(rp, 1, a1);
+  else if (nmine > 1) load_a(rpn, 0, a1);
+  auto block = [&](auto par_tag) {
+    constexpr int PAR = decltype(par_tag)::value;
+    const int64_t blk = first + b * kResWaves;
+    const bool has_next = b + 1 < nmine;
+    const bool has_next2 = b + 2 < nmine;
+    const float* rpn2 = has_next2 ? rowptr(blk + 2 * kResWaves) : rpn;
 #pragma unroll
-      for (int j = 0; j < FN; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[j][r] = 0.0f;
-      --left;
-      blk += kResWaves;
-      kc = 0;
-    } else {
-      ++kc;
+    for (int c = 0; c < NCH; ++c) {
+      // chunk c + 2 of this block, or chunk c + 2 - NCH of the next one(s)
+      constexpr int dummy = 0;
+      (void)dummy;
+      const int ahead = c + 2;
+      if (ahead < NCH) {
+        load_a(rp, ahead, set((ahead + PAR) % 3));
+      } else if (ahead - NCH < NCH) {
+        if (has_next) load_a(rpn, ahead - NCH, set((ahead + PAR) % 3));
+      } else {
+        if (has_next2) load_a(rpn2, ahead - 2 * NCH, set((ahead + PAR) % 3));
+      }
+      compute(set((c + PAR) % 3), c, c == 0);
     }
-    return more;
+    store_block(blk);
+    rp = rpn;
+    rpn = rpn2;
+    ++b;
+    return has_next;
   };
-
-  u32x4 a0[4], a1[4];
-  load_a(lblk, lkc, a0);
-  while (step(a0, a1) && step(a1, a0)) {
+  while (true) {
+    if (!block(std::integral_constant<int, 0>{})) break;
+    if constexpr (NCH % 3 != 0) {
+      if (!block(std::integral_constant<int, NCH % 3>{})) break;
+      if (!block(std::integral_constant<int, (2 * NCH) % 3>{})) break;
+    }
   }
 }
 
 }  // namespace
 
 bool wino_gemm_resident_ok(int64_t cs, int64_t o) {
-  return cs <= kResMaxChunks * 32 && o <= 96;
+  return cs % 32 == 0 && cs <= kResMaxChunks * 32 && o <= 96;
 }
 
 int wino_gemm_resident_launch(const float* v, const float* u, float* m, int64_t rows, int64_t o,
@@ -199,15 +221,19 @@ int wino_gemm_resident_launch(const float* v, const float* u, float* m, int64_t 
   // one workgroup per CU: 256 workgroups over the 64 tile positions
   const int wg_per_p = 4;
   const dim3 grid(unsigned(kWinoP * wg_per_p));
-  if (o <= 32)
-    hipLaunchKernelGGL((wino_gemm_resident_kernel<32>), grid, dim3(kResThreads), 0, s, v, u, m, rows,
-                       o, cs, v_plane, m_plane, wg_per_p);
-  else if (o <= 64)
-    hipLaunchKernelGGL((wino_gemm_resident_kernel<64>), grid, dim3(kResThreads), 0, s, v, u, m, rows,
-                       o, cs, v_plane, m_plane, wg_per_p);
-  else
-    hipLaunchKernelGGL((wino_gemm_resident_kernel<96>), grid, dim3(kResThreads), 0, s, v, u, m, rows,
-                       o, cs, v_plane, m_plane, wg_per_p);
+  const int nch = int(cs / 32);
+  const int bn = o <= 32 ? 32 : (o <= 64 ? 64 : 96);
+#define CNHWC_RES_LAUNCH(BN_, NCH_)                                                          \
+  if (bn == BN_ && nch == NCH_)                                                              \
+    hipLaunchKernelGGL((wino_gemm_resident_kernel<BN_, NCH_>), grid, dim3(kResThreads), 0, s, v, u, \
+                       m, rows, o, v_plane, m_plane, wg_per_p);
+  CNHWC_RES_LAUNCH(32, 1) CNHWC_RES_LAUNCH(32, 2) CNHWC_RES_LAUNCH(32, 3)
+  CNHWC_RES_LAUNCH(32, 4) CNHWC_RES_LAUNCH(32, 5) CNHWC_RES_LAUNCH(32, 6)
+  CNHWC_RES_LAUNCH(64, 1) CNHWC_RES_LAUNCH(64, 2) CNHWC_RES_LAUNCH(64, 3)
+  CNHWC_RES_LAUNCH(64, 4) CNHWC_RES_LAUNCH(64, 5) CNHWC_RES_LAUNCH(64, 6)
+  CNHWC_RES_LAUNCH(96, 1) CNHWC_RES_LAUNCH(96, 2) CNHWC_RES_LAUNCH(96, 3)
+  CNHWC_RES_LAUNCH(96, 4) CNHWC_RES_LAUNCH(96, 5) CNHWC_RES_LAUNCH(96, 6)
+#undef CNHWC_RES_LAUNCH
   return hipGetLastError();
 }
 

@@ -48,6 +48,18 @@ __device__ __forceinline__ void cmatvec(const float (&mat)[R][C], const float (&
   }
 }
 
+// Workgroups are dispatched round-robin over the 8 XCDs (each with its own L2).
+// Remap so that XCD x runs one contiguous range of logical workgroups:
+// neighbouring tiles, whose 8x8 windows overlap by two pixels, then share an
+// L2.  A bijection on [0, gridDim.x) for round-robin dispatch.
+__device__ __forceinline__ int64_t xcd_block(int64_t bid, int64_t nwg) {
+  constexpr int64_t kXcd = 8;
+  const int64_t x = bid % kXcd, k = bid / kXcd;
+  const int64_t q = nwg / kXcd, r = nwg % kXcd;
+  const int64_t start = x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q;
+  return start + k;
+}
+
 template <typename E, bool BF16>
 __global__ __launch_bounds__(256) void wino_filter_kernel(const E* __restrict__ w, int64_t ldo,
                                                           int64_t O, int64_t C, int64_t Cs,
@@ -88,7 +100,7 @@ __global__ __launch_bounds__(256) void wino_input_kernel(const E* __restrict__ x
                                                          int32_t ph, int32_t pw, int64_t TH,
                                                          int64_t TW, float* __restrict__ V,
                                                          int64_t plane, int64_t total) {
-  const int64_t t = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t t = xcd_block(blockIdx.x, gridDim.x) * 256 + threadIdx.x;
   if (t >= total) return;
   const int64_t r = t / Cs, c = t - r * Cs;
   const int64_t T = TH * TW;
@@ -131,7 +143,7 @@ __global__ __launch_bounds__(256) void wino_output_kernel(const float* __restric
                                                           int64_t O, int64_t TH, int64_t TW,
                                                           E* __restrict__ y, float* __restrict__ acc,
                                                           int32_t epi, int64_t total) {
-  const int64_t t = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t t = xcd_block(blockIdx.x, gridDim.x) * 256 + threadIdx.x;
   if (t >= total) return;
   const int64_t r = t / O, o = t - r * O;
   const int64_t T = TH * TW;
@@ -178,6 +190,7 @@ __global__ __launch_bounds__(256) void wino_output_kernel(const float* __restric
 }
 
 inline unsigned blocks_for(int64_t total) { return unsigned((total + 255) / 256); }
+
 
 }  // namespace
 
