@@ -51,7 +51,8 @@ class Desc(ctypes.Structure):
 class Opts(ctypes.Structure):
     _fields_ = [("ws_limit_bytes", ctypes.c_uint64), ("force_algo", ctypes.c_int32),
                 ("force_inner_algo", ctypes.c_int32), ("force_tile_batch", ctypes.c_int64),
-                ("force_unfold_rows", ctypes.c_int64)]
+                ("force_unfold_rows", ctypes.c_int64), ("force_gemm_config", ctypes.c_int32),
+                ("reserved_opts", ctypes.c_int32)]
 
 
 class Plan(ctypes.Structure):
@@ -117,7 +118,7 @@ def _load():
                        ctypes.c_int32, P(ctypes.c_int32)]
     lib.cnhwc_launch_count.restype = ctypes.c_int64
     lib.cnhwc_launch_count.argtypes = [P(Desc), P(Plan)]
-    if lib.cnhwc_abi_version() != 1:
+    if lib.cnhwc_abi_version() != 2:
         raise ImportError("libcnhwc.so ABI version mismatch")
     return lib
 
@@ -182,7 +183,7 @@ def default_ws_limit(device=None):
 
 
 def make_opts(ws_limit=None, algo="auto", inner_algo="auto", tile_batch=None, unfold_rows=None,
-              device=None):
+              gemm_config=None, device=None):
     o = Opts()
     o.ws_limit_bytes = int(ws_limit) if ws_limit is not None else default_ws_limit(device)
     o.force_algo = ALGOS[algo]
@@ -191,6 +192,7 @@ def make_opts(ws_limit=None, algo="auto", inner_algo="auto", tile_batch=None, un
         tile_batch = int(os.environ["CNHWC_TILE_BATCH"])
     o.force_tile_batch = int(tile_batch or 0)
     o.force_unfold_rows = int(unfold_rows or 0)
+    o.force_gemm_config = int(gemm_config or 0)
     return o
 
 
@@ -333,17 +335,20 @@ class KernelTimer:
 
 
 def conv2d(x, w, stride=1, padding=0, dilation=1, *, algo="auto", ws_limit=None, tile_batch=None,
-           unfold_rows=None, out=None, workspace=None, plan=None, timer=None):
+           unfold_rows=None, gemm_config=None, out=None, workspace=None, plan=None, timer=None):
     """y[N,OH,OW,O] = channels-last conv2d of x[N,H,W,C] with w[O,KH,KW,C]."""
-    opts = make_opts(ws_limit, algo, "auto", tile_batch, unfold_rows, x.device if x.is_cuda else None)
+    opts = make_opts(ws_limit, algo, "auto", tile_batch, unfold_rows, gemm_config=gemm_config,
+                     device=x.device if x.is_cuda else None)
     fn = lib.cnhwc_conv2d_fwd_timed if timer is not None else lib.cnhwc_conv2d_fwd
     return _run(fn, x, w, stride, padding, dilation, opts, out, workspace, plan, timer)
 
 
 def conv3d(x, w, stride=1, padding=0, dilation=1, *, algo="auto", inner_algo="auto", ws_limit=None,
-           tile_batch=None, unfold_rows=None, out=None, workspace=None, plan=None, timer=None):
+           tile_batch=None, unfold_rows=None, gemm_config=None, out=None, workspace=None, plan=None,
+           timer=None):
     """y[N,OD,OH,OW,O] = channels-last conv3d of x[N,D,H,W,C] with w[O,KD,KH,KW,C]."""
-    opts = make_opts(ws_limit, algo, inner_algo, tile_batch, unfold_rows, x.device if x.is_cuda else None)
+    opts = make_opts(ws_limit, algo, inner_algo, tile_batch, unfold_rows, gemm_config=gemm_config,
+                     device=x.device if x.is_cuda else None)
     fn = lib.cnhwc_conv3d_fwd_timed if timer is not None else lib.cnhwc_conv3d_fwd
     return _run(fn, x, w, stride, padding, dilation, opts, out, workspace, plan, timer)
 

@@ -429,6 +429,7 @@ int gemm_launch(const GemmParams& p, void* stream) {
     case kCfgH_128x128: return launch_half<TileCfg<128, 128, 64, 64, true, 1>>(p, s);
     case kCfgH_256x128: return launch_half<TileCfg<256, 128, 128, 64, true, 1>>(p, s);
     case kCfgH_128x256: return launch_half<TileCfg<128, 256, 64, 128, true, 1>>(p, s);
+    case kCfgH_256x256: return gemm_lds_launch(p, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -1,0 +1,424 @@
+// Large-tile fp16/bf16 MFMA GEMM for gfx950 with direct global -> LDS loads.
+//
+// C[M x N] = A[M x K] * B[N x K]^T for the implicit-GEMM conv (MLX PR "Bound
+// winograd conv2d working set by tiling the batch", Fix: the scratch-free
+// fallback; MLX PR "Use the explicit gemm for wide convs on neural
+// accelerators", intro: the wide-channel convs) and the per-tap 2D convs of the
+// 3D decomposition (MLX PR "Decompose small kernel-depth 3D convs into 2D
+// convs", Change).  A is gathered from the NHWC image (or read as dense rows
+// after an unfold), B is the weight rows [O][KH][KW][C], K-contiguous.
+//
+// Why a second GEMM core: with 64 x 64 wavefront tiles the MFMA fragments read
+// from LDS alone take about one LDS cycle per matrix-core cycle, and staging
+// the operands through registers into LDS adds half as much again, more than
+// one CU's LDS can serve.  Here:
+//  - a workgroup of 4 wavefronts owns a 256 x 256 output tile, each wavefront
+//    a 128 x 128 quadrant (16 accumulating 32x32 blocks, 256 fp32 per lane),
+//    which halves the LDS bytes read per MFMA;
+//  - operands go from global memory straight into LDS
+//    (global_load_lds_dwordx4: lane l's 16 bytes land at the wave's LDS base
+//    + 16 l), so no VGPRs and no ds_write are spent on staging;
+//  - K advances in chunks of 32 elements (64-byte LDS rows) through a ring of
+//    four LDS stages: while a chunk feeds the matrix cores up to three more
+//    are in flight, and one barrier per chunk orders reuse of a stage;
+//  - each chunk's loads, their address arithmetic and the fragment reads are
+//    interleaved with the MFMAs (scheduling groups), and the loop body is one
+//    basic block, so the matrix cores are not left idle while they issue.
+// LDS rows hold four 16-byte pieces, the piece index XOR-ed with bits 1..2 of
+// the row, so the 8 lanes served per LDS cycle (8 consecutive rows, same
+// logical piece) hit 8 distinct 16-byte bank groups.  Since a lane's LDS
+// destination is fixed by its lane index, the swizzle is applied on the
+// global side: lane l fetches the logical piece that belongs at its slot.
+//
+// MFMA: v_mfma_f32_32x32x16_{f16,bf16}; in K step q (0..1) of a chunk, lanes
+// 0..31 supply k = 16 q + 0..7 and lanes 32..63 k = 16 q + 8..15 of their row.
+// The K order of every output is fixed (chunk by chunk, step by step), so the
+// result does not depend on M, on the grid or on the launch a row is in.
+#include <hip/hip_runtime.h>
+
+#include "internal.hpp"
+#include "device_common.hpp"
+
+namespace cnhwc {
+namespace {
+
+constexpr int kBM = 256, kBN = 256, kBK = 32;  // tile; K chunk in elements (64 bytes)
+constexpr int kThreads = 256;
+constexpr int kRowBytes = kBK * 2;
+constexpr int kStageBytes = kBM * kRowBytes;  // 16 KB per operand and stage
+constexpr int kLoadsA = kBM * kRowBytes / (kThreads * 16);  // 16-byte loads per thread per chunk
+constexpr int kLoadsB = kBN * kRowBytes / (kThreads * 16);
+constexpr int kLoads = kLoadsA + kLoadsB;
+constexpr int kRowsPerLoad = 64 * 16 / kRowBytes;  // rows one wavefront load instruction fills
+#ifndef CNHWC_LDS_STAGES
+#define CNHWC_LDS_STAGES 4
+#endif
+constexpr int kStages = CNHWC_LDS_STAGES;
+static_assert(kStages >= 4 && kStages <= 5, "stage ring");
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef const u32x4 __attribute__((address_space(1)))* gvec_ptr;
+__device__ u32x4 g_lds_zero16 = {0u, 0u, 0u, 0u};
+template <typename T>
+__device__ __forceinline__ gvec_ptr gvec(const T* p) {
+  return (gvec_ptr)(p);
+}
+
+constexpr int64_t kGroupM = 8;
+
+// Bijection on [0, n): the workgroups dispatched to XCD x (ids x, x + 8, ...)
+// get one contiguous range of tile indices.
+__device__ __forceinline__ int64_t xcd_tile(int64_t bid, int64_t n) {
+  constexpr int64_t kXcd = 8;
+  const int64_t x = bid % kXcd, k = bid / kXcd;
+  const int64_t q = n / kXcd, r = n % kXcd;
+  return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + k;
+}
+
+// The stage ring lives in two LDS objects, A rows and B rows: the compiler
+// then tags every fragment read with the object it reads.  The loads into LDS
+// address the ring through a plain integer LDS address (see lds_addr), which
+// carries no such tag, so the compiler adds no wait of its own before a
+// fragment read; the explicit vmcnt waits and barriers below order them.
+constexpr int kRingBytes = kStages * kBM * kRowBytes;  // per operand (kBM == kBN)
+__shared__ __attribute__((aligned(1024))) uint8_t g_ring_a[kRingBytes];
+__shared__ __attribute__((aligned(1024))) uint8_t g_ring_b[kRingBytes];
+
+typedef void __attribute__((address_space(3)))* lds_ptr;
+__device__ __forceinline__ uint32_t lds_base(const uint8_t* p) {
+  typedef const uint8_t __attribute__((address_space(3)))* lds_cptr;
+  uint32_t v = uint32_t(reinterpret_cast<uintptr_t>((lds_cptr)p));
+  asm volatile("" : "+s"(v));  // opaque to constant folding; emits no instruction
+  return v;
+}
+__device__ __forceinline__ lds_ptr lds_addr(uint32_t a) {
+  return reinterpret_cast<lds_ptr>(uintptr_t(a));
+}
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+struct Frag {
+  uint4 a[4];
+  uint4 b[4];
+};
+
+template <bool BF16, bool IMPLICIT>
+__global__ __launch_bounds__(kThreads, 1) void gemm_lds_kernel(const GemmParams p) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
+  const int wm = wave >> 1, wn = wave & 1;
+  const int64_t M = p.M, N = p.N, K = p.K;
+
+  // Tile order: workgroups are dealt round-robin to the 8 XCDs (one L2
+  // each).  XCD x takes a contiguous range of tile indices, walked in groups
+  // of kGroupM row tiles: the 32 workgroups an XCD runs at once then cover
+  // about 8 row tiles x 4 column tiles and share their A and B rows in L2.
+  const int64_t mt = (M + kBM - 1) / kBM, nt = (N + kBN - 1) / kBN;
+  const int64_t t_all = xcd_tile(blockIdx.x, gridDim.x);
+  const int64_t bz = t_all / (mt * nt);
+  const int64_t t = t_all - bz * (mt * nt);
+  const int64_t group = t / (kGroupM * nt);
+  const int64_t first_m = group * kGroupM;
+  const int64_t gsz = mt - first_m < kGroupM ? mt - first_m : kGroupM;
+  const int64_t tg = t - group * (kGroupM * nt);
+  const int64_t m0 = (first_m + tg % gsz) * kBM;
+  const int64_t n0 = (tg / gsz) * kBN;
+  const uint16_t* __restrict__ A = reinterpret_cast<const uint16_t*>(p.a) + bz * p.stride_a;
+  const uint16_t* __restrict__ B = reinterpret_cast<const uint16_t*>(p.b) + bz * p.stride_b;
+
+  // ---- this lane's load slots: row (lane >> 2) of each 16-row block, piece
+  // slot lane & 3, holding logical piece lpc (the row swizzle inverted; block
+  // bases are multiples of 16 rows, so it is the same for every block).
+  const int lrow = lane >> 2;
+  const int lpc = (lane & 3) ^ ((lrow >> 1) & 3);
+  const int kin = lpc * 8;  // element offset of the piece within the chunk
+
+  int64_t a_off[kLoadsA];
+  int32_t a_ih0[kLoadsA], a_iw0[kLoadsA];
+#pragma unroll
+  for (int j = 0; j < kLoadsA; ++j) {
+    const int64_t m = m0 + (wave * kLoadsA + j) * kRowsPerLoad + lrow;
+    if (!IMPLICIT) {
+      a_off[j] = m < M ? m * p.lda + kin : -1;
+      a_ih0[j] = a_iw0[j] = 0;
+    } else if (m < M) {
+      const int64_t hw = p.oh * p.ow;
+      const int64_t n = m / hw;
+      const int64_t r = m - n * hw;
+      const int64_t oh = r / p.ow;
+      const int64_t ow = r - oh * p.ow;
+      a_ih0[j] = int32_t(oh * p.sh - p.ph);
+      a_iw0[j] = int32_t(ow * p.sw - p.pw);
+      a_off[j] = n * p.h * p.w * p.c + (int64_t(a_ih0[j]) * p.w + a_iw0[j]) * p.c + kin;
+    } else {
+      a_off[j] = 0;
+      a_ih0[j] = -0x40000000;
+      a_iw0[j] = -0x40000000;
+    }
+  }
+  int64_t b_off[kLoadsB];
+#pragma unroll
+  for (int j = 0; j < kLoadsB; ++j) {
+    const int64_t n = n0 + (wave * kLoadsB + j) * kRowsPerLoad + lrow;
+    b_off[j] = n < N ? n * p.ldb + kin : -1;
+  }
+
+  // ---- K position of the next chunk to issue (implicit: C % 32 == 0, so a
+  // chunk never straddles two taps and its tap is wave-uniform).  Chunks past
+  // the end are issued too (dense: as zero loads), so every wait count is
+  // fixed.
+  int64_t k_next = 0;
+  int32_t t_c = 0, t_kh = 0, t_kw = 0;
+  const gvec_ptr zero = gvec(&g_lds_zero16);
+
+  const uint32_t ring_a = lds_base(g_ring_a) + wave * (kLoadsA * 64 * 16);
+  const uint32_t ring_b = lds_base(g_ring_b) + wave * (kLoadsB * 64 * 16);
+  auto issue = [&](int stg) {
+    const uint32_t sa = ring_a + stg * kStageBytes;
+    const uint32_t sb = ring_b + stg * kStageBytes;
+    if constexpr (IMPLICIT) {
+      // Branch-free, so the address arithmetic can be interleaved with the
+      // MFMAs.  Chunks past the end wrap around to tap 0 and load real data,
+      // which lands in stages that are never read again.
+      const int32_t dhh = t_kh * p.dh, dww = t_kw * p.dw;
+      const int64_t tap_off = (int64_t(dhh) * p.w + dww) * p.c + t_c;
+#pragma unroll
+      for (int j = 0; j < kLoadsA; ++j) {
+        const bool ok = (uint32_t(a_ih0[j] + dhh) < uint32_t(p.h)) &
+                        (uint32_t(a_iw0[j] + dww) < uint32_t(p.w));
+        const gvec_ptr src = ok ? gvec(A + a_off[j] + tap_off) : zero;
+        __builtin_amdgcn_global_load_lds(src, lds_addr(sa + j * (64 * 16)), 16, 0, 0);
+      }
+      const int64_t kb = k_next < K ? k_next : 0;
+#pragma unroll
+      for (int j = 0; j < kLoadsB; ++j) {
+        const gvec_ptr src = b_off[j] >= 0 ? gvec(B + b_off[j] + kb) : zero;
+        __builtin_amdgcn_global_load_lds(src, lds_addr(sb + j * (64 * 16)), 16, 0, 0);
+      }
+      t_c += kBK;
+      const bool wc = t_c == p.c;
+      t_c = wc ? 0 : t_c;
+      t_kw += wc ? 1 : 0;
+      const bool ww = t_kw == p.kw;
+      t_kw = ww ? 0 : t_kw;
+      t_kh += ww ? 1 : 0;
+      t_kh = t_kh == p.kh ? 0 : t_kh;
+    } else {
+      const bool k_in = k_next + kin < K;
+#pragma unroll
+      for (int j = 0; j < kLoadsA; ++j) {
+        const gvec_ptr src = (a_off[j] >= 0 && k_in) ? gvec(A + a_off[j] + k_next) : zero;
+        __builtin_amdgcn_global_load_lds(src, lds_addr(sa + j * (64 * 16)), 16, 0, 0);
+      }
+#pragma unroll
+      for (int j = 0; j < kLoadsB; ++j) {
+        const gvec_ptr src = (b_off[j] >= 0 && k_in) ? gvec(B + b_off[j] + k_next) : zero;
+        __builtin_amdgcn_global_load_lds(src, lds_addr(sb + j * (64 * 16)), 16, 0, 0);
+      }
+    }
+    k_next += kBK;
+  };
+
+  // ---- fragment reads: lane's A rows wm*128 + 32 i + (lane & 31), B rows
+  // wn*128 + 32 j + (lane & 31), logical piece 2 q + (lane >> 5), physical
+  // piece that ^ ((row >> 1) & 3) (the same for all four 32-row groups).
+  // Each read is addressed as ring + (offset + stage base) with the offsets
+  // precomputed and kept opaque, so the compiler sees every fragment read as a
+  // read of its ring object (and tags it so).
+  const int frow = lane & 31;
+  const int khalf = lane >> 5;
+  uint32_t ra_off[2][4], rb_off[2][4];
+#pragma unroll
+  for (int q = 0; q < 2; ++q)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t ph = uint32_t(((2 * q + khalf) ^ ((frow >> 1) & 3)) << 4);
+      ra_off[q][i] = uint32_t((wm * 128 + i * 32 + frow) * kRowBytes) + ph;
+      rb_off[q][i] = uint32_t((wn * 128 + i * 32 + frow) * kRowBytes) + ph;
+      asm volatile("" : "+v"(ra_off[q][i]));
+      asm volatile("" : "+v"(rb_off[q][i]));
+    }
+  auto read = [&](int stg, int q, Frag& f) {
+    const uint32_t sb = uint32_t(stg * kStageBytes);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f.a[i] = *reinterpret_cast<const uint4*>(g_ring_a + (ra_off[q][i] + sb));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) f.b[j] = *reinterpret_cast<const uint4*>(g_ring_b + (rb_off[q][j] + sb));
+  };
+
+  v16f acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  auto mma = [&](const Frag& f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = mfma_32x32x16<BF16>(f.a[i], f.b[j], acc[i][j]);
+  };
+
+  const int64_t nk = (K + kBK - 1) / kBK;
+  Frag f0, f1;
+  // Prologue: chunks 0 .. kStages-2 in flight; wait for chunk 0 everywhere.
+#pragma unroll
+  for (int i = 0; i < kStages - 1; ++i) issue(i);
+  wait_vmcnt<(kStages - 2) * kLoads>();
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  read(0, 0, f0);
+
+  // Chunk kc sits in stage cur; its K step 0 fragments are already in f0.
+  // Mid-chunk: wait until chunk kc + 1 has landed everywhere.  After that
+  // barrier every wavefront has also issued all MFMAs of chunk kc - 1, so its
+  // reads are done and stage cur - 1 can take chunk kc + kStages - 1.
+  int cur = 0;
+  for (int64_t kc = 0; kc < nk; ++kc) {
+    const int nxt = cur + 1 == kStages ? 0 : cur + 1;
+    const int prv = cur == 0 ? kStages - 1 : cur - 1;
+    // K step 1 reads interleaved with K step 0 MFMAs: two MFMAs, one read
+    read(cur, 1, f1);
+    mma(f0);
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // two MFMAs
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vmcnt<(kStages - 3) * kLoads>();
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    // The next chunk's loads and K step 0 reads interleaved with K step 1
+    // MFMAs: per MFMA one load into LDS and its address arithmetic, and a
+    // fragment read every other MFMA.
+    issue(prv);
+    read(nxt, 0, f0);
+    mma(f1);
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 1);  // load into LDS
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 1);  // VALU
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);  // LDS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 1);  // load into LDS
+      __builtin_amdgcn_sched_group_barrier(0x002, 6, 1);  // VALU
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // The next chunk's step 0 reads were issued 16 MFMAs ago and are done;
+    // saying so here lets the loop head wait for its own reads only.
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    cur = nxt;
+  }
+  wait_vmcnt<0>();  // the trailing zero loads must land before LDS is reused
+
+  // ---- epilogue through LDS, one 32-row slice of the wavefront's quadrant
+  // at a time.  D[row][col] of a 32x32 block sits in lane l, register r at
+  // row = 8 (r / 4) + 4 (l / 32) + r % 4, col = l % 32; the slice is written to
+  // the wavefront's own LDS area and read back as 8 consecutive columns per
+  // lane, 16 lanes per row, so global stores are 16-byte and row-contiguous.
+  __builtin_amdgcn_s_barrier();  // every wavefront has finished its LDS reads
+  constexpr int EP = 128 + 4;    // padded slice row (floats)
+  static_assert(2 * 32 * EP * 4 <= kRingBytes, "two epilogue slices fit one ring");
+  float* ep = reinterpret_cast<float*>((wave < 2 ? g_ring_a : g_ring_b) + (wave & 1) * (kRingBytes / 2));
+  uint16_t* __restrict__ out = reinterpret_cast<uint16_t*>(p.out) + bz * p.stride_out;
+  float* __restrict__ accbuf = p.acc ? p.acc + bz * p.stride_out : nullptr;
+  const int epi = p.epi;
+  const bool vec = (p.ldc % 8) == 0 && (reinterpret_cast<uintptr_t>(out) & 15) == 0 &&
+                   (accbuf == nullptr || (reinterpret_cast<uintptr_t>(accbuf) & 15) == 0);
+  const int rl = lane >> 4;        // row within a group of 4
+  const int cl = (lane & 15) * 8;  // first column of this lane's 8
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        ep[(8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * EP + 32 * j + (lane & 31)] = acc[i][j][r];
+    for (int g = 0; g < 8; ++g) {
+      const int rr = g * 4 + rl;
+      const int64_t row = m0 + wm * 128 + i * 32 + rr;
+      const int64_t col = n0 + wn * 128 + cl;
+      const float4 lo = *reinterpret_cast<const float4*>(ep + rr * EP + cl);
+      const float4 hi = *reinterpret_cast<const float4*>(ep + rr * EP + cl + 4);
+      float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+      if (row >= M || col >= N) continue;
+      const int64_t idx = row * p.ldc + col;
+      if (vec && col + 8 <= N) {
+        if (epi == kEpiAccFirst || epi == kEpiAccMid) {
+          float4* dst = reinterpret_cast<float4*>(accbuf + idx);
+          if (epi == kEpiAccMid) {
+            const float4 a0 = dst[0], a1 = dst[1];
+            v[0] += a0.x; v[1] += a0.y; v[2] += a0.z; v[3] += a0.w;
+            v[4] += a1.x; v[5] += a1.y; v[6] += a1.z; v[7] += a1.w;
+          }
+          dst[0] = make_float4(v[0], v[1], v[2], v[3]);
+          dst[1] = make_float4(v[4], v[5], v[6], v[7]);
+        } else {
+          if (epi == kEpiAccLast) {
+            const float4* src = reinterpret_cast<const float4*>(accbuf + idx);
+            const float4 a0 = src[0], a1 = src[1];
+            v[0] = a0.x + v[0]; v[1] = a0.y + v[1]; v[2] = a0.z + v[2]; v[3] = a0.w + v[3];
+            v[4] = a1.x + v[4]; v[5] = a1.y + v[5]; v[6] = a1.z + v[6]; v[7] = a1.w + v[7];
+          }
+          uint4 o;
+          o.x = uint32_t(from_f32<uint16_t, BF16>(v[0])) | (uint32_t(from_f32<uint16_t, BF16>(v[1])) << 16);
+          o.y = uint32_t(from_f32<uint16_t, BF16>(v[2])) | (uint32_t(from_f32<uint16_t, BF16>(v[3])) << 16);
+          o.z = uint32_t(from_f32<uint16_t, BF16>(v[4])) | (uint32_t(from_f32<uint16_t, BF16>(v[5])) << 16);
+          o.w = uint32_t(from_f32<uint16_t, BF16>(v[6])) | (uint32_t(from_f32<uint16_t, BF16>(v[7])) << 16);
+          *reinterpret_cast<uint4*>(out + idx) = o;
+        }
+      } else {
+        for (int t = 0; t < 8 && col + t < N; ++t) {
+          const float x = v[t];
+          if (epi == kEpiStore) {
+            out[idx + t] = from_f32<uint16_t, BF16>(x);
+          } else if (epi == kEpiAccFirst) {
+            accbuf[idx + t] = x;
+          } else if (epi == kEpiAccMid) {
+            accbuf[idx + t] = accbuf[idx + t] + x;
+          } else {
+            out[idx + t] = from_f32<uint16_t, BF16>(accbuf[idx + t] + x);
+          }
+        }
+      }
+    }
+  }
+}
+
+template <bool BF16>
+hipError_t launch_lds(const GemmParams& p, hipStream_t s) {
+  const int64_t tiles = ((p.M + kBM - 1) / kBM) * ((p.N + kBN - 1) / kBN) * p.batch;
+  const dim3 grid{unsigned(tiles), 1u, 1u};
+  if (p.a_mode == kADense)
+    hipLaunchKernelGGL((gemm_lds_kernel<BF16, false>), grid, dim3(kThreads), 0, s, p);
+  else
+    hipLaunchKernelGGL((gemm_lds_kernel<BF16, true>), grid, dim3(kThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool gemm_lds_ok(const GemmParams& p) {
+  if (p.dtype == CNHWC_F32 || p.K <= 0) return false;
+  if (((p.M + kBM - 1) / kBM) * ((p.N + kBN - 1) / kBN) * p.batch >= (int64_t(1) << 31)) return false;
+  if (p.K % 8 != 0 || p.ldb % 8 != 0) return false;
+  if (p.a_mode == kADense) return p.lda % 8 == 0;
+  return p.c % kBK == 0;  // a chunk never straddles two taps
+}
+
+int gemm_lds_launch(const GemmParams& p, void* stream) {
+  if (!gemm_lds_ok(p)) return hipErrorInvalidValue;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  return p.dtype == CNHWC_BF16 ? launch_lds<true>(p, s) : launch_lds<false>(p, s);
+}
+
+}  // namespace cnhwc

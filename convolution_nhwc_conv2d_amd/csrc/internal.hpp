@@ -38,6 +38,8 @@ enum GemmConfig : int32_t {
   kCfgH_128x128 = 11,
   kCfgH_256x128 = 12,
   kCfgH_128x256 = 13,
+  // 256 x 256, direct global -> LDS operand loads (gemm_lds.hip)
+  kCfgH_256x256 = 14,
   // Winograd tile-position GEMMs: persistent fp32 kernel with U_p resident in LDS
   kCfgWinoResident = 20,
 };
@@ -45,8 +47,9 @@ enum GemmConfig : int32_t {
 // Pick the tile configuration.  fp32: from the output-channel count only (the
 // Winograd GEMM's configuration must not depend on the batch or its tiling).
 // fp16/bf16: from the GEMM shape (rows M of the whole conv, columns N), by a
-// simple occupancy model over the 256 compute units.
-int32_t pick_gemm_config(int dtype, int64_t m_rows, int64_t n_cols);
+// simple occupancy model over the 256 compute units; lds_ok admits the
+// 256x256 direct-to-LDS tile.
+int32_t pick_gemm_config(int dtype, int64_t m_rows, int64_t n_cols, bool lds_ok);
 
 // Epilogue: how a GEMM / output-transform result r is written.
 enum EpiMode : int32_t {
@@ -84,6 +87,12 @@ struct GemmParams {
 };
 
 int gemm_launch(const GemmParams& p, void* stream);  // returns hipError_t
+
+// fp16/bf16 256 x 256 tile GEMM with direct global -> LDS operand loads.
+// Applicable for dense A (lda, ldb, K multiples of 8) and for implicit A with
+// C a multiple of 32.
+bool gemm_lds_ok(const GemmParams& p);
+int gemm_lds_launch(const GemmParams& p, void* stream);  // returns hipError_t
 
 // Persistent Winograd GEMM (all 64 positions): M_p[rows][o] = V_p[rows][cs] * U_p[o][cs]^T.
 // Applicable when U_p fits in LDS (cs <= 192, o <= 96).

@@ -92,6 +92,26 @@ void tile_rule(uint64_t ws_limit, uint64_t own, uint64_t scratch, int64_t n, int
   *fallback = (t < 1) || (force_tile <= 0 && t < n && t * rows < CNHWC_MIN_TILE_ROWS);
 }
 
+// Tile configuration of the implicit / unfold GEMM: forced, or picked.  The
+// 256x256 direct-to-LDS tile needs C % 32 == 0 (implicit: a K chunk never
+// straddles two taps) or K % 8 == 0 (unfold rows).
+cnhwc_status_t gemm_config_for(const cnhwc_conv_desc_t& d, int64_t m_rows, bool implicit,
+                               int32_t force, int32_t* cfg) {
+  const int64_t k = d.kh * d.kw * d.c;
+  const bool lds_ok = d.dtype != CNHWC_F32 && (implicit ? d.c % 32 == 0 : k % 8 == 0);
+  if (force == 0) {
+    *cfg = pick_gemm_config(d.dtype, m_rows, d.o, lds_ok);
+    return CNHWC_OK;
+  }
+  const bool f32 = force >= kCfgF32_N32 && force <= kCfgF32_N128;
+  const bool half = force >= kCfgH_128x64 && force <= kCfgH_256x256;
+  if ((d.dtype == CNHWC_F32 && !f32) || (d.dtype != CNHWC_F32 && !half) ||
+      (force == kCfgH_256x256 && !lds_ok))
+    return CNHWC_ERR_NOT_APPLICABLE;
+  *cfg = force;
+  return CNHWC_OK;
+}
+
 cnhwc_status_t select_2d(const cnhwc_conv_desc_t& d, const int64_t out[3],
                          const cnhwc_select_opts_t& o, int32_t force, cnhwc_plan_t* p) {
   const uint64_t es = dtype_size(d.dtype);
@@ -131,7 +151,7 @@ cnhwc_status_t select_2d(const cnhwc_conv_desc_t& d, const int64_t out[3],
       p->workspace_bytes = lay.total;
       // the GEMM configuration depends on (C, O) only, never on the batch tiling
       p->kernel_config = wino_gemm_resident_ok(lay.cs, d.o) ? int32_t(kCfgWinoResident)
-                                                            : pick_gemm_config(CNHWC_F32, 0, d.o);
+                                                            : pick_gemm_config(CNHWC_F32, 0, d.o, false);
       return CNHWC_OK;
     }
   }
@@ -148,15 +168,13 @@ cnhwc_status_t select_2d(const cnhwc_conv_desc_t& d, const int64_t out[3],
     p->unfold_rows = rows;
     p->n_chunks = ceil_div(m_rows, rows);
     p->workspace_bytes = align_up(uint64_t(rows) * kp * es, 256);
-    p->kernel_config = pick_gemm_config(d.dtype, m_rows, d.o);
-    return CNHWC_OK;
+    return gemm_config_for(d, m_rows, false, o.force_gemm_config, &p->kernel_config);
   }
 
   // 3. Implicit GEMM (scratch-free).
   p->algo = p->inner_algo = CNHWC_ALGO_IMPLICIT_GEMM;
   p->workspace_bytes = 0;
-  p->kernel_config = pick_gemm_config(d.dtype, m_rows, d.o);
-  return CNHWC_OK;
+  return gemm_config_for(d, m_rows, true, o.force_gemm_config, &p->kernel_config);
 }
 
 cnhwc_status_t select_3d(const cnhwc_conv_desc_t& d, const int64_t out[3],
@@ -220,7 +238,7 @@ cnhwc_conv_desc_t frame_desc(const cnhwc_conv_desc_t& d3, int64_t od) {
   return f;
 }
 
-int32_t pick_gemm_config(int dtype, int64_t m_rows, int64_t n_cols) {
+int32_t pick_gemm_config(int dtype, int64_t m_rows, int64_t n_cols, bool lds_ok) {
   if (dtype == CNHWC_F32) {
     if (n_cols <= 32) return kCfgF32_N32;
     if (n_cols <= 64) return kCfgF32_N64;
@@ -241,13 +259,17 @@ int32_t pick_gemm_config(int dtype, int64_t m_rows, int64_t n_cols) {
   // the tile shape on MI355X (128x128 at two workgroups per CU is the fastest
   // on every large conv of the sweep; the 256-wide tiles need one CU each and
   // lose about 20%; 128x64 is for problems too small to fill the chip).
+  // The 256x256 tile with direct loads into LDS (one workgroup per CU) ran
+  // 1.32-1.47x the 128x128 rate on the large convs of the sweep.
   struct Cand { int32_t id; int64_t bm, bn, occ; double eff; };
-  const Cand cands[4] = {{kCfgH_128x128, 128, 128, 2, 1.00}, {kCfgH_128x256, 128, 256, 1, 0.85},
-                         {kCfgH_256x128, 256, 128, 1, 0.80}, {kCfgH_128x64, 128, 64, 2, 0.70}};
+  const Cand cands[5] = {{kCfgH_128x128, 128, 128, 2, 1.00}, {kCfgH_128x256, 128, 256, 1, 0.85},
+                         {kCfgH_256x128, 256, 128, 1, 0.80}, {kCfgH_128x64, 128, 64, 2, 0.70},
+                         {kCfgH_256x256, 256, 256, 1, 1.35}};
   constexpr int64_t kCUs = 256;
   int32_t best = kCfgH_128x128;
   double best_t = 1e300;
   for (const Cand& c : cands) {
+    if (c.id == kCfgH_256x256 && !lds_ok) continue;
     const int64_t tiles = ceil_div(m_rows, c.bm) * ceil_div(n_cols, c.bn);
     const int64_t slots = kCUs * c.occ;
     const int64_t waves = ceil_div(tiles, slots);
@@ -269,13 +291,15 @@ bool plan_equal(const cnhwc_plan_t& a, const cnhwc_plan_t& b) {
          a.opts.force_algo == b.opts.force_algo &&
          a.opts.force_inner_algo == b.opts.force_inner_algo &&
          a.opts.force_tile_batch == b.opts.force_tile_batch &&
-         a.opts.force_unfold_rows == b.opts.force_unfold_rows;
+         a.opts.force_unfold_rows == b.opts.force_unfold_rows &&
+         a.opts.force_gemm_config == b.opts.force_gemm_config;
 }
 
 cnhwc_status_t select_impl(const cnhwc_conv_desc_t* desc, const cnhwc_select_opts_t* opts,
                            cnhwc_plan_t* plan) {
   if (!desc || !opts || !plan) return CNHWC_ERR_INVALID_ARGUMENT;
-  if (opts->ws_limit_bytes == 0 || opts->force_tile_batch < 0 || opts->force_unfold_rows < 0)
+  if (opts->ws_limit_bytes == 0 || opts->force_tile_batch < 0 || opts->force_unfold_rows < 0 ||
+      opts->force_gemm_config < 0 || opts->reserved_opts != 0)
     return CNHWC_ERR_INVALID_ARGUMENT;
   if (opts->force_algo < CNHWC_ALGO_AUTO || opts->force_algo > CNHWC_ALGO_SMALL_KD ||
       opts->force_inner_algo < CNHWC_ALGO_AUTO || opts->force_inner_algo > CNHWC_ALGO_UNFOLD_GEMM)

@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define CNHWC_ABI_VERSION 1
+#define CNHWC_ABI_VERSION 2
 
 /* Fewest GEMM rows (tile_batch * tiles_per_image) a Winograd batch tile may
  * carry when the batch does not fit in one tile; below it AUTO falls back to
@@ -119,6 +119,11 @@ typedef struct {
   int32_t force_inner_algo;  /* SMALL_KD only: per-tap 2D algorithm; AUTO = select */
   int64_t force_tile_batch;  /* Winograd: 0 = budget rule; else min(value, budget tile) */
   int64_t force_unfold_rows; /* Unfold: 0 = the fixed byte cap; else rows per chunk */
+  int32_t force_gemm_config; /* 0 = select; else a GEMM tile configuration id for the
+                                implicit / unfold GEMM (fp16/bf16: 10..14; fp32: 1..4).
+                                An id that does not suit the dtype or the shape is
+                                CNHWC_ERR_NOT_APPLICABLE. */
+  int32_t reserved_opts;     /* must be 0 */
 } cnhwc_select_opts_t;
 
 /* A plan: a plain value, a pure function of (descriptor, options). */

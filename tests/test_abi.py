@@ -28,7 +28,7 @@ def test_header_constants_match_binding_layout():
     assert int(re.search(r"#define CNHWC_ABI_VERSION (\d+)", text).group(1)) == cn.lib.cnhwc_abi_version()
     # struct sizes as a C compiler lays them out
     assert ctypes.sizeof(cn.Desc) == 4 + 4 + 9 * 8 + 3 * 12 + 4
-    assert ctypes.sizeof(cn.Opts) == 8 + 4 + 4 + 8 + 8
+    assert ctypes.sizeof(cn.Opts) == 8 + 4 + 4 + 8 + 8 + 4 + 4
 
 
 def test_single_hip_runtime_in_process():

@@ -167,3 +167,53 @@ def test_conv3d_kd1_bit_identical_to_conv2d(dtype):
     y3 = cn.conv3d(x, w, 1, (0, 1, 1), 1)
     y2 = cn.conv2d(x[0], w[:, 0].contiguous(), 1, 1, 1)
     assert torch.equal(bits(y3[0]), bits(y2))
+
+
+# ------------------------------- 256x256 tile with direct loads into LDS
+# Shapes chosen to span several row and column tiles with ragged tails, every
+# filter geometry of the half grid, and C = 32 / 64 / 96 / 128 (the tile needs
+# C % 32 == 0 for the implicit gather, K % 8 == 0 for unfold rows).
+
+LDS_CASES = [  # name, n, h, w, c, o, k, stride, pad, dil
+    ("c64_o300", 2, 20, 20, 64, 300, 3, 1, 1, 1),
+    ("c96_s2", 3, 33, 31, 96, 260, 3, 2, 1, 1),
+    ("c32_k5_d2", 2, 24, 24, 32, 256, 5, 1, 4, 2),
+    ("c128_k1", 1, 30, 30, 128, 520, 1, 1, 0, 1),
+    ("c64_k7_s2", 2, 40, 40, 64, 64, 7, 2, 3, 1),
+    ("c32_k1_one_chunk", 1, 17, 15, 32, 96, 1, 1, 0, 1),
+]
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("spec", LDS_CASES, ids=[c[0] for c in LDS_CASES])
+def test_lds_tile_parity(dtype, spec):
+    name, n, h, w, c, o, k, s, p, d = spec
+    case = cw.ConvCase(f"lds_{name}_{dtype}", n, h, w, c, o, k, k, (s, s), (p, p), (d, d), dtype,
+                       "normal", "normal", None, 21, len(name) * 7 + c)
+    x, wt = case.input(), case.weight()
+    yr, den = oracle.conv(to_oracle(x), to_oracle(wt), **case.conv_kwargs())
+    for algo in ("implicit_gemm", "unfold_gemm"):
+        plan = cn.plan2d(case.x_shape(), case.w_shape(), **case.conv_kwargs(), dtype=x.dtype, algo=algo,
+                         gemm_config=14)
+        assert plan.kernel_config == 14
+        y = cn.conv2d(_dev(x), _dev(wt), **case.conv_kwargs(), algo=algo, gemm_config=14)
+        check_parity(y.cpu(), yr, den, y.dtype, f"{case.name}/{algo}/256x256")
+        # same K order as the 128x128 tile: bit-identical results
+        y11 = cn.conv2d(_dev(x), _dev(wt), **case.conv_kwargs(), algo=algo, gemm_config=11)
+        assert torch.equal(bits(y), bits(y11)), f"{case.name}/{algo}: 256x256 and 128x128 tiles differ"
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_lds_tile_3d_accumulating_epilogue(dtype):
+    """Per-tap 2D convs of the 3D decomposition accumulate in fp32 through the
+    256x256 tile's epilogue modes (first / middle / last tap)."""
+    case = cw.ConvCase(f"lds3d_{dtype}", 1, 18, 19, 64, 272, 3, 3, (1, 1, 1), (0, 1, 1), (1, 1, 1), dtype,
+                       "normal", "normal", None, 23, 5, nd=3, d=6, kd=3)
+    x, wt = case.input(), case.weight()
+    plan = cn.plan3d(case.x_shape(), case.w_shape(), **case.conv_kwargs(), dtype=x.dtype, gemm_config=14)
+    assert plan.algo_name == "small_kd" and plan.kernel_config == 14
+    y = cn.conv3d(_dev(x), _dev(wt), **case.conv_kwargs(), gemm_config=14)
+    yr, den = oracle.conv(to_oracle(x), to_oracle(wt), **case.conv_kwargs())
+    check_parity(y.cpu(), yr, den, y.dtype, case.name)
+    y11 = cn.conv3d(_dev(x), _dev(wt), **case.conv_kwargs(), gemm_config=11)
+    assert torch.equal(bits(y), bits(y11))

@@ -290,3 +290,48 @@ def test_3d_guard_each_clause(change):
 def test_3d_forced_inner_winograd():
     p = cn.plan3d(X3, W3, 1, (0, 1, 1), 1, torch.bfloat16, inner_algo="winograd")
     assert p.inner_algo_name == "winograd" and p.tile_batch == 39
+
+
+# ------------------------------------------------------- GEMM tile choice
+
+F16 = torch.float16
+
+
+def test_large_half_convs_take_the_256_tile():
+    """Large fp16/bf16 implicit GEMMs (C % 32 == 0) get the 256x256 direct-to-LDS tile;
+    small ones (a ResNet-50 batch-1 layer) and C % 32 != 0 do not."""
+    big = cn.plan2d((64, 32, 32, 256), (4096, 3, 3, 256), 1, 1, 1, F16, algo="implicit_gemm")
+    assert big.kernel_config == 14
+    big3 = cn.plan3d((1, 41, 120, 208, 512), (512, 3, 3, 3, 512), 1, (0, 1, 1), 1, torch.bfloat16)
+    assert big3.algo_name == "small_kd" and big3.kernel_config == 14
+    small = cn.plan2d((1, 56, 56, 64), (64, 3, 3, 64), 1, 1, 1, F16)
+    assert small.kernel_config != 14
+    odd = cn.plan2d((64, 32, 32, 120), (4096, 3, 3, 120), 1, 1, 1, F16, algo="implicit_gemm")
+    assert odd.kernel_config != 14
+
+
+def test_forced_gemm_config():
+    p = cn.plan2d((2, 20, 20, 64), (300, 3, 3, 64), 1, 1, 1, F16, gemm_config=14)
+    assert p.kernel_config == 14 and p.opts.force_gemm_config == 14
+    p = cn.plan2d((2, 20, 20, 64), (300, 3, 3, 64), 1, 1, 1, F16, algo="unfold_gemm", gemm_config=14)
+    assert p.kernel_config == 14
+    for xs, ws, dt, algo, cfg in [((2, 20, 20, 64), (300, 3, 3, 64), torch.float32, "implicit_gemm", 14),
+                                  ((2, 20, 20, 48), (300, 3, 3, 48), F16, "implicit_gemm", 14),
+                                  ((2, 20, 20, 20), (300, 3, 3, 20), F16, "unfold_gemm", 14),
+                                  ((2, 20, 20, 64), (300, 3, 3, 64), F16, "implicit_gemm", 3),
+                                  ((2, 20, 20, 64), (300, 3, 3, 64), torch.float32, "implicit_gemm", 11),
+                                  ((2, 20, 20, 64), (300, 3, 3, 64), F16, "implicit_gemm", 99)]:
+        with pytest.raises(cn.CnhwcError) as e:
+            cn.plan2d(xs, ws, 1, 1, 1, dt, algo=algo, gemm_config=cfg)
+        assert e.value.name == "NOT_APPLICABLE", (xs, dt, algo, cfg)
+    d = cn.make_desc((1, 8, 8, 8), (8, 3, 3, 8), 1, 1, 1)
+    o = cn.make_opts()
+    o.force_gemm_config = -1
+    with pytest.raises(cn.CnhwcError) as e:
+        cn.select(d, o)
+    assert e.value.name == "INVALID_ARGUMENT"
+    o = cn.make_opts()
+    o.reserved_opts = 1
+    with pytest.raises(cn.CnhwcError) as e:
+        cn.select(d, o)
+    assert e.value.name == "INVALID_ARGUMENT"
