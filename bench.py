@@ -195,19 +195,23 @@ def traffic_from(fetch_csv, write_csv, calib_bytes, workload_key):
     return out
 
 
-def _time_call(fn, reps=10, warmup=2):
-    """Average ms per call of fn() on the current stream (torch events)."""
+def _time_call(fn, reps=15, warmup=3):
+    """Median ms per call of fn() on the current stream (torch events around
+    each call), so that a one-off stall of the machine does not move the
+    figure; the minimum is in _time_call.last_min."""
     import torch
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record()
-    for _ in range(reps):
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in ev:
+        a.record()
         fn()
-    b.record()
-    b.synchronize()
-    return a.elapsed_time(b) / reps
+        b.record()
+    torch.cuda.synchronize()
+    t = sorted(a.elapsed_time(b) for a, b in ev)
+    _time_call.last_min = t[0]
+    return t[len(t) // 2]
 
 
 def _kernel_split(fn, reps=3):
@@ -248,10 +252,11 @@ def run_suite(names):
         ws = torch.empty(max(1, plan.workspace_bytes), dtype=torch.uint8, device=dev)
         call = lambda timer=None: fn(x, w, **case.conv_kwargs(), plan=plan, out=y, workspace=ws, timer=timer)
         ms = _time_call(call)
+        ms_min = _time_call.last_min
         split = _kernel_split(call)
         flops = cn.direct_flops(tuple(x.shape), tuple(w.shape), plan)
         return {"workload": case.name, "dtype": case.dtype, "algo": plan.algo_name,
-                "inner_algo": plan.inner_algo_name, "ms": ms, "tflops": flops / ms / 1e9,
+                "inner_algo": plan.inner_algo_name, "ms": ms, "ms_min": ms_min, "tflops": flops / ms / 1e9,
                 "kernels_ms": split, "flops": flops}
 
     if "small" in names:

@@ -50,11 +50,14 @@ constexpr int kLoadsA = kBM * kRowBytes / (kThreads * 16);  // 16-byte loads per
 constexpr int kLoadsB = kBN * kRowBytes / (kThreads * 16);
 constexpr int kLoads = kLoadsA + kLoadsB;
 constexpr int kRowsPerLoad = 64 * 16 / kRowBytes;  // rows one wavefront load instruction fills
-#ifndef CNHWC_LDS_STAGES
-#define CNHWC_LDS_STAGES 4
-#endif
-constexpr int kStages = CNHWC_LDS_STAGES;
-static_assert(kStages >= 4 && kStages <= 5, "stage ring");
+constexpr int kSteps = kBK / 16;  // MFMA K steps per chunk
+constexpr int kPieces = kRowBytes / 16;  // 16-byte pieces per LDS row (4)
+constexpr int kStages = 4;
+
+// Physical 16-byte piece of logical piece c in 64-byte LDS row r: c XOR bits
+// 1..2 of the row, so the 8 lanes served per LDS cycle (8 consecutive rows,
+// same logical piece) hit distinct bank groups.
+__device__ __forceinline__ int piece(int r, int c) { return c ^ ((r >> 1) & 3); }
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef const u32x4 __attribute__((address_space(1)))* gvec_ptr;
@@ -134,8 +137,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_lds_kernel(const GemmParams 
   // ---- this lane's load slots: row (lane >> 2) of each 16-row block, piece
   // slot lane & 3, holding logical piece lpc (the row swizzle inverted; block
   // bases are multiples of 16 rows, so it is the same for every block).
-  const int lrow = lane >> 2;
-  const int lpc = (lane & 3) ^ ((lrow >> 1) & 3);
+  const int lrow = lane / kPieces;
+  const int lpc = piece(lrow, lane % kPieces);  // the swizzle is its own inverse
   const int kin = lpc * 8;  // element offset of the piece within the chunk
 
   int64_t a_off[kLoadsA];
@@ -232,12 +235,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_lds_kernel(const GemmParams 
   // read of its ring object (and tags it so).
   const int frow = lane & 31;
   const int khalf = lane >> 5;
-  uint32_t ra_off[2][4], rb_off[2][4];
+  uint32_t ra_off[kSteps][4], rb_off[kSteps][4];
 #pragma unroll
-  for (int q = 0; q < 2; ++q)
+  for (int q = 0; q < kSteps; ++q)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const uint32_t ph = uint32_t(((2 * q + khalf) ^ ((frow >> 1) & 3)) << 4);
+      const uint32_t ph = uint32_t(piece(frow, 2 * q + khalf) << 4);
       ra_off[q][i] = uint32_t((wm * 128 + i * 32 + frow) * kRowBytes) + ph;
       rb_off[q][i] = uint32_t((wn * 128 + i * 32 + frow) * kRowBytes) + ph;
       asm volatile("" : "+v"(ra_off[q][i]));
