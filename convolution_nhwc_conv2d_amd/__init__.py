@@ -52,7 +52,7 @@ class Opts(ctypes.Structure):
     _fields_ = [("ws_limit_bytes", ctypes.c_uint64), ("force_algo", ctypes.c_int32),
                 ("force_inner_algo", ctypes.c_int32), ("force_tile_batch", ctypes.c_int64),
                 ("force_unfold_rows", ctypes.c_int64), ("force_gemm_config", ctypes.c_int32),
-                ("reserved_opts", ctypes.c_int32)]
+                ("force_split_k", ctypes.c_int32)]
 
 
 class Plan(ctypes.Structure):
@@ -63,7 +63,7 @@ class Plan(ctypes.Structure):
                 ("n_chunks", ctypes.c_int64), ("own_bytes", ctypes.c_uint64),
                 ("budget_bytes", ctypes.c_uint64), ("scratch_per_element", ctypes.c_uint64),
                 ("workspace_bytes", ctypes.c_uint64), ("kernel_config", ctypes.c_int32),
-                ("reserved", ctypes.c_int32), ("opts", Opts)]
+                ("split_k", ctypes.c_int32), ("opts", Opts)]
 
     @property
     def algo_name(self):
@@ -74,7 +74,7 @@ class Plan(ctypes.Structure):
         return ALGO_NAMES[self.inner_algo]
 
     def as_dict(self):
-        d = {f: getattr(self, f) for f, _ in self._fields_ if f not in ("opts", "reserved")}
+        d = {f: getattr(self, f) for f, _ in self._fields_ if f != "opts"}
         d["algo"] = self.algo_name
         d["inner_algo"] = self.inner_algo_name
         d["opts"] = {f: getattr(self.opts, f) for f, _ in Opts._fields_}
@@ -130,7 +130,7 @@ EXPORTED = ("cnhwc_abi_version", "cnhwc_status_string", "cnhwc_conv_select",
             "cnhwc_launch_count", "cnhwc_conv2d_fwd_timed", "cnhwc_conv3d_fwd_timed")
 
 KERNEL_KINDS = {0: "end", 1: "wino_filter", 2: "wino_input", 3: "wino_gemm", 4: "wino_output",
-                5: "implicit_gemm", 6: "unfold", 7: "unfold_gemm"}
+                5: "implicit_gemm", 6: "unfold", 7: "unfold_gemm", 8: "splitk_reduce"}
 
 
 # ------------------------------------------------------------------ helpers
@@ -183,7 +183,7 @@ def default_ws_limit(device=None):
 
 
 def make_opts(ws_limit=None, algo="auto", inner_algo="auto", tile_batch=None, unfold_rows=None,
-              gemm_config=None, device=None):
+              gemm_config=None, split_k=None, device=None):
     o = Opts()
     o.ws_limit_bytes = int(ws_limit) if ws_limit is not None else default_ws_limit(device)
     o.force_algo = ALGOS[algo]
@@ -193,6 +193,7 @@ def make_opts(ws_limit=None, algo="auto", inner_algo="auto", tile_batch=None, un
     o.force_tile_batch = int(tile_batch or 0)
     o.force_unfold_rows = int(unfold_rows or 0)
     o.force_gemm_config = int(gemm_config or 0)
+    o.force_split_k = int(split_k or 0)
     return o
 
 
@@ -335,20 +336,21 @@ class KernelTimer:
 
 
 def conv2d(x, w, stride=1, padding=0, dilation=1, *, algo="auto", ws_limit=None, tile_batch=None,
-           unfold_rows=None, gemm_config=None, out=None, workspace=None, plan=None, timer=None):
+           unfold_rows=None, gemm_config=None, split_k=None, out=None, workspace=None, plan=None,
+           timer=None):
     """y[N,OH,OW,O] = channels-last conv2d of x[N,H,W,C] with w[O,KH,KW,C]."""
     opts = make_opts(ws_limit, algo, "auto", tile_batch, unfold_rows, gemm_config=gemm_config,
-                     device=x.device if x.is_cuda else None)
+                     split_k=split_k, device=x.device if x.is_cuda else None)
     fn = lib.cnhwc_conv2d_fwd_timed if timer is not None else lib.cnhwc_conv2d_fwd
     return _run(fn, x, w, stride, padding, dilation, opts, out, workspace, plan, timer)
 
 
 def conv3d(x, w, stride=1, padding=0, dilation=1, *, algo="auto", inner_algo="auto", ws_limit=None,
-           tile_batch=None, unfold_rows=None, gemm_config=None, out=None, workspace=None, plan=None,
-           timer=None):
+           tile_batch=None, unfold_rows=None, gemm_config=None, split_k=None, out=None, workspace=None,
+           plan=None, timer=None):
     """y[N,OD,OH,OW,O] = channels-last conv3d of x[N,D,H,W,C] with w[O,KD,KH,KW,C]."""
     opts = make_opts(ws_limit, algo, inner_algo, tile_batch, unfold_rows, gemm_config=gemm_config,
-                     device=x.device if x.is_cuda else None)
+                     split_k=split_k, device=x.device if x.is_cuda else None)
     fn = lib.cnhwc_conv3d_fwd_timed if timer is not None else lib.cnhwc_conv3d_fwd
     return _run(fn, x, w, stride, padding, dilation, opts, out, workspace, plan, timer)
 

@@ -45,8 +45,9 @@ struct Recorder {
 
 // Kernels launched by one 2D conv with this plan.
 int64_t launches_2d(const cnhwc_plan_t& p, int32_t algo) {
-  if (algo == CNHWC_ALGO_IMPLICIT_GEMM) return 1;
-  if (algo == CNHWC_ALGO_UNFOLD_GEMM) return 2 * p.n_chunks;
+  const int64_t reduce = p.split_k > 1 ? 1 : 0;  // the K-split sum after each GEMM
+  if (algo == CNHWC_ALGO_IMPLICIT_GEMM) return 1 + reduce;
+  if (algo == CNHWC_ALGO_UNFOLD_GEMM) return (2 + reduce) * p.n_chunks;
   if (algo == CNHWC_ALGO_WINOGRAD) return 1 + 3 * p.n_tiles;
   return -1;
 }
@@ -82,6 +83,22 @@ cnhwc_status_t run_2d(const cnhwc_conv_desc_t& d, const cnhwc_plan_t& p, int32_t
   g.dh = d.dil[1];
   g.dw = d.dil[2];
   g.batch = 1;
+  // K split (plan.split_k > 1): whole K chunks per split; the partial slices
+  // sit in the workspace after the unfold buffer (if any).
+  g.ksplit = p.split_k;
+  if (p.split_k > 1) {
+    const int64_t bk = gemm_config_bk(p.kernel_config);
+    g.kchunk = ceil_div(ceil_div(k, bk), p.split_k) * bk;
+  }
+  auto gemm = [&](int32_t kind) -> cnhwc_status_t {
+    rec.mark(kind);
+    if (gemm_launch(g, stream) != hipSuccess) return CNHWC_ERR_HIP;
+    if (g.ksplit > 1) {
+      rec.mark(CNHWC_KERNEL_SPLITK_REDUCE);
+      if (splitk_reduce_launch(g, stream) != hipSuccess) return CNHWC_ERR_HIP;
+    }
+    return CNHWC_OK;
+  };
 
   if (algo == CNHWC_ALGO_IMPLICIT_GEMM) {
     g.a_mode = kAImplicit;
@@ -93,13 +110,14 @@ cnhwc_status_t run_2d(const cnhwc_conv_desc_t& d, const cnhwc_plan_t& p, int32_t
     g.out = y;
     g.ldc = d.o;
     g.acc = acc;
-    rec.mark(CNHWC_KERNEL_IMPLICIT_GEMM);
-    return hip_status(gemm_launch(g, stream));
+    g.part = reinterpret_cast<float*>(ws);
+    return gemm(CNHWC_KERNEL_IMPLICIT_GEMM);
   }
 
   if (algo == CNHWC_ALGO_UNFOLD_GEMM) {
     const int64_t kp = unfold_kp(k, d.dtype);
     const int64_t rows = p.unfold_rows;
+    g.part = reinterpret_cast<float*>(ws + align_up(uint64_t(rows) * kp * es, 256));
     for (int64_t m0 = 0; m0 < m_rows; m0 += rows) {
       const int64_t r = m0 + rows <= m_rows ? rows : m_rows - m0;
       rec.mark(CNHWC_KERNEL_UNFOLD);
@@ -117,9 +135,8 @@ cnhwc_status_t run_2d(const cnhwc_conv_desc_t& d, const cnhwc_plan_t& p, int32_t
       g.out = static_cast<char*>(y) + uint64_t(m0) * d.o * es;
       g.ldc = d.o;
       g.acc = acc ? acc + m0 * d.o : nullptr;
-      rec.mark(CNHWC_KERNEL_UNFOLD_GEMM);
-      e = gemm_launch(g, stream);
-      if (e != hipSuccess) return CNHWC_ERR_HIP;
+      const cnhwc_status_t st = gemm(CNHWC_KERNEL_UNFOLD_GEMM);
+      if (st != CNHWC_OK) return st;
     }
     return CNHWC_OK;
   }

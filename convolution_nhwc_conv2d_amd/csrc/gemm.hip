@@ -94,11 +94,15 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_kernel(const GemmParams p) {
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
   const int64_t m0 = int64_t(blockIdx.x) * BM;
   const int64_t n0 = int64_t(blockIdx.y) * BN;
-  const int64_t bz = blockIdx.z;
+  // blockIdx.z: batch index, or the K split (then the batch is 1)
+  const bool split = p.ksplit > 1;
+  const int64_t bz = split ? 0 : blockIdx.z;
+  const int64_t kstart = split ? int64_t(blockIdx.z) * p.kchunk : 0;
 
   const E* __restrict__ A = reinterpret_cast<const E*>(p.a) + bz * p.stride_a;
   const E* __restrict__ B = reinterpret_cast<const E*>(p.b) + bz * p.stride_b;
   const int64_t M = p.M, N = p.N, K = p.K;
+  const int64_t kend = split && kstart + p.kchunk < K ? kstart + p.kchunk : K;
 
   const int kv = tid & 7;   // this thread's 16-byte chunk within a row
   const int row0 = tid >> 3;
@@ -140,7 +144,7 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_kernel(const GemmParams p) {
   // ---- K position of the next chunk to load (implicit vector path)
   int32_t k_c = 0, k_kh = 0, k_kw = 0;
   if (LOAD == kLoadImplicit) {
-    const int64_t k0 = int64_t(kv) * VE;
+    const int64_t k0 = kstart + int64_t(kv) * VE;
     const int64_t tap = k0 / p.c;
     k_c = int32_t(k0 - tap * p.c);
     k_kh = int32_t(tap / p.kw);
@@ -314,11 +318,13 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_kernel(const GemmParams p) {
     mma(f1);
   };
 
-  const int64_t nk = (K + BK - 1) / BK;
+  // chunks of this split; kstart and the split length are multiples of BK,
+  // so only the last chunk of the whole K can be partial (masked by kk < K)
+  const int64_t nk = (kend - kstart + BK - 1) / BK;
   if constexpr (Cfg::NSETS == 1) {
     // ---- main loop, one staging set: chunk k+1 in flight while chunk k computes
     St s0;
-    load_chunk(0, s0);
+    load_chunk(kstart, s0);
     store_chunk(0, s0);
     __syncthreads();
     for (int64_t kc = 0; kc < nk; ++kc) {
@@ -326,7 +332,7 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_kernel(const GemmParams p) {
       const bool more = kc + 1 < nk;
       if (more) {
         advance_k();
-        load_chunk((kc + 1) * BK, s0);
+        load_chunk(kstart + (kc + 1) * BK, s0);
       }
       compute(cur);
       if (more) store_chunk(cur ^ 1, s0);
@@ -335,17 +341,17 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_kernel(const GemmParams p) {
   } else {
   // ---- main loop, two staging sets: chunk k+2 in flight while chunk k computes
   St s0, s1;
-  load_chunk(0, s0);
+  load_chunk(kstart, s0);
   store_chunk(0, s0);
   if (nk > 1) {
     advance_k();
-    load_chunk(BK, s1);
+    load_chunk(kstart + BK, s1);
   }
   __syncthreads();
   for (int64_t kc = 0; kc < nk; kc += 2) {
     if (kc + 2 < nk) {
       advance_k();
-      load_chunk((kc + 2) * BK, s0);
+      load_chunk(kstart + (kc + 2) * BK, s0);
     }
     compute(0);
     if (kc + 1 < nk) store_chunk(1, s1);
@@ -353,7 +359,7 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_kernel(const GemmParams p) {
     if (kc + 1 >= nk) break;
     if (kc + 3 < nk) {
       advance_k();
-      load_chunk((kc + 3) * BK, s1);
+      load_chunk(kstart + (kc + 3) * BK, s1);
     }
     compute(1);
     if (kc + 2 < nk) store_chunk(0, s0);
@@ -365,6 +371,9 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_kernel(const GemmParams p) {
   // row = 8*(r/4) + 4*(l/32) + r%4, col = l%32.
   E* __restrict__ out = reinterpret_cast<E*>(p.out) + bz * p.stride_out;
   float* __restrict__ accbuf = p.acc ? p.acc + bz * p.stride_out : nullptr;
+  // a K split stores its fp32 partial sums to its own slice (epilogue later)
+  float* __restrict__ partbuf = split ? p.part + int64_t(blockIdx.z) * M * p.ldc : nullptr;
+  const int epi = split ? -1 : p.epi;
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -376,11 +385,13 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_kernel(const GemmParams p) {
         if (row < M && col < N) {
           const int64_t idx = row * p.ldc + col;
           const float v = acc[i][j][r];
-          if (p.epi == kEpiStore) {
+          if (epi < 0) {
+            partbuf[idx] = v;
+          } else if (epi == kEpiStore) {
             out[idx] = from_f32<E, BF16>(v);
-          } else if (p.epi == kEpiAccFirst) {
+          } else if (epi == kEpiAccFirst) {
             accbuf[idx] = v;
-          } else if (p.epi == kEpiAccMid) {
+          } else if (epi == kEpiAccMid) {
             accbuf[idx] = accbuf[idx] + v;
           } else {
             out[idx] = from_f32<E, BF16>(accbuf[idx] + v);
@@ -389,10 +400,33 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_kernel(const GemmParams p) {
       }
 }
 
+// y (or the fp32 accumulator) from the K-split partial slices: the slices are
+// added in order 0, 1, ..., ksplit-1, then the epilogue of p is applied.
+template <typename E, bool BF16>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const GemmParams p) {
+  const int64_t t = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (t >= p.M * p.N) return;
+  const int64_t row = t / p.N, col = t - row * p.N;
+  const int64_t idx = row * p.ldc + col;
+  const int64_t slice = p.M * p.ldc;
+  float v = p.part[idx];
+  for (int s = 1; s < p.ksplit; ++s) v += p.part[s * slice + idx];
+  E* __restrict__ out = reinterpret_cast<E*>(p.out);
+  if (p.epi == kEpiStore) {
+    out[idx] = from_f32<E, BF16>(v);
+  } else if (p.epi == kEpiAccFirst) {
+    p.acc[idx] = v;
+  } else if (p.epi == kEpiAccMid) {
+    p.acc[idx] = p.acc[idx] + v;
+  } else {
+    out[idx] = from_f32<E, BF16>(p.acc[idx] + v);
+  }
+}
+
 template <class Cfg, bool BF16>
 hipError_t launch_cfg(const GemmParams& p, hipStream_t s) {
   const dim3 grid(unsigned((p.M + Cfg::BM - 1) / Cfg::BM), unsigned((p.N + Cfg::BN - 1) / Cfg::BN),
-                  unsigned(p.batch));
+                  unsigned(p.ksplit > 1 ? p.ksplit : p.batch));
   const int ve = Cfg::HALF ? 8 : 4;
   const bool bvec = p.ldb % ve == 0 && p.K % ve == 0;
   if (p.a_mode == kADense) {
@@ -415,11 +449,29 @@ hipError_t launch_half(const GemmParams& p, hipStream_t s) {
 
 }  // namespace
 
+int splitk_reduce_launch(const GemmParams& p, void* stream) {
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (p.M <= 0 || p.N <= 0) return hipSuccess;
+  if (p.ksplit < 2 || !p.part) return hipErrorInvalidValue;
+  const dim3 grid(unsigned((p.M * p.N + 255) / 256));
+  if (p.dtype == CNHWC_F32)
+    hipLaunchKernelGGL((splitk_reduce_kernel<float, false>), grid, dim3(256), 0, s, p);
+  else if (p.dtype == CNHWC_F16)
+    hipLaunchKernelGGL((splitk_reduce_kernel<uint16_t, false>), grid, dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL((splitk_reduce_kernel<uint16_t, true>), grid, dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
 int gemm_launch(const GemmParams& p, void* stream) {
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (p.M <= 0 || p.N <= 0) return hipSuccess;
   const bool f32cfg = p.config >= kCfgF32_N32 && p.config <= kCfgF32_N128;
   if (f32cfg != (p.dtype == CNHWC_F32)) return hipErrorInvalidValue;
+  if (p.ksplit > 1 && (p.batch != 1 || !p.part || p.config == kCfgH_256x256 ||
+                       p.kchunk <= 0 || p.kchunk % gemm_config_bk(p.config) != 0 ||
+                       (p.ksplit - 1) * p.kchunk >= p.K))
+    return hipErrorInvalidValue;
   switch (p.config) {
     case kCfgF32_N32: return launch_cfg<TileCfg<128, 32, 32, 32, false, 2>, false>(p, s);
     case kCfgF32_N64: return launch_cfg<TileCfg<128, 64, 32, 64, false, 1>, false>(p, s);

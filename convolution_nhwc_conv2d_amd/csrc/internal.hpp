@@ -84,9 +84,24 @@ struct GemmParams {
   // batched GEMM (Winograd tile positions): element offsets per batch index
   int64_t batch;
   int64_t stride_a, stride_b, stride_out;
+  // split K (batch == 1 only): split s covers k in [s*kchunk, min(K, (s+1)*kchunk))
+  // and stores its fp32 partial sums to part + s*M*ldc; a second kernel adds
+  // the splits in order 0, 1, ... and applies the epilogue.
+  int32_t ksplit;        // 0 or 1: no split
+  int64_t kchunk;        // multiple of the configuration's K chunk
+  float* part;
 };
 
 int gemm_launch(const GemmParams& p, void* stream);  // returns hipError_t
+
+// Sum of the ksplit partial slices (fixed order) with the epilogue of p.
+int splitk_reduce_launch(const GemmParams& p, void* stream);  // returns hipError_t
+
+// Most K splits of one GEMM (each adds an fp32 M x N slice to the workspace).
+constexpr int64_t kMaxSplitK = 16;
+
+// K elements per MFMA chunk of a tile configuration (split-K granularity).
+inline int64_t gemm_config_bk(int32_t config) { return config >= kCfgH_128x64 ? 64 : 32; }
 
 // fp16/bf16 256 x 256 tile GEMM with direct global -> LDS operand loads.
 // Applicable for dense A (lda, ldb, K multiples of 8) and for implicit A with

@@ -92,6 +92,56 @@ void tile_rule(uint64_t ws_limit, uint64_t own, uint64_t scratch, int64_t n, int
   *fallback = (t < 1) || (force_tile <= 0 && t < n && t * rows < CNHWC_MIN_TILE_ROWS);
 }
 
+// K splits for a GEMM grid too small to fill the device (tiles of gemm.hip
+// only; the 256x256 tile and the Winograd GEMMs never split).  Each split
+// gets a whole number of K chunks and at least 4; trailing empty splits are
+// dropped.  Returns 1 for no split.
+int32_t pick_split_k(int32_t cfg, int64_t m, int64_t n, int64_t k) {
+  int64_t bm = 128, bn = 128, occ = 2;
+  switch (cfg) {
+    case kCfgF32_N32: bn = 32; break;
+    case kCfgF32_N64: bn = 64; break;
+    case kCfgF32_N96: bn = 96; break;
+    case kCfgF32_N128: bn = 128; break;
+    case kCfgH_128x64: bn = 64; break;
+    case kCfgH_128x128: break;
+    case kCfgH_256x128: bm = 256; occ = 1; break;
+    case kCfgH_128x256: bn = 256; occ = 1; break;
+    default: return 1;
+  }
+  constexpr int64_t kCUs = 256;
+  const int64_t tiles = ceil_div(m, bm) * ceil_div(n, bn);
+  const int64_t slots = kCUs * occ;
+  if (2 * tiles > slots) return 1;
+  const int64_t nk = ceil_div(k, gemm_config_bk(cfg));
+  const int64_t s = std::min<int64_t>(std::min<int64_t>(slots / tiles, nk / 4), kMaxSplitK);
+  if (s < 2) return 1;
+  const int64_t per = ceil_div(nk, s);
+  return int32_t(ceil_div(nk, per));
+}
+
+// K splits: forced, or picked.
+cnhwc_status_t split_k_for(int32_t cfg, int64_t m, int64_t n, int64_t k, int32_t force,
+                           int32_t* splits) {
+  if (force == 0) {
+    *splits = pick_split_k(cfg, m, n, k);
+    return CNHWC_OK;
+  }
+  if (force == 1) {
+    *splits = 1;
+    return CNHWC_OK;
+  }
+  const int64_t nk = ceil_div(k, gemm_config_bk(cfg));
+  if (cfg == kCfgH_256x256 || force > nk) return CNHWC_ERR_NOT_APPLICABLE;
+  *splits = int32_t(ceil_div(nk, ceil_div(nk, int64_t(force))));
+  return CNHWC_OK;
+}
+
+// Bytes of the fp32 partial slices of a split GEMM with `rows` rows.
+uint64_t split_k_bytes(int32_t splits, int64_t rows, int64_t o) {
+  return splits > 1 ? align_up(uint64_t(splits) * uint64_t(rows) * uint64_t(o) * 4, 256) : 0;
+}
+
 // Tile configuration of the implicit / unfold GEMM: forced, or picked.  The
 // 256x256 direct-to-LDS tile needs C % 32 == 0 (implicit: a K chunk never
 // straddles two taps) or K % 8 == 0 (unfold rows).
@@ -120,6 +170,8 @@ cnhwc_status_t select_2d(const cnhwc_conv_desc_t& d, const int64_t out[3],
   p->out_d = 1;
   p->out_h = out[1];
   p->out_w = out[2];
+  p->split_k = 1;
+  cnhwc_status_t st = CNHWC_OK;
 
   if (force != CNHWC_ALGO_AUTO && force != CNHWC_ALGO_WINOGRAD &&
       force != CNHWC_ALGO_IMPLICIT_GEMM && force != CNHWC_ALGO_UNFOLD_GEMM)
@@ -167,14 +219,22 @@ cnhwc_status_t select_2d(const cnhwc_conv_desc_t& d, const int64_t out[3],
     p->algo = p->inner_algo = CNHWC_ALGO_UNFOLD_GEMM;
     p->unfold_rows = rows;
     p->n_chunks = ceil_div(m_rows, rows);
-    p->workspace_bytes = align_up(uint64_t(rows) * kp * es, 256);
-    return gemm_config_for(d, m_rows, false, o.force_gemm_config, &p->kernel_config);
+    st = gemm_config_for(d, m_rows, false, o.force_gemm_config, &p->kernel_config);
+    if (st != CNHWC_OK) return st;
+    st = split_k_for(p->kernel_config, m_rows, d.o, k, o.force_split_k, &p->split_k);
+    if (st != CNHWC_OK) return st;
+    p->workspace_bytes = align_up(uint64_t(rows) * kp * es, 256) + split_k_bytes(p->split_k, rows, d.o);
+    return CNHWC_OK;
   }
 
   // 3. Implicit GEMM (scratch-free).
   p->algo = p->inner_algo = CNHWC_ALGO_IMPLICIT_GEMM;
-  p->workspace_bytes = 0;
-  return gemm_config_for(d, m_rows, true, o.force_gemm_config, &p->kernel_config);
+  st = gemm_config_for(d, m_rows, true, o.force_gemm_config, &p->kernel_config);
+  if (st != CNHWC_OK) return st;
+  st = split_k_for(p->kernel_config, m_rows, d.o, k, o.force_split_k, &p->split_k);
+  if (st != CNHWC_OK) return st;
+  p->workspace_bytes = split_k_bytes(p->split_k, m_rows, d.o);
+  return CNHWC_OK;
 }
 
 cnhwc_status_t select_3d(const cnhwc_conv_desc_t& d, const int64_t out[3],
@@ -287,19 +347,21 @@ bool plan_equal(const cnhwc_plan_t& a, const cnhwc_plan_t& b) {
          a.own_bytes == b.own_bytes && a.budget_bytes == b.budget_bytes &&
          a.scratch_per_element == b.scratch_per_element &&
          a.workspace_bytes == b.workspace_bytes && a.kernel_config == b.kernel_config &&
+         a.split_k == b.split_k &&
          a.opts.ws_limit_bytes == b.opts.ws_limit_bytes &&
          a.opts.force_algo == b.opts.force_algo &&
          a.opts.force_inner_algo == b.opts.force_inner_algo &&
          a.opts.force_tile_batch == b.opts.force_tile_batch &&
          a.opts.force_unfold_rows == b.opts.force_unfold_rows &&
-         a.opts.force_gemm_config == b.opts.force_gemm_config;
+         a.opts.force_gemm_config == b.opts.force_gemm_config &&
+         a.opts.force_split_k == b.opts.force_split_k;
 }
 
 cnhwc_status_t select_impl(const cnhwc_conv_desc_t* desc, const cnhwc_select_opts_t* opts,
                            cnhwc_plan_t* plan) {
   if (!desc || !opts || !plan) return CNHWC_ERR_INVALID_ARGUMENT;
   if (opts->ws_limit_bytes == 0 || opts->force_tile_batch < 0 || opts->force_unfold_rows < 0 ||
-      opts->force_gemm_config < 0 || opts->reserved_opts != 0)
+      opts->force_gemm_config < 0 || opts->force_split_k < 0)
     return CNHWC_ERR_INVALID_ARGUMENT;
   if (opts->force_algo < CNHWC_ALGO_AUTO || opts->force_algo > CNHWC_ALGO_SMALL_KD ||
       opts->force_inner_algo < CNHWC_ALGO_AUTO || opts->force_inner_algo > CNHWC_ALGO_UNFOLD_GEMM)

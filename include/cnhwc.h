@@ -123,7 +123,11 @@ typedef struct {
                                 implicit / unfold GEMM (fp16/bf16: 10..14; fp32: 1..4).
                                 An id that does not suit the dtype or the shape is
                                 CNHWC_ERR_NOT_APPLICABLE. */
-  int32_t reserved_opts;     /* must be 0 */
+  int32_t force_split_k;     /* implicit / unfold GEMM: 0 = select, 1 = no K split,
+                                s > 1 = s splits of whole K chunks (trailing empty
+                                splits dropped).  NOT_APPLICABLE with the 256x256
+                                tile or for more splits than K chunks.  Winograd
+                                ignores it. */
 } cnhwc_select_opts_t;
 
 /* A plan: a plain value, a pure function of (descriptor, options). */
@@ -141,7 +145,12 @@ typedef struct {
   uint64_t scratch_per_element; /* Winograd: V + M bytes of one batch element */
   uint64_t workspace_bytes;  /* bytes the forward call needs in `workspace` */
   int32_t kernel_config;     /* GEMM tile configuration id */
-  int32_t reserved;
+  int32_t split_k;           /* implicit / unfold GEMM: K splits (1 = none).  With
+                                s > 1 the GEMM grid is too small to fill the device:
+                                split i sums its share of K into an fp32 slice of
+                                the workspace, and a second kernel adds the slices
+                                in order 0..s-1, so the result is still a function
+                                of the plan and the data only. */
   cnhwc_select_opts_t opts;  /* the options this plan was made from */
 } cnhwc_plan_t;
 
@@ -218,7 +227,8 @@ typedef enum {
   CNHWC_KERNEL_WINO_OUTPUT = 4,  /* Winograd output transform (per batch tile) */
   CNHWC_KERNEL_IMPLICIT_GEMM = 5,
   CNHWC_KERNEL_UNFOLD = 6,       /* one unfold chunk */
-  CNHWC_KERNEL_UNFOLD_GEMM = 7   /* the dense GEMM of one unfold chunk */
+  CNHWC_KERNEL_UNFOLD_GEMM = 7,  /* the dense GEMM of one unfold chunk */
+  CNHWC_KERNEL_SPLITK_REDUCE = 8 /* sum of the K-split partial sums + epilogue */
 } cnhwc_kernel_kind_t;
 
 /* Number of kernels a forward call with this plan launches (3D: over all

@@ -198,8 +198,8 @@ def test_lds_tile_parity(dtype, spec):
         assert plan.kernel_config == 14
         y = cn.conv2d(_dev(x), _dev(wt), **case.conv_kwargs(), algo=algo, gemm_config=14)
         check_parity(y.cpu(), yr, den, y.dtype, f"{case.name}/{algo}/256x256")
-        # same K order as the 128x128 tile: bit-identical results
-        y11 = cn.conv2d(_dev(x), _dev(wt), **case.conv_kwargs(), algo=algo, gemm_config=11)
+        # same K order as the 128x128 tile (unsplit): bit-identical results
+        y11 = cn.conv2d(_dev(x), _dev(wt), **case.conv_kwargs(), algo=algo, gemm_config=11, split_k=1)
         assert torch.equal(bits(y), bits(y11)), f"{case.name}/{algo}: 256x256 and 128x128 tiles differ"
 
 
@@ -215,5 +215,52 @@ def test_lds_tile_3d_accumulating_epilogue(dtype):
     y = cn.conv3d(_dev(x), _dev(wt), **case.conv_kwargs(), gemm_config=14)
     yr, den = oracle.conv(to_oracle(x), to_oracle(wt), **case.conv_kwargs())
     check_parity(y.cpu(), yr, den, y.dtype, case.name)
-    y11 = cn.conv3d(_dev(x), _dev(wt), **case.conv_kwargs(), gemm_config=11)
+    y11 = cn.conv3d(_dev(x), _dev(wt), **case.conv_kwargs(), gemm_config=11, split_k=1)
     assert torch.equal(bits(y), bits(y11))
+
+
+# ---------------------------------------------------------------- split K
+# Small-grid GEMMs split K; the partial sums are added in a fixed order by a
+# second kernel.  Forced splits (including a short last split) on every dtype
+# and path, against the oracle, and the same bits on every run.
+
+SPLIT_CASES = [  # name, n, h, w, c, o, k, stride, pad, dil, dtype
+    ("l4_7x7_512", 1, 7, 7, 512, 512, 3, 1, 1, 1, "f16"),
+    ("c120_unaligned", 1, 9, 11, 120, 72, 3, 1, 1, 1, "bf16"),
+    ("s2_d2", 1, 21, 19, 64, 96, 5, 2, 2, 2, "bf16"),
+    ("f32_small", 1, 16, 16, 32, 32, 3, 1, 1, 1, "f32"),
+    ("f32_c30", 2, 10, 9, 30, 40, 3, 1, 1, 1, "f32"),
+]
+
+
+@pytest.mark.parametrize("spec", SPLIT_CASES, ids=[c[0] for c in SPLIT_CASES])
+def test_split_k_parity(spec):
+    name, n, h, w, c, o, k, s, p, d, dt = spec
+    case = cw.ConvCase(f"split_{name}", n, h, w, c, o, k, k, (s, s), (p, p), (d, d), dt,
+                       "normal", "normal", None, 31, len(name) + c)
+    x, wt = case.input(), case.weight()
+    yr, den = oracle.conv(to_oracle(x), to_oracle(wt), **case.conv_kwargs())
+    for algo in ("implicit_gemm", "unfold_gemm"):
+        for sk in (2, 3, 5):
+            plan = cn.plan2d(case.x_shape(), case.w_shape(), **case.conv_kwargs(), dtype=x.dtype, algo=algo,
+                             split_k=sk)
+            if plan.split_k < 2:
+                continue
+            y = cn.conv2d(_dev(x), _dev(wt), **case.conv_kwargs(), algo=algo, split_k=sk)
+            check_parity(y.cpu(), yr, den, y.dtype, f"{case.name}/{algo}/split{plan.split_k}")
+            y2 = cn.conv2d(_dev(x), _dev(wt), **case.conv_kwargs(), algo=algo, split_k=sk)
+            assert torch.equal(bits(y), bits(y2)), f"{case.name}/{algo}/split{sk}: run-to-run bits differ"
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16"])
+def test_split_k_3d_accumulating_epilogue(dtype):
+    """Per-tap 2D convs of the 3D decomposition through split GEMMs: the sum
+    kernel applies the first / middle / last tap epilogues."""
+    case = cw.ConvCase(f"split3d_{dtype}", 1, 6, 7, 64, 48, 3, 3, (1, 1, 1), (0, 1, 1), (1, 1, 1), dtype,
+                       "normal", "normal", None, 37, 3, nd=3, d=5, kd=3)
+    x, wt = case.input(), case.weight()
+    plan = cn.plan3d(case.x_shape(), case.w_shape(), **case.conv_kwargs(), dtype=x.dtype, split_k=3)
+    assert plan.algo_name == "small_kd" and plan.split_k == 3
+    y = cn.conv3d(_dev(x), _dev(wt), **case.conv_kwargs(), split_k=3)
+    yr, den = oracle.conv(to_oracle(x), to_oracle(wt), **case.conv_kwargs())
+    check_parity(y.cpu(), yr, den, y.dtype, case.name)

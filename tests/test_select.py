@@ -331,7 +331,38 @@ def test_forced_gemm_config():
         cn.select(d, o)
     assert e.value.name == "INVALID_ARGUMENT"
     o = cn.make_opts()
-    o.reserved_opts = 1
+    o.force_split_k = -1
     with pytest.raises(cn.CnhwcError) as e:
         cn.select(d, o)
     assert e.value.name == "INVALID_ARGUMENT"
+
+
+# ------------------------------------------------------------- split K
+
+def test_split_k_for_small_grids_only():
+    """A GEMM grid too small to fill the device splits K; a large one does not."""
+    small = cn.plan2d((1, 7, 7, 512), (512, 3, 3, 512), 1, 1, 1, F16)   # ResNet-50 layer4, batch 1
+    assert small.split_k > 1
+    m, o = 49, 512
+    assert small.workspace_bytes == -(-small.split_k * m * o * 4 // 256) * 256
+    assert cn.lib.cnhwc_launch_count(ctypes.byref(cn.make_desc((1, 7, 7, 512), (512, 3, 3, 512), 1, 1, 1, F16)),
+                                     ctypes.byref(small)) == 2
+    big = cn.plan2d((64, 32, 32, 256), (4096, 3, 3, 256), 1, 1, 1, F16)
+    assert big.split_k == 1
+    wino = cn.plan2d((2, 64, 64, 192), (96, 3, 3, 192), 1, 1, 1, algo="winograd", split_k=4)
+    assert wino.split_k == 1
+
+
+def test_forced_split_k():
+    xs, ws = (1, 7, 7, 512), (512, 3, 3, 512)   # K = 4608 = 72 chunks of 64
+    assert cn.plan2d(xs, ws, 1, 1, 1, F16, split_k=1).split_k == 1
+    assert cn.plan2d(xs, ws, 1, 1, 1, F16, split_k=3).split_k == 3
+    assert cn.plan2d(xs, ws, 1, 1, 1, F16, split_k=7).split_k == 7    # 11 chunks per split, last 6
+    assert cn.plan2d(xs, ws, 1, 1, 1, F16, split_k=72).split_k == 72
+    assert cn.plan2d(xs, ws, 1, 1, 1, F16, split_k=50).split_k == 36  # 2 chunks each: 36 splits
+    p = cn.plan2d(xs, ws, 1, 1, 1, F16, algo="unfold_gemm", split_k=5)
+    assert p.split_k == 5 and p.workspace_bytes >= 5 * 49 * 512 * 4
+    for kw in [dict(split_k=73), dict(split_k=2, gemm_config=14)]:
+        with pytest.raises(cn.CnhwcError) as e:
+            cn.plan2d(xs, ws, 1, 1, 1, F16, **kw)
+        assert e.value.name == "NOT_APPLICABLE", kw
