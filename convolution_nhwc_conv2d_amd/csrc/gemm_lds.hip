@@ -105,6 +105,15 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
+// Workgroup barrier that the compiler may not move memory accesses across
+// (the signal fences emit no instruction and no wait; the LDS ordering
+// itself comes from the explicit vmcnt waits before each barrier).
+__device__ __forceinline__ void block_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 struct Frag {
   uint4 a[4];
   uint4 b[4];
@@ -275,7 +284,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_lds_kernel(const GemmParams 
 #pragma unroll
   for (int i = 0; i < kStages - 1; ++i) issue(i);
   wait_vmcnt<(kStages - 2) * kLoads>();
-  __builtin_amdgcn_s_barrier();
+  block_barrier();
   __builtin_amdgcn_sched_barrier(0);
   read(0, 0, f0);
 
@@ -297,7 +306,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_lds_kernel(const GemmParams 
     }
     __builtin_amdgcn_sched_barrier(0);
     wait_vmcnt<(kStages - 3) * kLoads>();
-    __builtin_amdgcn_s_barrier();
+    block_barrier();
     __builtin_amdgcn_sched_barrier(0);
     // The next chunk's loads and K step 0 reads interleaved with K step 1
     // MFMAs: per MFMA one load into LDS and its address arithmetic, and a
@@ -328,7 +337,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_lds_kernel(const GemmParams 
   // row = 8 (r / 4) + 4 (l / 32) + r % 4, col = l % 32; the slice is written to
   // the wavefront's own LDS area and read back as 8 consecutive columns per
   // lane, 16 lanes per row, so global stores are 16-byte and row-contiguous.
-  __builtin_amdgcn_s_barrier();  // every wavefront has finished its LDS reads
+  block_barrier();  // every wavefront has finished its LDS reads
   constexpr int EP = 128 + 4;    // padded slice row (floats)
   static_assert(2 * 32 * EP * 4 <= kRingBytes, "two epilogue slices fit one ring");
   float* ep = reinterpret_cast<float*>((wave < 2 ? g_ring_a : g_ring_b) + (wave & 1) * (kRingBytes / 2));
