@@ -222,6 +222,7 @@ cnhwc_status_t validate(const cnhwc_conv_desc_t* desc, const cnhwc_plan_t* plan,
 
 // Kernels a whole forward call launches (3D: all taps).
 int64_t plan_launch_count(const cnhwc_conv_desc_t& d, const cnhwc_plan_t& p) {
+  if (d.nd == 3 && p.algo == CNHWC_ALGO_IMPLICIT_GEMM) return p.split_k > 1 ? 2 : 1;
   if (p.algo == CNHWC_ALGO_SMALL_KD) {
     const int64_t per = launches_2d(p, p.inner_algo);
     return per < 0 ? -1 : per * d.kd;
@@ -248,10 +249,62 @@ cnhwc_status_t fwd3d(const cnhwc_conv_desc_t* desc, const cnhwc_plan_t* plan, co
                      void* stream, Recorder& rec) {
   const cnhwc_status_t st = validate(desc, plan, 3, x, w, y, workspace, workspace_bytes);
   if (st != CNHWC_OK) return st;
-  if (plan->algo != CNHWC_ALGO_SMALL_KD) return CNHWC_ERR_INTERNAL;
+  if (plan->algo != CNHWC_ALGO_SMALL_KD && plan->algo != CNHWC_ALGO_IMPLICIT_GEMM)
+    return CNHWC_ERR_INTERNAL;
   if (rec.events && plan_launch_count(*desc, *plan) + 1 > rec.n) return CNHWC_ERR_INVALID_ARGUMENT;
   rec.n = 0;
   const cnhwc_conv_desc_t& d = *desc;
+  if (plan->algo == CNHWC_ALGO_IMPLICIT_GEMM) {
+    // native 3D implicit GEMM: rows (n, od, oh, ow), k = ((kd*KH + kh)*KW + kw)*C + c
+    GemmParams g;
+    std::memset(&g, 0, sizeof(g));
+    g.dtype = d.dtype;
+    g.a_mode = kAImplicit;
+    g.epi = kEpiStore;
+    g.config = plan->kernel_config;
+    g.M = d.n * plan->out_d * plan->out_h * plan->out_w;
+    g.N = d.o;
+    g.K = d.kd * d.kh * d.kw * d.c;
+    g.a = x;
+    g.b = w;
+    g.ldb = g.K;
+    g.out = y;
+    g.ldc = d.o;
+    g.h = d.h;
+    g.w = d.w;
+    g.c = d.c;
+    g.oh = plan->out_h;
+    g.ow = plan->out_w;
+    g.kh = d.kh;
+    g.kw = d.kw;
+    g.sh = d.stride[1];
+    g.sw = d.stride[2];
+    g.ph = d.pad[1];
+    g.pw = d.pad[2];
+    g.dh = d.dil[1];
+    g.dw = d.dil[2];
+    g.d = d.d;
+    g.od = plan->out_d;
+    g.kd = d.kd;
+    g.sd = d.stride[0];
+    g.pd = d.pad[0];
+    g.dd = d.dil[0];
+    g.batch = 1;
+    g.ksplit = plan->split_k;
+    if (plan->split_k > 1) {
+      const int64_t bk = gemm_config_bk(plan->kernel_config);
+      g.kchunk = ceil_div(ceil_div(g.K, bk), plan->split_k) * bk;
+      g.part = static_cast<float*>(workspace);
+    }
+    rec.mark(CNHWC_KERNEL_IMPLICIT_GEMM);
+    if (gemm_launch(g, stream) != hipSuccess) return CNHWC_ERR_HIP;
+    if (g.ksplit > 1) {
+      rec.mark(CNHWC_KERNEL_SPLITK_REDUCE);
+      if (splitk_reduce_launch(g, stream) != hipSuccess) return CNHWC_ERR_HIP;
+    }
+    rec.mark(CNHWC_KERNEL_END);
+    return CNHWC_OK;
+  }
   const int64_t od = plan->out_d;
   const cnhwc_conv_desc_t f = frame_desc(d, od);
   const uint64_t es = dtype_size(d.dtype);

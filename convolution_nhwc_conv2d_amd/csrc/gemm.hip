@@ -70,7 +70,8 @@ struct Stage {
   u32x4 b[NB];
 };
 
-template <class Cfg, int LOAD, bool BF16>
+// D3: the implicit A operand is a 3D NDHWC gather (depth window as well).
+template <class Cfg, int LOAD, bool BF16, bool D3 = false>
 __global__ __launch_bounds__(Cfg::NT) void gemm_kernel(const GemmParams p) {
   using E = typename std::conditional<Cfg::HALF, uint16_t, float>::type;
   constexpr int BM = Cfg::BM, BN = Cfg::BN, BK = Cfg::BK, WM = Cfg::WM, WN = Cfg::WN;
@@ -112,26 +113,40 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_kernel(const GemmParams p) {
   // the row's window origin (oh*sh - ph, ow*sw - pw) in image n (may be
   // negative: only used once the tap is known to be inside the image).
   int64_t a_off[A_VEC];
-  int32_t a_ih0[A_VEC], a_iw0[A_VEC];
+  int32_t a_ih0[A_VEC], a_iw0[A_VEC], a_id0[A_VEC];
 #pragma unroll
   for (int j = 0; j < A_VEC; ++j) {
     const int64_t m = m0 + row0 + j * RP;
+    a_id0[j] = 0;
     if (LOAD == kLoadDense || LOAD == kLoadDenseScalar) {
       a_off[j] = m < M ? m * p.lda : -1;
       a_ih0[j] = a_iw0[j] = 0;
     } else if (m < M) {
       const int64_t hw = p.oh * p.ow;
-      const int64_t n = m / hw;
-      const int64_t r = m - n * hw;
+      int64_t n, r;
+      if constexpr (D3) {
+        const int64_t dhw = p.od * hw;
+        n = m / dhw;
+        r = m - n * dhw;
+        const int64_t od = r / hw;
+        r -= od * hw;
+        a_id0[j] = int32_t(od * p.sd - p.pd);
+      } else {
+        n = m / hw;
+        r = m - n * hw;
+      }
       const int64_t oh = r / p.ow;
       const int64_t ow = r - oh * p.ow;
       a_ih0[j] = int32_t(oh * p.sh - p.ph);
       a_iw0[j] = int32_t(ow * p.sw - p.pw);
-      a_off[j] = n * p.h * p.w * p.c + (int64_t(a_ih0[j]) * p.w + a_iw0[j]) * p.c;
+      const int64_t depth = D3 ? p.d : 1;
+      a_off[j] = n * depth * p.h * p.w * p.c +
+                 ((int64_t(a_id0[j]) * p.h + a_ih0[j]) * p.w + a_iw0[j]) * p.c;
     } else {
       a_off[j] = 0;
       a_ih0[j] = -0x40000000;  // every tap out of range -> zeros
       a_iw0[j] = -0x40000000;
+      a_id0[j] = -0x40000000;
     }
   }
   // B rows
@@ -142,13 +157,20 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_kernel(const GemmParams p) {
     b_off[j] = n < N ? n * p.ldb : -1;
   }
   // ---- K position of the next chunk to load (implicit vector path)
-  int32_t k_c = 0, k_kh = 0, k_kw = 0;
+  // (3D: the tap is (k_kd, k_kh, k_kw); past the end k_kd >= KD, 2D: k_kh >= KH)
+  int32_t k_c = 0, k_kh = 0, k_kw = 0, k_kd = 0;
   if (LOAD == kLoadImplicit) {
     const int64_t k0 = kstart + int64_t(kv) * VE;
     const int64_t tap = k0 / p.c;
     k_c = int32_t(k0 - tap * p.c);
-    k_kh = int32_t(tap / p.kw);
-    k_kw = int32_t(tap - int64_t(k_kh) * p.kw);
+    const int64_t t2 = tap / p.kw;
+    k_kw = int32_t(tap - t2 * p.kw);
+    if constexpr (D3) {
+      k_kd = int32_t(t2 / p.kh);
+      k_kh = int32_t(t2 - int64_t(k_kd) * p.kh);
+    } else {
+      k_kh = int32_t(t2);
+    }
   }
   auto advance_k = [&]() {
     if (LOAD == kLoadImplicit) {
@@ -158,6 +180,10 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_kernel(const GemmParams p) {
         if (++k_kw == p.kw) {
           k_kw = 0;
           ++k_kh;
+          if (D3 && k_kh == p.kh) {
+            k_kh = 0;
+            ++k_kd;
+          }
         }
       }
     }
@@ -176,13 +202,14 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_kernel(const GemmParams p) {
       }
     } else if constexpr (LOAD == kLoadImplicit) {
       // one tap for the whole chunk slot: shared offset, per-row bounds
-      const int32_t dhh = k_kh * p.dh, dww = k_kw * p.dw;
-      const int64_t tap_off = (int64_t(dhh) * p.w + dww) * p.c + k_c;
-      const bool tap_in = k_kh < p.kh;
+      const int32_t dhh = k_kh * p.dh, dww = k_kw * p.dw, ddd = D3 ? k_kd * p.dd : 0;
+      const int64_t tap_off = ((int64_t(ddd) * p.h + dhh) * p.w + dww) * p.c + k_c;
+      const bool tap_in = D3 ? k_kd < p.kd : k_kh < p.kh;
 #pragma unroll
       for (int j = 0; j < A_VEC; ++j) {
         const bool ok = tap_in && uint32_t(a_ih0[j] + dhh) < uint32_t(p.h) &&
-                        uint32_t(a_iw0[j] + dww) < uint32_t(p.w);
+                        uint32_t(a_iw0[j] + dww) < uint32_t(p.w) &&
+                        (!D3 || uint32_t(a_id0[j] + ddd) < uint32_t(p.d));
         const gvec_ptr ptr = ok ? gvec(A + a_off[j] + tap_off) : zero;
         st.a[j] = *ptr;
       }
@@ -202,13 +229,16 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_kernel(const GemmParams p) {
             if (k < K) {
               const int64_t tap = k / p.c;
               const int64_t c = k - tap * p.c;
-              const int64_t kh = tap / p.kw;
-              const int64_t kw = tap - kh * p.kw;
-              const int64_t dh_ = kh * p.dh, dw_ = kw * p.dw;
+              const int64_t t2 = tap / p.kw;
+              const int64_t kw = tap - t2 * p.kw;
+              const int64_t kd = D3 ? t2 / p.kh : 0;
+              const int64_t kh = t2 - kd * p.kh;
+              const int64_t dd_ = kd * p.dd, dh_ = kh * p.dh, dw_ = kw * p.dw;
+              const int64_t id = a_id0[j] + dd_;
               const int64_t ih = a_ih0[j] + dh_;
               const int64_t iw = a_iw0[j] + dw_;
-              if (ih >= 0 && ih < p.h && iw >= 0 && iw < p.w)
-                e[t] = A[a_off[j] + (dh_ * p.w + dw_) * p.c + c];
+              if ((!D3 || (id >= 0 && id < p.d)) && ih >= 0 && ih < p.h && iw >= 0 && iw < p.w)
+                e[t] = A[a_off[j] + ((dd_ * p.h + dh_) * p.w + dw_) * p.c + c];
             }
           }
         }
@@ -434,6 +464,11 @@ hipError_t launch_cfg(const GemmParams& p, hipStream_t s) {
       hipLaunchKernelGGL((gemm_kernel<Cfg, kLoadDense, BF16>), grid, dim3(Cfg::NT), 0, s, p);
     else
       hipLaunchKernelGGL((gemm_kernel<Cfg, kLoadDenseScalar, BF16>), grid, dim3(Cfg::NT), 0, s, p);
+  } else if (p.kd > 0) {  // native 3D gather
+    if (p.c % ve == 0 && bvec)
+      hipLaunchKernelGGL((gemm_kernel<Cfg, kLoadImplicit, BF16, true>), grid, dim3(Cfg::NT), 0, s, p);
+    else
+      hipLaunchKernelGGL((gemm_kernel<Cfg, kLoadScalar, BF16, true>), grid, dim3(Cfg::NT), 0, s, p);
   } else if (p.c % ve == 0 && bvec) {
     hipLaunchKernelGGL((gemm_kernel<Cfg, kLoadImplicit, BF16>), grid, dim3(Cfg::NT), 0, s, p);
   } else {

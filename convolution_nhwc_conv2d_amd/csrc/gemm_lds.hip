@@ -119,7 +119,8 @@ struct Frag {
   uint4 b[4];
 };
 
-template <bool BF16, bool IMPLICIT>
+// D3: the implicit A operand is a 3D NDHWC gather (depth window as well).
+template <bool BF16, bool IMPLICIT, bool D3 = false>
 __global__ __launch_bounds__(kThreads, 1) void gemm_lds_kernel(const GemmParams p) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
@@ -151,26 +152,40 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_lds_kernel(const GemmParams 
   const int kin = lpc * 8;  // element offset of the piece within the chunk
 
   int64_t a_off[kLoadsA];
-  int32_t a_ih0[kLoadsA], a_iw0[kLoadsA];
+  int32_t a_ih0[kLoadsA], a_iw0[kLoadsA], a_id0[kLoadsA];
 #pragma unroll
   for (int j = 0; j < kLoadsA; ++j) {
     const int64_t m = m0 + (wave * kLoadsA + j) * kRowsPerLoad + lrow;
+    a_id0[j] = 0;
     if (!IMPLICIT) {
       a_off[j] = m < M ? m * p.lda + kin : -1;
       a_ih0[j] = a_iw0[j] = 0;
     } else if (m < M) {
       const int64_t hw = p.oh * p.ow;
-      const int64_t n = m / hw;
-      const int64_t r = m - n * hw;
+      int64_t n, r;
+      if constexpr (D3) {
+        const int64_t dhw = p.od * hw;
+        n = m / dhw;
+        r = m - n * dhw;
+        const int64_t od = r / hw;
+        r -= od * hw;
+        a_id0[j] = int32_t(od * p.sd - p.pd);
+      } else {
+        n = m / hw;
+        r = m - n * hw;
+      }
       const int64_t oh = r / p.ow;
       const int64_t ow = r - oh * p.ow;
       a_ih0[j] = int32_t(oh * p.sh - p.ph);
       a_iw0[j] = int32_t(ow * p.sw - p.pw);
-      a_off[j] = n * p.h * p.w * p.c + (int64_t(a_ih0[j]) * p.w + a_iw0[j]) * p.c + kin;
+      const int64_t depth = D3 ? p.d : 1;
+      a_off[j] = n * depth * p.h * p.w * p.c +
+                 ((int64_t(a_id0[j]) * p.h + a_ih0[j]) * p.w + a_iw0[j]) * p.c + kin;
     } else {
       a_off[j] = 0;
       a_ih0[j] = -0x40000000;
       a_iw0[j] = -0x40000000;
+      a_id0[j] = -0x40000000;
     }
   }
   int64_t b_off[kLoadsB];
@@ -185,7 +200,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_lds_kernel(const GemmParams 
   // the end are issued too (dense: as zero loads), so every wait count is
   // fixed.
   int64_t k_next = 0;
-  int32_t t_c = 0, t_kh = 0, t_kw = 0;
+  int32_t t_c = 0, t_kh = 0, t_kw = 0, t_kd = 0;
   const gvec_ptr zero = gvec(&g_lds_zero16);
 
   const uint32_t ring_a = lds_base(g_ring_a) + wave * (kLoadsA * 64 * 16);
@@ -197,12 +212,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_lds_kernel(const GemmParams 
       // Branch-free, so the address arithmetic can be interleaved with the
       // MFMAs.  Chunks past the end wrap around to tap 0 and load real data,
       // which lands in stages that are never read again.
-      const int32_t dhh = t_kh * p.dh, dww = t_kw * p.dw;
-      const int64_t tap_off = (int64_t(dhh) * p.w + dww) * p.c + t_c;
+      const int32_t dhh = t_kh * p.dh, dww = t_kw * p.dw, ddd = D3 ? t_kd * p.dd : 0;
+      const int64_t tap_off = ((int64_t(ddd) * p.h + dhh) * p.w + dww) * p.c + t_c;
 #pragma unroll
       for (int j = 0; j < kLoadsA; ++j) {
-        const bool ok = (uint32_t(a_ih0[j] + dhh) < uint32_t(p.h)) &
-                        (uint32_t(a_iw0[j] + dww) < uint32_t(p.w));
+        bool ok = (uint32_t(a_ih0[j] + dhh) < uint32_t(p.h)) &
+                  (uint32_t(a_iw0[j] + dww) < uint32_t(p.w));
+        if constexpr (D3) ok = ok & (uint32_t(a_id0[j] + ddd) < uint32_t(p.d));
         const gvec_ptr src = ok ? gvec(A + a_off[j] + tap_off) : zero;
         __builtin_amdgcn_global_load_lds(src, lds_addr(sa + j * (64 * 16)), 16, 0, 0);
       }
@@ -219,7 +235,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_lds_kernel(const GemmParams 
       const bool ww = t_kw == p.kw;
       t_kw = ww ? 0 : t_kw;
       t_kh += ww ? 1 : 0;
-      t_kh = t_kh == p.kh ? 0 : t_kh;
+      if constexpr (D3) {
+        const bool wh = t_kh == p.kh;
+        t_kh = wh ? 0 : t_kh;
+        t_kd += wh ? 1 : 0;
+        t_kd = t_kd == p.kd ? 0 : t_kd;
+      } else {
+        t_kh = t_kh == p.kh ? 0 : t_kh;
+      }
     } else {
       const bool k_in = k_next + kin < K;
 #pragma unroll
@@ -412,6 +435,8 @@ hipError_t launch_lds(const GemmParams& p, hipStream_t s) {
   const dim3 grid{unsigned(tiles), 1u, 1u};
   if (p.a_mode == kADense)
     hipLaunchKernelGGL((gemm_lds_kernel<BF16, false>), grid, dim3(kThreads), 0, s, p);
+  else if (p.kd > 0)  // native 3D gather
+    hipLaunchKernelGGL((gemm_lds_kernel<BF16, true, true>), grid, dim3(kThreads), 0, s, p);
   else
     hipLaunchKernelGGL((gemm_lds_kernel<BF16, true>), grid, dim3(kThreads), 0, s, p);
   return hipGetLastError();

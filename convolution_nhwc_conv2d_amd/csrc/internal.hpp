@@ -76,6 +76,10 @@ struct GemmParams {
   // implicit-A geometry (input image [n][h][w][c])
   int64_t h, w, c, oh, ow, kh, kw;
   int32_t sh, sw, ph, pw, dh, dw;
+  // native 3D implicit A (input [n][d][h][w][c], k = ((kd*KH + kh)*KW + kw)*C + c);
+  // all zero for 2D
+  int64_t d, od, kd;
+  int32_t sd, pd, dd;
   const void* b;
   int64_t ldb;           // B row stride (elements)
   void* out;             // output rows, row stride ldc (elements of dtype)
@@ -101,7 +105,9 @@ int splitk_reduce_launch(const GemmParams& p, void* stream);  // returns hipErro
 constexpr int64_t kMaxSplitK = 16;
 
 // K elements per MFMA chunk of a tile configuration (split-K granularity).
-inline int64_t gemm_config_bk(int32_t config) { return config >= kCfgH_128x64 ? 64 : 32; }
+inline int64_t gemm_config_bk(int32_t config) {
+  return config >= kCfgH_128x64 && config != kCfgH_256x256 ? 64 : 32;
+}
 
 // fp16/bf16 256 x 256 tile GEMM with direct global -> LDS operand loads.
 // Applicable for dense A (lda, ldb, K multiples of 8) and for implicit A with

@@ -239,31 +239,63 @@ cnhwc_status_t select_2d(const cnhwc_conv_desc_t& d, const int64_t out[3],
 
 cnhwc_status_t select_3d(const cnhwc_conv_desc_t& d, const int64_t out[3],
                          const cnhwc_select_opts_t& o, cnhwc_plan_t* p) {
-  const bool forced = o.force_algo == CNHWC_ALGO_SMALL_KD;
-  if (o.force_algo != CNHWC_ALGO_AUTO && !forced) return CNHWC_ERR_NOT_APPLICABLE;
+  const bool force_kd = o.force_algo == CNHWC_ALGO_SMALL_KD;
+  const bool force_native = o.force_algo == CNHWC_ALGO_IMPLICIT_GEMM;
+  if (o.force_algo != CNHWC_ALGO_AUTO && !force_kd && !force_native)
+    return CNHWC_ERR_NOT_APPLICABLE;
   // Structural requirements of the decomposition itself.
   const bool structural = d.n == 1 && d.stride[0] == 1 && d.dil[0] == 1 && d.pad[0] == 0;
   // AUTO guard: also KD <= 7, dilation 1 everywhere, channels multiple of 16.
   const bool guard = structural && d.kd <= 7 && d.dil[1] == 1 && d.dil[2] == 1 &&
                      d.c % 16 == 0 && d.o % 16 == 0;
-  if (forced ? !structural : !guard)
-    return forced ? CNHWC_ERR_NOT_APPLICABLE : CNHWC_ERR_UNSUPPORTED;
-  const cnhwc_conv_desc_t f = frame_desc(d, out[0]);
-  int64_t fo[3];
-  cnhwc_status_t st = check_desc(f, fo);
-  if (st != CNHWC_OK) return st;
-  cnhwc_plan_t inner;
-  std::memset(&inner, 0, sizeof(inner));
-  st = select_2d(f, fo, o, o.force_inner_algo, &inner);
-  if (st != CNHWC_OK) return st;
-  *p = inner;
-  p->algo = CNHWC_ALGO_SMALL_KD;
-  p->inner_algo = inner.algo;
+  if (force_kd && !structural) return CNHWC_ERR_NOT_APPLICABLE;
+  if (force_native && o.force_inner_algo != CNHWC_ALGO_AUTO) return CNHWC_ERR_INVALID_ARGUMENT;
+
+  // 1. Depth decomposition (MLX PR "Decompose small kernel-depth 3D convs into
+  // 2D convs", Change): forced, or under AUTO when the guard holds and the
+  // per-frame 2D conv takes Winograd (the reason the page decomposes: the 2D
+  // path has Winograd, the native 3D path does not) or an inner algorithm is
+  // forced.
+  if (force_kd || (!force_native && guard)) {
+    const cnhwc_conv_desc_t f = frame_desc(d, out[0]);
+    int64_t fo[3];
+    cnhwc_status_t st = check_desc(f, fo);
+    if (st != CNHWC_OK) return st;
+    cnhwc_plan_t inner;
+    std::memset(&inner, 0, sizeof(inner));
+    st = select_2d(f, fo, o, o.force_inner_algo, &inner);
+    if (st != CNHWC_OK) return st;
+    if (force_kd || inner.algo == CNHWC_ALGO_WINOGRAD || o.force_inner_algo != CNHWC_ALGO_AUTO) {
+      *p = inner;
+      p->algo = CNHWC_ALGO_SMALL_KD;
+      p->inner_algo = inner.algo;
+      p->out_d = out[0];
+      const uint64_t acc = d.dtype == CNHWC_F32
+                               ? 0
+                               : align_up(uint64_t(out[0]) * out[1] * out[2] * d.o * 4, 256);
+      p->workspace_bytes = acc + inner.workspace_bytes;
+      return CNHWC_OK;
+    }
+  } else if (o.force_inner_algo != CNHWC_ALGO_AUTO) {
+    return CNHWC_ERR_NOT_APPLICABLE;  // an inner algorithm needs the decomposition
+  }
+
+  // 2. Native 3D implicit GEMM: one GEMM with K = KD*KH*KW*C over the NDHWC
+  // gather, any batch, depth stride, padding and dilation.  It is the page's
+  // fall-through for what the guard rejects, and (all taps in one K loop, no
+  // per-tap accumulator passes) the fused form of the decomposition.
+  const int64_t m_rows = d.n * out[0] * out[1] * out[2];
+  const int64_t k = d.kd * d.kh * d.kw * d.c;
+  p->algo = p->inner_algo = CNHWC_ALGO_IMPLICIT_GEMM;
   p->out_d = out[0];
-  const uint64_t acc = d.dtype == CNHWC_F32
-                           ? 0
-                           : align_up(uint64_t(out[0]) * out[1] * out[2] * d.o * 4, 256);
-  p->workspace_bytes = acc + inner.workspace_bytes;
+  p->out_h = out[1];
+  p->out_w = out[2];
+  p->split_k = 1;
+  cnhwc_status_t st = gemm_config_for(d, m_rows, true, o.force_gemm_config, &p->kernel_config);
+  if (st != CNHWC_OK) return st;
+  st = split_k_for(p->kernel_config, m_rows, d.o, k, o.force_split_k, &p->split_k);
+  if (st != CNHWC_OK) return st;
+  p->workspace_bytes = split_k_bytes(p->split_k, m_rows, d.o);
   return CNHWC_OK;
 }
 

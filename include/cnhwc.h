@@ -82,7 +82,7 @@ typedef enum {
   CNHWC_ALGO_WINOGRAD = 1,      /* 3x3 stride-1 dilation-1 2D only */
   CNHWC_ALGO_IMPLICIT_GEMM = 2, /* any 2D conv; scratch-free */
   CNHWC_ALGO_UNFOLD_GEMM = 3,   /* any 2D conv; unfold buffer in the workspace */
-  CNHWC_ALGO_SMALL_KD = 4       /* 3D as KD accumulated 2D convs */
+  CNHWC_ALGO_SMALL_KD = 4       /* 3D as KD accumulated 2D convs (3D: IMPLICIT_GEMM = native) */
 } cnhwc_algo_t;
 
 typedef enum {
@@ -170,13 +170,19 @@ const char* cnhwc_status_string(cnhwc_status_t s);
  *  2. Unfold + GEMM for F16/BF16 with O >= CNHWC_UNFOLD_MIN_COUT.
  *  3. Implicit GEMM.
  * AUTO, 3D (3D page, Change): SMALL_KD when N == 1, KD <= 7, depth stride 1,
- *   dilation 1 in every dim, depth pad 0, C % 16 == 0 and O % 16 == 0; the
- *   per-tap 2D algorithm is AUTO-selected on the [OD,H,W,C] frame conv.  Any
- *   other 3D conv returns CNHWC_ERR_UNSUPPORTED.
+ *   dilation 1 in every dim, depth pad 0, C % 16 == 0 and O % 16 == 0 and the
+ *   per-tap 2D algorithm (AUTO-selected on the [OD,H,W,C] frame conv, or
+ *   forced by force_inner_algo) is Winograd; the decomposition exists to give
+ *   the frames the 2D Winograd path.  Otherwise IMPLICIT_GEMM: the native 3D
+ *   implicit GEMM, one GEMM with K = KD*KH*KW*C over the NDHWC gather (any
+ *   batch, depth stride, padding and dilation; the page's fall-through for
+ *   what the guard rejects, and the decomposition with its taps fused).
  * Forcing: WINOGRAD needs only 3x3/stride 1/dilation 1 (the channel gates are
  *   skipped); a forced tile size is capped by the budget tile (tiling page,
  *   Testing).  SMALL_KD needs N == 1, depth stride 1, depth dilation 1, depth
- *   pad 0.
+ *   pad 0.  For 3D, IMPLICIT_GEMM (the native path) and SMALL_KD can be
+ *   forced; WINOGRAD and UNFOLD_GEMM are NOT_APPLICABLE, and force_inner_algo
+ *   with the native path is INVALID_ARGUMENT.
  * Returns OK and fills *plan, or an error (plan untouched). */
 cnhwc_status_t cnhwc_conv_select(const cnhwc_conv_desc_t* desc, const cnhwc_select_opts_t* opts,
                                  cnhwc_plan_t* plan);
@@ -208,7 +214,9 @@ cnhwc_status_t cnhwc_conv2d_fwd(const cnhwc_conv_desc_t* desc, const cnhwc_plan_
                                 const void* x, const void* w, void* y, void* workspace,
                                 uint64_t workspace_bytes, void* hip_stream);
 
-/* 3D forward (nd == 3), same conventions.  SMALL_KD (3D page, Change): for each
+/* 3D forward (nd == 3), same conventions.  IMPLICIT_GEMM: one GEMM over the
+ * NDHWC gather, rows (n, od, oh, ow), k = ((kd*KH + kh)*KW + kw)*C + c, the
+ * weight rows [O][KD*KH*KW*C] as they are.  SMALL_KD (3D page, Change): for each
  * depth tap kd, the frames x[0, kd:kd+OD] (a pointer offset) and the weight
  * slice w[:, kd] (a strided view) form a 2D conv with batch OD, computed by the
  * plan's inner algorithm and accumulated in fp32 (in y itself for F32, in the

@@ -191,14 +191,17 @@ def test_video3d_bf16(shape):
     t, h, w_, c, o = shape
     case = cw.video3d(t, h, w_, c, o)
     x, w = case.input(), case.weight()
-    y = cn.conv3d(x.cuda(), w.cuda(), **case.conv_kwargs())
     p = cn.plan3d(tuple(x.shape), tuple(w.shape), **case.conv_kwargs(), dtype=x.dtype)
-    assert p.algo_name == "small_kd"
+    assert p.algo_name == "implicit_gemm"  # native 3D GEMM (bf16 frames would not take Winograd)
     per = p.out_h * p.out_w
     frames = sorted(np.random.default_rng(5).choice(p.out_d, 2, replace=False).tolist())
     rows = np.concatenate([f * per + _rows_for(per, 1024, f) for f in frames]).astype(np.int64)
     yr, den = oracle.conv(to_oracle(x), to_oracle(w), **case.conv_kwargs(), rows=rows)
-    check_parity(gather_rows(y, rows), yr, den, x.dtype, case.name)
+    xg, wg = x.cuda(), w.cuda()
+    for algo in ("auto", "small_kd"):
+        y = cn.conv3d(xg, wg, **case.conv_kwargs(), algo=algo)
+        check_parity(gather_rows(y, rows), yr, den, x.dtype, f"{case.name}/{algo}")
+        del y
 
 
 def test_video3d_inner_winograd_variant():

@@ -155,7 +155,7 @@ def test_winograd_half_precision_forced(dtype):
 def test_conv3d_small_kd(kd, inner):
     case = cw.ConvCase(f"c3d_kd{kd}", 1, 9, 10, 32, 48, 3, 3, (1, 1, 1), (0, 1, 1), (1, 1, 1), "bf16",
                        "normal", "normal", None, 5, kd, nd=3, d=kd + 4, kd=kd)
-    err, _ = _run_case(case, "auto", inner_algo=inner) if inner != "auto" else _run_case(case, "auto")
+    err, _ = _run_case(case, "small_kd", inner_algo=inner)
     assert err < 1e-2
 
 
@@ -210,12 +210,13 @@ def test_lds_tile_3d_accumulating_epilogue(dtype):
     case = cw.ConvCase(f"lds3d_{dtype}", 1, 18, 19, 64, 272, 3, 3, (1, 1, 1), (0, 1, 1), (1, 1, 1), dtype,
                        "normal", "normal", None, 23, 5, nd=3, d=6, kd=3)
     x, wt = case.input(), case.weight()
-    plan = cn.plan3d(case.x_shape(), case.w_shape(), **case.conv_kwargs(), dtype=x.dtype, gemm_config=14)
+    plan = cn.plan3d(case.x_shape(), case.w_shape(), **case.conv_kwargs(), dtype=x.dtype, algo="small_kd",
+                     gemm_config=14)
     assert plan.algo_name == "small_kd" and plan.kernel_config == 14
-    y = cn.conv3d(_dev(x), _dev(wt), **case.conv_kwargs(), gemm_config=14)
+    y = cn.conv3d(_dev(x), _dev(wt), **case.conv_kwargs(), algo="small_kd", gemm_config=14)
     yr, den = oracle.conv(to_oracle(x), to_oracle(wt), **case.conv_kwargs())
     check_parity(y.cpu(), yr, den, y.dtype, case.name)
-    y11 = cn.conv3d(_dev(x), _dev(wt), **case.conv_kwargs(), gemm_config=11, split_k=1)
+    y11 = cn.conv3d(_dev(x), _dev(wt), **case.conv_kwargs(), algo="small_kd", gemm_config=11, split_k=1)
     assert torch.equal(bits(y), bits(y11))
 
 
@@ -259,8 +260,57 @@ def test_split_k_3d_accumulating_epilogue(dtype):
     case = cw.ConvCase(f"split3d_{dtype}", 1, 6, 7, 64, 48, 3, 3, (1, 1, 1), (0, 1, 1), (1, 1, 1), dtype,
                        "normal", "normal", None, 37, 3, nd=3, d=5, kd=3)
     x, wt = case.input(), case.weight()
-    plan = cn.plan3d(case.x_shape(), case.w_shape(), **case.conv_kwargs(), dtype=x.dtype, split_k=3)
+    plan = cn.plan3d(case.x_shape(), case.w_shape(), **case.conv_kwargs(), dtype=x.dtype, algo="small_kd",
+                     split_k=3)
     assert plan.algo_name == "small_kd" and plan.split_k == 3
-    y = cn.conv3d(_dev(x), _dev(wt), **case.conv_kwargs(), split_k=3)
+    y = cn.conv3d(_dev(x), _dev(wt), **case.conv_kwargs(), algo="small_kd", split_k=3)
     yr, den = oracle.conv(to_oracle(x), to_oracle(wt), **case.conv_kwargs())
     check_parity(y.cpu(), yr, den, y.dtype, case.name)
+
+
+# ------------------------------------------------- native 3D implicit GEMM
+# One GEMM with K = KD*KH*KW*C over the NDHWC gather: the fall-through for 3D
+# convs the decomposition does not take (batch > 1, depth stride, padding,
+# dilation) and the decomposition with its taps fused.
+
+NATIVE3D_CASES = [  # name, n, d, h, w, c, o, (kd, kh, kw), stride, pad, dil, dtype, gemm_config
+    ("n2_pad_d", 2, 6, 9, 10, 64, 80, (3, 3, 3), (1, 1, 1), (1, 1, 1), (1, 1, 1), "bf16", 0),
+    ("stride_d2", 1, 9, 12, 11, 32, 48, (3, 3, 3), (2, 1, 2), (0, 1, 1), (1, 1, 1), "f16", 0),
+    ("dil2_k5d", 1, 12, 8, 8, 64, 64, (5, 3, 3), (1, 1, 1), (2, 1, 1), (2, 1, 2), "bf16", 0),
+    ("c40_scalar", 2, 5, 7, 9, 40, 24, (2, 3, 3), (1, 2, 1), (1, 0, 1), (1, 1, 1), "f16", 0),
+    ("f32", 2, 5, 8, 7, 32, 40, (3, 3, 3), (1, 1, 1), (1, 1, 1), (1, 1, 1), "f32", 0),
+    ("f32_c6", 1, 6, 7, 8, 6, 10, (3, 2, 3), (1, 1, 1), (0, 1, 0), (1, 1, 1), "f32", 0),
+    ("lds_tile", 1, 7, 20, 22, 64, 288, (3, 3, 3), (1, 1, 1), (1, 1, 1), (1, 1, 1), "bf16", 14),
+    ("lds_tile_s2", 2, 8, 17, 15, 32, 256, (3, 3, 3), (2, 2, 1), (1, 1, 1), (1, 1, 2), "f16", 14),
+    ("cfg11_split", 1, 5, 9, 9, 64, 96, (3, 3, 3), (1, 1, 1), (0, 1, 1), (1, 1, 1), "f16", 11),
+]
+
+
+@pytest.mark.parametrize("spec", NATIVE3D_CASES, ids=[c[0] for c in NATIVE3D_CASES])
+def test_native3d_parity(spec):
+    name, n, d, h, w, c, o, (kd, kh, kw), s, p, dl, dt, cfg = spec
+    case = cw.ConvCase(f"native3d_{name}", n, h, w, c, o, kh, kw, s, p, dl, dt, "normal", "normal", None,
+                       41, len(name) + c, nd=3, d=d, kd=kd)
+    x, wt = case.input(), case.weight()
+    kw_ = dict(gemm_config=cfg or None)
+    splits = (None, 1, 3) if name == "cfg11_split" else (None, 1)
+    yr, den = oracle.conv(to_oracle(x), to_oracle(wt), **case.conv_kwargs())
+    for sk in splits:
+        plan = cn.plan3d(case.x_shape(), case.w_shape(), **case.conv_kwargs(), dtype=x.dtype,
+                         algo="implicit_gemm", split_k=sk, **kw_)
+        assert plan.algo_name == "implicit_gemm"
+        if cfg:
+            assert plan.kernel_config == cfg
+        y = cn.conv3d(_dev(x), _dev(wt), **case.conv_kwargs(), algo="implicit_gemm", split_k=sk, **kw_)
+        check_parity(y.cpu(), yr, den, y.dtype, f"{case.name}/split{plan.split_k}")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_native3d_depth1_bit_identical_to_conv2d(dtype):
+    """D = KD = 1: the native 3D GEMM is the 2D implicit GEMM row for row."""
+    case = cw.ConvCase(f"native3d_d1_{dtype}", 2, 10, 11, 64, 48, 3, 3, (1, 1), (1, 1), (1, 1), dtype,
+                       "normal", "normal", None, 43, 1)
+    x, wt = _dev(case.input()), _dev(case.weight())
+    y2 = cn.conv2d(x, wt, 1, 1, 1, algo="implicit_gemm")
+    y3 = cn.conv3d(x.unsqueeze(1), wt.unsqueeze(1), 1, (0, 1, 1), 1, algo="implicit_gemm")
+    assert torch.equal(bits(y3.squeeze(1)), bits(y2))

@@ -249,12 +249,22 @@ def test_invalid_opts_and_groups():
 X3, W3 = (1, 41, 60, 104, 256), (256, 3, 3, 3, 256)
 
 
-def test_3d_video_shapes_take_small_kd():
+def test_3d_video_shapes_take_the_native_gemm():
+    """bf16 video shapes pass the decomposition guard, but the per-frame 2D conv
+    would not take Winograd, so AUTO runs the native 3D GEMM (all taps in one K
+    loop); the decomposition stays available when forced."""
     for t, h, w, c, o in ((17, 64, 64, 256, 256), (41, 60, 104, 256, 256), (41, 120, 208, 512, 512)):
         p = cn.plan3d((1, t, h, w, c), (o, 3, 3, 3, c), 1, (0, 1, 1), 1, torch.bfloat16)
-        assert p.algo_name == "small_kd" and p.out_d == t - 2
-        assert p.inner_algo_name in ("implicit_gemm", "unfold_gemm")
-        assert p.workspace_bytes >= (t - 2) * h * w * o * 4  # fp32 accumulator
+        assert p.algo_name == "implicit_gemm" and p.out_d == t - 2
+        q = cn.plan3d((1, t, h, w, c), (o, 3, 3, 3, c), 1, (0, 1, 1), 1, torch.bfloat16, algo="small_kd")
+        assert q.algo_name == "small_kd" and q.inner_algo_name in ("implicit_gemm", "unfold_gemm")
+        assert q.workspace_bytes >= (t - 2) * h * w * o * 4  # fp32 accumulator
+
+
+def test_3d_fp32_decomposes_for_winograd():
+    """fp32 frames pass the 2D Winograd gate: AUTO keeps the decomposition."""
+    p = cn.plan3d((1, 9, 64, 64, 128), (128, 3, 3, 3, 128), 1, (0, 1, 1), 1, torch.float32)
+    assert p.algo_name == "small_kd" and p.inner_algo_name == "winograd"
 
 
 @pytest.mark.parametrize("change", ["n2", "kd9", "stride_d", "dil_h", "pad_d", "c_mod16", "o_mod16"])
@@ -275,9 +285,12 @@ def test_3d_guard_each_clause(change):
         xs[-1] = ws[-1] = 250
     elif change == "o_mod16":
         ws[0] = 250
+    # what the guard rejects falls through to the native 3D GEMM
+    assert cn.plan3d(tuple(xs), tuple(ws), s, p, d, torch.bfloat16).algo_name == "implicit_gemm"
+    # a forced inner algorithm needs the decomposition, so it follows the guard
     with pytest.raises(cn.CnhwcError) as e:
-        cn.plan3d(tuple(xs), tuple(ws), s, p, d, torch.bfloat16)
-    assert e.value.name == "UNSUPPORTED"
+        cn.plan3d(tuple(xs), tuple(ws), s, p, d, torch.bfloat16, inner_algo="implicit_gemm")
+    assert e.value.name == "NOT_APPLICABLE"
     structural = change in ("n2", "stride_d", "pad_d")
     if structural:
         with pytest.raises(cn.CnhwcError) as e:
@@ -285,6 +298,17 @@ def test_3d_guard_each_clause(change):
         assert e.value.name == "NOT_APPLICABLE"
     else:  # forcing the decomposition only needs its structural conditions
         assert cn.plan3d(tuple(xs), tuple(ws), s, p, d, torch.bfloat16, algo="small_kd").algo_name == "small_kd"
+
+
+def test_3d_forced_algorithms():
+    assert cn.plan3d(X3, W3, 1, (0, 1, 1), 1, torch.bfloat16, algo="implicit_gemm").algo_name == "implicit_gemm"
+    for algo in ("winograd", "unfold_gemm"):
+        with pytest.raises(cn.CnhwcError) as e:
+            cn.plan3d(X3, W3, 1, (0, 1, 1), 1, torch.bfloat16, algo=algo)
+        assert e.value.name == "NOT_APPLICABLE"
+    with pytest.raises(cn.CnhwcError) as e:
+        cn.plan3d(X3, W3, 1, (0, 1, 1), 1, torch.bfloat16, algo="implicit_gemm", inner_algo="implicit_gemm")
+    assert e.value.name == "INVALID_ARGUMENT"
 
 
 def test_3d_forced_inner_winograd():
@@ -303,7 +327,7 @@ def test_large_half_convs_take_the_256_tile():
     big = cn.plan2d((64, 32, 32, 256), (4096, 3, 3, 256), 1, 1, 1, F16, algo="implicit_gemm")
     assert big.kernel_config == 14
     big3 = cn.plan3d((1, 41, 120, 208, 512), (512, 3, 3, 3, 512), 1, (0, 1, 1), 1, torch.bfloat16)
-    assert big3.algo_name == "small_kd" and big3.kernel_config == 14
+    assert big3.algo_name == "implicit_gemm" and big3.kernel_config == 14
     small = cn.plan2d((1, 56, 56, 64), (64, 3, 3, 64), 1, 1, 1, F16)
     assert small.kernel_config != 14
     odd = cn.plan2d((64, 32, 32, 120), (4096, 3, 3, 120), 1, 1, 1, F16, algo="implicit_gemm")
