@@ -59,7 +59,7 @@ def parse():
                          "with --calib-copy, write profiles/traffic.json, print it and exit")
     ap.add_argument("--suite", default=None,
                     help="instead of the headline line, time other workloads: "
-                         "comma list of small,wide,sweep,resnet,video or 'all' (one JSON line each)")
+                         "comma list of small,wide,sweep,resnet,video,conv1d or 'all' (one JSON line each)")
     return ap.parse_args()
 
 
@@ -311,6 +311,16 @@ def run_suite(names):
                 r = measure(case, inner=None if inner == "auto" else inner)
                 r["suite"] = "video3d"
                 emit(r)
+    if "conv1d" in names:
+        # Whisper-large-shaped encoder convs (128 log-mel bins -> 1280, k3 p1;
+        # 1280 -> 1280, k3 s2 p1) over 3000 frames, through the 2D path (H = 1)
+        for batch in (1, 8):
+            for c, o, s in ((128, 1280, 1), (1280, 1280, 2)):
+                case = cw.ConvCase(f"conv1d_f16_b{batch}_{c}to{o}_k3s{s}", batch, 1, 3000, c, o, 1, 3, (1, s),
+                                   (0, 1), (1, 1), "f16", "normal", "normal", None, 6, c + s)
+                r = measure(case)
+                r["suite"] = "conv1d"
+                emit(r)
 
 
 def main():
@@ -320,7 +330,8 @@ def main():
         print(json.dumps(traffic_from(args.traffic_from[0], args.traffic_from[1], args.calib_copy, key), indent=1))
         return
     if args.suite:
-        names = {"small", "wide", "sweep", "resnet", "video"} if args.suite == "all" else set(args.suite.split(","))
+        names = ({"small", "wide", "sweep", "resnet", "video", "conv1d"} if args.suite == "all"
+                 else set(args.suite.split(",")))
         run_suite(names)
         return
     if args.gpus != 1:

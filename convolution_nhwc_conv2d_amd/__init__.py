@@ -355,6 +355,20 @@ def conv3d(x, w, stride=1, padding=0, dilation=1, *, algo="auto", inner_algo="au
     return _run(fn, x, w, stride, padding, dilation, opts, out, workspace, plan, timer)
 
 
+def conv1d(x, w, stride=1, padding=0, dilation=1, **kw):
+    """y[N,OL,O] = channels-last conv1d of x[N,L,C] with w[O,K,C], routed through
+    the 2D path as an H = KH = 1 conv (MLX PR "Use the explicit gemm for wide
+    convs on neural accelerators", Whisper follow-up: conv1d dispatches to the
+    2D conv).  Keyword options as for conv2d; `out`, if given, is [N,OL,O]."""
+    if x.dim() != 3 or w.dim() != 3:
+        raise ValueError("conv1d: x must be [N,L,C] and w [O,K,C]")
+    one = lambda v: v[0] if isinstance(v, (tuple, list)) else v
+    out = kw.pop("out", None)
+    y = conv2d(x.unsqueeze(1), w.unsqueeze(1), (1, one(stride)), (0, one(padding)), (1, one(dilation)),
+               out=None if out is None else out.unsqueeze(1), **kw)
+    return y.squeeze(1)
+
+
 def direct_flops(x_shape, w_shape, plan):
     """2*N*OD*OH*OW*O*C*KD*KH*KW: the metric's flop count (direct-equivalent)."""
     o = w_shape[0]

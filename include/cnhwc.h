@@ -98,7 +98,9 @@ typedef enum {
 } cnhwc_status_t;
 
 /* Convolution descriptor.  For nd == 2 set d = kd = 1, and index 0 of
- * stride/pad/dil to 1/0/1.  Index order of the triples: depth, height, width. */
+ * stride/pad/dil to 1/0/1.  Index order of the triples: depth, height, width.
+ * conv1d is nd == 2 with h = kh = 1 (x [N,1,L,C], w [O,1,K,C]): the 1D conv
+ * goes through the 2D dispatch (explicit page, Whisper follow-up). */
 typedef struct {
   int32_t nd;        /* 2 or 3 */
   int32_t dtype;     /* cnhwc_dtype_t: element type of x, w and y */

@@ -314,3 +314,29 @@ def test_native3d_depth1_bit_identical_to_conv2d(dtype):
     y2 = cn.conv2d(x, wt, 1, 1, 1, algo="implicit_gemm")
     y3 = cn.conv3d(x.unsqueeze(1), wt.unsqueeze(1), 1, (0, 1, 1), 1, algo="implicit_gemm")
     assert torch.equal(bits(y3.squeeze(1)), bits(y2))
+
+
+# ------------------------------------------------------------------ conv1d
+# conv1d routed through the 2D path (H = KH = 1): Whisper-encoder-shaped convs
+# (log-mel -> d_model, k3 p1; d_model -> d_model, k3 s2 p1, 3000 frames) and
+# odd geometries.
+
+CONV1D_CASES = [  # name, n, l, c, o, k, stride, pad, dil, dtype
+    ("enc_conv1", 1, 3000, 80, 384, 3, 1, 1, 1, "f16"),
+    ("enc_conv2", 1, 3000, 384, 384, 3, 2, 1, 1, "f16"),
+    ("enc_conv2_bf16_b2", 2, 1000, 512, 512, 3, 2, 1, 1, "bf16"),
+    ("f32_k5_d2", 3, 77, 24, 40, 5, 1, 4, 2, "f32"),
+    ("c7_k1", 2, 50, 7, 9, 1, 1, 0, 1, "f16"),
+]
+
+
+@pytest.mark.parametrize("spec", CONV1D_CASES, ids=[c[0] for c in CONV1D_CASES])
+def test_conv1d_parity(spec):
+    name, n, l, c, o, k, s, p, d, dt = spec
+    case = cw.ConvCase(f"conv1d_{name}", n, 1, l, c, o, 1, k, (1, s), (0, p), (1, d), dt,
+                       "normal", "normal", None, 51, len(name) + c)
+    x, wt = case.input(), case.weight()                      # [N,1,L,C], [O,1,K,C]
+    yr, den = oracle.conv(to_oracle(x), to_oracle(wt), **case.conv_kwargs())
+    y = cn.conv1d(_dev(x[:, 0]), _dev(wt[:, 0]), s, p, d)   # [N,OL,O]
+    assert y.shape == (n, yr.shape[2], o)
+    check_parity(y.cpu().unsqueeze(1), yr, den, y.dtype, case.name)

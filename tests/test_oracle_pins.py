@@ -85,6 +85,19 @@ def test_oracle_matches_torch_conv2d_fp64(k, s, d, p):
     assert np.all(np.abs(y - ref) <= 1e-12 * den + 1e-300)
 
 
+@pytest.mark.parametrize("k,s,d,p", [(3, 1, 1, 1), (3, 2, 1, 1), (5, 1, 2, 4), (1, 1, 1, 0)])
+def test_oracle_conv1d_as_h1_matches_torch_conv1d_fp64(k, s, d, p):
+    """conv1d through the 2D definition with H = KH = 1 equals torch's conv1d."""
+    rng = np.random.default_rng([15, k, s, d, p])
+    x = rng.standard_normal((2, 37, 20)).astype(np.float32)
+    wt = rng.standard_normal((12, k, 20)).astype(np.float32)
+    y, den = oracle.conv(x[:, None], wt[:, None], (1, s), (0, p), (1, d))
+    ref = F.conv1d(torch.from_numpy(x).double().permute(0, 2, 1), torch.from_numpy(wt).double().permute(0, 2, 1),
+                   stride=s, padding=p, dilation=d).permute(0, 2, 1).numpy()
+    assert y[:, 0].shape == ref.shape
+    assert np.all(np.abs(y[:, 0] - ref) <= 1e-12 * den[:, 0] + 1e-300)
+
+
 def test_oracle_matches_torch_conv3d_fp64():
     rng = np.random.default_rng(14)
     x = rng.standard_normal((2, 6, 9, 8, 16)).astype(np.float32)
