@@ -42,17 +42,14 @@
 namespace cnhwc {
 namespace {
 
-constexpr int kBM = 256, kBN = 256, kBK = 32;  // tile; K chunk in elements (64 bytes)
+constexpr int kBM = 256, kBK = 32;  // tile rows; K chunk in elements (64 bytes)
 constexpr int kThreads = 256;
 constexpr int kRowBytes = kBK * 2;
 constexpr int kStageBytes = kBM * kRowBytes;  // 16 KB per operand and stage
 constexpr int kLoadsA = kBM * kRowBytes / (kThreads * 16);  // 16-byte loads per thread per chunk
-constexpr int kLoadsB = kBN * kRowBytes / (kThreads * 16);
-constexpr int kLoads = kLoadsA + kLoadsB;
 constexpr int kRowsPerLoad = 64 * 16 / kRowBytes;  // rows one wavefront load instruction fills
 constexpr int kSteps = kBK / 16;  // MFMA K steps per chunk
 constexpr int kPieces = kRowBytes / 16;  // 16-byte pieces per LDS row (4)
-constexpr int kStages = 4;
 
 // Physical 16-byte piece of logical piece c in 64-byte LDS row r: c XOR bits
 // 1..2 of the row, so the 8 lanes served per LDS cycle (8 consecutive rows,
@@ -78,14 +75,42 @@ __device__ __forceinline__ int64_t xcd_tile(int64_t bid, int64_t n) {
   return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + k;
 }
 
-// The stage ring lives in two LDS objects, A rows and B rows: the compiler
-// then tags every fragment read with the object it reads.  The loads into LDS
-// address the ring through a plain integer LDS address (see lds_addr), which
-// carries no such tag, so the compiler adds no wait of its own before a
-// fragment read; the explicit vmcnt waits and barriers below order them.
-constexpr int kRingBytes = kStages * kBM * kRowBytes;  // per operand (kBM == kBN)
-__shared__ __attribute__((aligned(1024))) uint8_t g_ring_a[kRingBytes];
-__shared__ __attribute__((aligned(1024))) uint8_t g_ring_b[kRingBytes];
+// Tile shapes.  4 wavefronts in a 2 x 2 grid; each owns (kBM/2) x (BN/2).
+//  - 256 x 256, 4 stages, one workgroup per CU (128 KB of LDS);
+//  - 256 x 128, 3 stages, two workgroups per CU (72 KB each): the other
+//    workgroup's MFMAs cover one workgroup's waits for its loads.
+template <int BN_, int NS_, int OCC_>
+struct LdsTile {
+  static constexpr int BN = BN_, NS = NS_, OCC = OCC_;
+  static constexpr int WN = BN / 2;        // wavefront tile columns
+  static constexpr int FN = WN / 32;       // 32x32 accumulators per 32-row group
+  static constexpr int LOADS_B = BN * kRowBytes / (kThreads * 16);
+  static constexpr int LOADS = kLoadsA + LOADS_B;  // 16-byte loads per thread per chunk
+  static constexpr int RING_A = NS * kBM * kRowBytes, RING_B = NS * BN * kRowBytes;
+};
+using Tile256 = LdsTile<256, 4, 1>;
+using Tile128 = LdsTile<128, 3, 2>;
+
+// Each tile shape's stage ring lives in two LDS objects, A rows and B rows:
+// the compiler then tags every fragment read with the object it reads.  The
+// loads into LDS address the ring through a plain integer LDS address (see
+// lds_addr), which carries no such tag, so the compiler adds no wait of its
+// own before a fragment read; the explicit vmcnt waits and barriers below
+// order them.
+__shared__ __attribute__((aligned(1024))) uint8_t g_ring_a[Tile256::RING_A];
+__shared__ __attribute__((aligned(1024))) uint8_t g_ring_b[Tile256::RING_B];
+__shared__ __attribute__((aligned(1024))) uint8_t g_ring_a2[Tile128::RING_A];
+__shared__ __attribute__((aligned(1024))) uint8_t g_ring_b2[Tile128::RING_B];
+template <class T>
+__device__ __forceinline__ uint8_t* ring_a_obj() {
+  if constexpr (T::BN == 256) return g_ring_a;
+  else return g_ring_a2;
+}
+template <class T>
+__device__ __forceinline__ uint8_t* ring_b_obj() {
+  if constexpr (T::BN == 256) return g_ring_b;
+  else return g_ring_b2;
+}
 
 typedef void __attribute__((address_space(3)))* lds_ptr;
 __device__ __forceinline__ uint32_t lds_base(const uint8_t* p) {
@@ -114,14 +139,17 @@ __device__ __forceinline__ void block_barrier() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
+template <int FN>
 struct Frag {
   uint4 a[4];
-  uint4 b[4];
+  uint4 b[FN];
 };
 
 // D3: the implicit A operand is a 3D NDHWC gather (depth window as well).
-template <bool BF16, bool IMPLICIT, bool D3 = false>
-__global__ __launch_bounds__(kThreads, 1) void gemm_lds_kernel(const GemmParams p) {
+template <class T, bool BF16, bool IMPLICIT, bool D3 = false>
+__global__ __launch_bounds__(kThreads, T::OCC) void gemm_lds_kernel(const GemmParams p) {
+  constexpr int kBN = T::BN, kStages = T::NS, kLoadsB = T::LOADS_B, kLoads = T::LOADS;
+  constexpr int WN = T::WN, FN = T::FN;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
   const int wm = wave >> 1, wn = wave & 1;
@@ -203,11 +231,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_lds_kernel(const GemmParams 
   int32_t t_c = 0, t_kh = 0, t_kw = 0, t_kd = 0;
   const gvec_ptr zero = gvec(&g_lds_zero16);
 
-  const uint32_t ring_a = lds_base(g_ring_a) + wave * (kLoadsA * 64 * 16);
-  const uint32_t ring_b = lds_base(g_ring_b) + wave * (kLoadsB * 64 * 16);
+  const uint32_t ring_a = lds_base(ring_a_obj<T>()) + wave * (kLoadsA * 64 * 16);
+  const uint32_t ring_b = lds_base(ring_b_obj<T>()) + wave * (kLoadsB * 64 * 16);
   auto issue = [&](int stg) {
     const uint32_t sa = ring_a + stg * kStageBytes;
-    const uint32_t sb = ring_b + stg * kStageBytes;
+    const uint32_t sb = ring_b + stg * (kBN * kRowBytes);
     if constexpr (IMPLICIT) {
       // Branch-free, so the address arithmetic can be interleaved with the
       // MFMAs.  Chunks past the end wrap around to tap 0 and load real data,
@@ -267,42 +295,44 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_lds_kernel(const GemmParams 
   // read of its ring object (and tags it so).
   const int frow = lane & 31;
   const int khalf = lane >> 5;
-  uint32_t ra_off[kSteps][4], rb_off[kSteps][4];
+  uint32_t ra_off[kSteps][4], rb_off[kSteps][FN];
 #pragma unroll
   for (int q = 0; q < kSteps; ++q)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const uint32_t ph = uint32_t(piece(frow, 2 * q + khalf) << 4);
       ra_off[q][i] = uint32_t((wm * 128 + i * 32 + frow) * kRowBytes) + ph;
-      rb_off[q][i] = uint32_t((wn * 128 + i * 32 + frow) * kRowBytes) + ph;
       asm volatile("" : "+v"(ra_off[q][i]));
-      asm volatile("" : "+v"(rb_off[q][i]));
+      if (i < FN) {
+        rb_off[q][i] = uint32_t((wn * WN + i * 32 + frow) * kRowBytes) + ph;
+        asm volatile("" : "+v"(rb_off[q][i]));
+      }
     }
-  auto read = [&](int stg, int q, Frag& f) {
-    const uint32_t sb = uint32_t(stg * kStageBytes);
+  auto read = [&](int stg, int q, Frag<FN>& f) {
+    const uint32_t sa = uint32_t(stg * kStageBytes), sb = uint32_t(stg * kBN * kRowBytes);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) f.a[i] = *reinterpret_cast<const uint4*>(g_ring_a + (ra_off[q][i] + sb));
+    for (int i = 0; i < 4; ++i) f.a[i] = *reinterpret_cast<const uint4*>(ring_a_obj<T>() + (ra_off[q][i] + sa));
 #pragma unroll
-    for (int j = 0; j < 4; ++j) f.b[j] = *reinterpret_cast<const uint4*>(g_ring_b + (rb_off[q][j] + sb));
+    for (int j = 0; j < FN; ++j) f.b[j] = *reinterpret_cast<const uint4*>(ring_b_obj<T>() + (rb_off[q][j] + sb));
   };
 
-  v16f acc[4][4];
+  v16f acc[4][FN];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < FN; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  auto mma = [&](const Frag& f) {
+  auto mma = [&](const Frag<FN>& f) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = mfma_32x32x16<BF16>(f.a[i], f.b[j], acc[i][j]);
+      for (int j = 0; j < FN; ++j) acc[i][j] = mfma_32x32x16<BF16>(f.a[i], f.b[j], acc[i][j]);
   };
 
   const int64_t nk = (K + kBK - 1) / kBK;
-  Frag f0, f1;
+  Frag<FN> f0, f1;
   // Prologue: chunks 0 .. kStages-2 in flight; wait for chunk 0 everywhere.
 #pragma unroll
   for (int i = 0; i < kStages - 1; ++i) issue(i);
@@ -319,13 +349,21 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_lds_kernel(const GemmParams 
   for (int64_t kc = 0; kc < nk; ++kc) {
     const int nxt = cur + 1 == kStages ? 0 : cur + 1;
     const int prv = cur == 0 ? kStages - 1 : cur - 1;
-    // K step 1 reads interleaved with K step 0 MFMAs: two MFMAs, one read
+    // K step 1 reads interleaved with K step 0 MFMAs
     read(cur, 1, f1);
     mma(f0);
+    if constexpr (FN == 4) {
 #pragma unroll
-    for (int g = 0; g < 8; ++g) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // two MFMAs
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+      for (int g = 0; g < 8; ++g) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // two MFMAs
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+      }
+    } else {
+#pragma unroll
+      for (int g = 0; g < 4 + FN; ++g) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
     wait_vmcnt<(kStages - 3) * kLoads>();
@@ -337,15 +375,25 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_lds_kernel(const GemmParams 
     issue(prv);
     read(nxt, 0, f0);
     mma(f1);
+    if constexpr (FN == 4) {
 #pragma unroll
-    for (int g = 0; g < 8; ++g) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 1);  // load into LDS
-      __builtin_amdgcn_sched_group_barrier(0x002, 6, 1);  // VALU
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);  // LDS read
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 1);  // load into LDS
-      __builtin_amdgcn_sched_group_barrier(0x002, 6, 1);  // VALU
+      for (int g = 0; g < 8; ++g) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 1);  // load into LDS
+        __builtin_amdgcn_sched_group_barrier(0x002, 6, 1);  // VALU
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);  // LDS read
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 1);  // load into LDS
+        __builtin_amdgcn_sched_group_barrier(0x002, 6, 1);  // VALU
+      }
+    } else {
+#pragma unroll
+      for (int g = 0; g < kLoads; ++g) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 1);  // load into LDS
+        __builtin_amdgcn_sched_group_barrier(0x002, 8, 1);  // VALU
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);  // LDS read
+      }
     }
     __builtin_amdgcn_sched_barrier(0);
     // The next chunk's step 0 reads were issued 16 MFMAs ago and are done;
@@ -361,27 +409,30 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_lds_kernel(const GemmParams 
   // the wavefront's own LDS area and read back as 8 consecutive columns per
   // lane, 16 lanes per row, so global stores are 16-byte and row-contiguous.
   block_barrier();  // every wavefront has finished its LDS reads
-  constexpr int EP = 128 + 4;    // padded slice row (floats)
-  static_assert(2 * 32 * EP * 4 <= kRingBytes, "two epilogue slices fit one ring");
-  float* ep = reinterpret_cast<float*>((wave < 2 ? g_ring_a : g_ring_b) + (wave & 1) * (kRingBytes / 2));
+  constexpr int EP = WN + 4;     // padded slice row (floats)
+  static_assert(32 * EP * 4 <= T::RING_B / 2, "an epilogue slice fits half a ring");
+  float* ep = reinterpret_cast<float*>(wave < 2 ? ring_a_obj<T>() + (wave & 1) * (T::RING_A / 2)
+                                                : ring_b_obj<T>() + (wave & 1) * (T::RING_B / 2));
   uint16_t* __restrict__ out = reinterpret_cast<uint16_t*>(p.out) + bz * p.stride_out;
   float* __restrict__ accbuf = p.acc ? p.acc + bz * p.stride_out : nullptr;
   const int epi = p.epi;
   const bool vec = (p.ldc % 8) == 0 && (reinterpret_cast<uintptr_t>(out) & 15) == 0 &&
                    (accbuf == nullptr || (reinterpret_cast<uintptr_t>(accbuf) & 15) == 0);
-  const int rl = lane >> 4;        // row within a group of 4
-  const int cl = (lane & 15) * 8;  // first column of this lane's 8
+  constexpr int LPR = WN / 8;      // lanes per slice row (8 columns each)
+  constexpr int RPG = 64 / LPR;    // slice rows per group of 64 lanes
+  const int rl = lane / LPR;       // row within a group
+  const int cl = (lane % LPR) * 8; // first column of this lane's 8
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < FN; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r)
         ep[(8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * EP + 32 * j + (lane & 31)] = acc[i][j][r];
-    for (int g = 0; g < 8; ++g) {
-      const int rr = g * 4 + rl;
+    for (int g = 0; g < 32 / RPG; ++g) {
+      const int rr = g * RPG + rl;
       const int64_t row = m0 + wm * 128 + i * 32 + rr;
-      const int64_t col = n0 + wn * 128 + cl;
+      const int64_t col = n0 + wn * WN + cl;
       const float4 lo = *reinterpret_cast<const float4*>(ep + rr * EP + cl);
       const float4 hi = *reinterpret_cast<const float4*>(ep + rr * EP + cl + 4);
       float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
@@ -429,24 +480,31 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_lds_kernel(const GemmParams 
   }
 }
 
-template <bool BF16>
+template <class T, bool BF16>
 hipError_t launch_lds(const GemmParams& p, hipStream_t s) {
-  const int64_t tiles = ((p.M + kBM - 1) / kBM) * ((p.N + kBN - 1) / kBN) * p.batch;
+  const int64_t tiles = ((p.M + kBM - 1) / kBM) * ((p.N + T::BN - 1) / T::BN) * p.batch;
   const dim3 grid{unsigned(tiles), 1u, 1u};
   if (p.a_mode == kADense)
-    hipLaunchKernelGGL((gemm_lds_kernel<BF16, false>), grid, dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL((gemm_lds_kernel<T, BF16, false>), grid, dim3(kThreads), 0, s, p);
   else if (p.kd > 0)  // native 3D gather
-    hipLaunchKernelGGL((gemm_lds_kernel<BF16, true, true>), grid, dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL((gemm_lds_kernel<T, BF16, true, true>), grid, dim3(kThreads), 0, s, p);
   else
-    hipLaunchKernelGGL((gemm_lds_kernel<BF16, true>), grid, dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL((gemm_lds_kernel<T, BF16, true>), grid, dim3(kThreads), 0, s, p);
   return hipGetLastError();
+}
+
+template <class T>
+hipError_t launch_tile(const GemmParams& p, hipStream_t s) {
+  return p.dtype == CNHWC_BF16 ? launch_lds<T, true>(p, s) : launch_lds<T, false>(p, s);
 }
 
 }  // namespace
 
 bool gemm_lds_ok(const GemmParams& p) {
   if (p.dtype == CNHWC_F32 || p.K <= 0) return false;
-  if (((p.M + kBM - 1) / kBM) * ((p.N + kBN - 1) / kBN) * p.batch >= (int64_t(1) << 31)) return false;
+  if (p.config != kCfgH_256x256 && p.config != kCfgH_256x128L) return false;
+  const int64_t bn = p.config == kCfgH_256x256 ? 256 : 128;
+  if (((p.M + kBM - 1) / kBM) * ((p.N + bn - 1) / bn) * p.batch >= (int64_t(1) << 31)) return false;
   if (p.K % 8 != 0 || p.ldb % 8 != 0) return false;
   if (p.a_mode == kADense) return p.lda % 8 == 0;
   return p.c % kBK == 0;  // a chunk never straddles two taps
@@ -455,7 +513,7 @@ bool gemm_lds_ok(const GemmParams& p) {
 int gemm_lds_launch(const GemmParams& p, void* stream) {
   if (!gemm_lds_ok(p)) return hipErrorInvalidValue;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  return p.dtype == CNHWC_BF16 ? launch_lds<true>(p, s) : launch_lds<false>(p, s);
+  return p.config == kCfgH_256x256 ? launch_tile<Tile256>(p, s) : launch_tile<Tile128>(p, s);
 }
 
 }  // namespace cnhwc

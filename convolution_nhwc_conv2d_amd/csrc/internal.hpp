@@ -38,8 +38,10 @@ enum GemmConfig : int32_t {
   kCfgH_128x128 = 11,
   kCfgH_256x128 = 12,
   kCfgH_128x256 = 13,
-  // 256 x 256, direct global -> LDS operand loads (gemm_lds.hip)
+  // direct global -> LDS operand loads (gemm_lds.hip): 256 x 256 at one
+  // workgroup per CU, 256 x 128 at two
   kCfgH_256x256 = 14,
+  kCfgH_256x128L = 15,
   // Winograd tile-position GEMMs: persistent fp32 kernel with U_p resident in LDS
   kCfgWinoResident = 20,
 };
@@ -106,7 +108,7 @@ constexpr int64_t kMaxSplitK = 16;
 
 // K elements per MFMA chunk of a tile configuration (split-K granularity).
 inline int64_t gemm_config_bk(int32_t config) {
-  return config >= kCfgH_128x64 && config != kCfgH_256x256 ? 64 : 32;
+  return config >= kCfgH_128x64 && config != kCfgH_256x256 && config != kCfgH_256x128L ? 64 : 32;
 }
 
 // fp16/bf16 256 x 256 tile GEMM with direct global -> LDS operand loads.

@@ -93,7 +93,7 @@ void tile_rule(uint64_t ws_limit, uint64_t own, uint64_t scratch, int64_t n, int
 }
 
 // K splits for a GEMM grid too small to fill the device (tiles of gemm.hip
-// only; the 256x256 tile and the Winograd GEMMs never split).  Each split
+// only; the direct-to-LDS tiles and the Winograd GEMMs never split).  Each split
 // gets a whole number of K chunks and at least 4; trailing empty splits are
 // dropped.  Returns 1 for no split.
 int32_t pick_split_k(int32_t cfg, int64_t m, int64_t n, int64_t k) {
@@ -132,7 +132,7 @@ cnhwc_status_t split_k_for(int32_t cfg, int64_t m, int64_t n, int64_t k, int32_t
     return CNHWC_OK;
   }
   const int64_t nk = ceil_div(k, gemm_config_bk(cfg));
-  if (cfg == kCfgH_256x256 || force > nk) return CNHWC_ERR_NOT_APPLICABLE;
+  if (cfg == kCfgH_256x256 || cfg == kCfgH_256x128L || force > nk) return CNHWC_ERR_NOT_APPLICABLE;
   *splits = int32_t(ceil_div(nk, ceil_div(nk, int64_t(force))));
   return CNHWC_OK;
 }
@@ -143,7 +143,7 @@ uint64_t split_k_bytes(int32_t splits, int64_t rows, int64_t o) {
 }
 
 // Tile configuration of the implicit / unfold GEMM: forced, or picked.  The
-// 256x256 direct-to-LDS tile needs C % 32 == 0 (implicit: a K chunk never
+// direct-to-LDS tiles need C % 32 == 0 (implicit: a K chunk never
 // straddles two taps) or K % 8 == 0 (unfold rows).
 cnhwc_status_t gemm_config_for(const cnhwc_conv_desc_t& d, int64_t m_rows, bool implicit,
                                int32_t force, int32_t* cfg) {
@@ -154,9 +154,9 @@ cnhwc_status_t gemm_config_for(const cnhwc_conv_desc_t& d, int64_t m_rows, bool 
     return CNHWC_OK;
   }
   const bool f32 = force >= kCfgF32_N32 && force <= kCfgF32_N128;
-  const bool half = force >= kCfgH_128x64 && force <= kCfgH_256x256;
-  if ((d.dtype == CNHWC_F32 && !f32) || (d.dtype != CNHWC_F32 && !half) ||
-      (force == kCfgH_256x256 && !lds_ok))
+  const bool half = force >= kCfgH_128x64 && force <= kCfgH_256x128L;
+  const bool lds = force == kCfgH_256x256 || force == kCfgH_256x128L;
+  if ((d.dtype == CNHWC_F32 && !f32) || (d.dtype != CNHWC_F32 && !half) || (lds && !lds_ok))
     return CNHWC_ERR_NOT_APPLICABLE;
   *cfg = force;
   return CNHWC_OK;
@@ -351,17 +351,19 @@ int32_t pick_gemm_config(int dtype, int64_t m_rows, int64_t n_cols, bool lds_ok)
   // the tile shape on MI355X (128x128 at two workgroups per CU is the fastest
   // on every large conv of the sweep; the 256-wide tiles need one CU each and
   // lose about 20%; 128x64 is for problems too small to fill the chip).
-  // The 256x256 tile with direct loads into LDS (one workgroup per CU) ran
-  // 1.32-1.47x the 128x128 rate on the large convs of the sweep.
+  // The tiles with direct loads into LDS ran, on the large convs of the
+  // sweep, 1.32-1.47x (256x256, one workgroup per CU) and 1.13-1.40x (256x128,
+  // two per CU) the 128x128 rate; the 256x128 tile wastes less when O is not
+  // a multiple of 256.
   struct Cand { int32_t id; int64_t bm, bn, occ; double eff; };
-  const Cand cands[5] = {{kCfgH_128x128, 128, 128, 2, 1.00}, {kCfgH_128x256, 128, 256, 1, 0.85},
+  const Cand cands[6] = {{kCfgH_128x128, 128, 128, 2, 1.00}, {kCfgH_128x256, 128, 256, 1, 0.85},
                          {kCfgH_256x128, 256, 128, 1, 0.80}, {kCfgH_128x64, 128, 64, 2, 0.70},
-                         {kCfgH_256x256, 256, 256, 1, 1.35}};
+                         {kCfgH_256x256, 256, 256, 1, 1.35}, {kCfgH_256x128L, 256, 128, 2, 1.20}};
   constexpr int64_t kCUs = 256;
   int32_t best = kCfgH_128x128;
   double best_t = 1e300;
   for (const Cand& c : cands) {
-    if (c.id == kCfgH_256x256 && !lds_ok) continue;
+    if ((c.id == kCfgH_256x256 || c.id == kCfgH_256x128L) && !lds_ok) continue;
     const int64_t tiles = ceil_div(m_rows, c.bm) * ceil_div(n_cols, c.bn);
     const int64_t slots = kCUs * c.occ;
     const int64_t waves = ceil_div(tiles, slots);

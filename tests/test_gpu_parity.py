@@ -184,9 +184,10 @@ LDS_CASES = [  # name, n, h, w, c, o, k, stride, pad, dil
 ]
 
 
+@pytest.mark.parametrize("tile", [14, 15])
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("spec", LDS_CASES, ids=[c[0] for c in LDS_CASES])
-def test_lds_tile_parity(dtype, spec):
+def test_lds_tile_parity(dtype, spec, tile):
     name, n, h, w, c, o, k, s, p, d = spec
     case = cw.ConvCase(f"lds_{name}_{dtype}", n, h, w, c, o, k, k, (s, s), (p, p), (d, d), dtype,
                        "normal", "normal", None, 21, len(name) * 7 + c)
@@ -194,13 +195,13 @@ def test_lds_tile_parity(dtype, spec):
     yr, den = oracle.conv(to_oracle(x), to_oracle(wt), **case.conv_kwargs())
     for algo in ("implicit_gemm", "unfold_gemm"):
         plan = cn.plan2d(case.x_shape(), case.w_shape(), **case.conv_kwargs(), dtype=x.dtype, algo=algo,
-                         gemm_config=14)
-        assert plan.kernel_config == 14
-        y = cn.conv2d(_dev(x), _dev(wt), **case.conv_kwargs(), algo=algo, gemm_config=14)
-        check_parity(y.cpu(), yr, den, y.dtype, f"{case.name}/{algo}/256x256")
+                         gemm_config=tile)
+        assert plan.kernel_config == tile
+        y = cn.conv2d(_dev(x), _dev(wt), **case.conv_kwargs(), algo=algo, gemm_config=tile)
+        check_parity(y.cpu(), yr, den, y.dtype, f"{case.name}/{algo}/cfg{tile}")
         # same K order as the 128x128 tile (unsplit): bit-identical results
         y11 = cn.conv2d(_dev(x), _dev(wt), **case.conv_kwargs(), algo=algo, gemm_config=11, split_k=1)
-        assert torch.equal(bits(y), bits(y11)), f"{case.name}/{algo}: 256x256 and 128x128 tiles differ"
+        assert torch.equal(bits(y), bits(y11)), f"{case.name}/{algo}: cfg {tile} and 128x128 tiles differ"
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
@@ -282,6 +283,7 @@ NATIVE3D_CASES = [  # name, n, d, h, w, c, o, (kd, kh, kw), stride, pad, dil, dt
     ("f32_c6", 1, 6, 7, 8, 6, 10, (3, 2, 3), (1, 1, 1), (0, 1, 0), (1, 1, 1), "f32", 0),
     ("lds_tile", 1, 7, 20, 22, 64, 288, (3, 3, 3), (1, 1, 1), (1, 1, 1), (1, 1, 1), "bf16", 14),
     ("lds_tile_s2", 2, 8, 17, 15, 32, 256, (3, 3, 3), (2, 2, 1), (1, 1, 1), (1, 1, 2), "f16", 14),
+    ("lds_tile128", 1, 6, 19, 21, 96, 200, (3, 3, 3), (1, 1, 1), (1, 1, 1), (1, 1, 1), "bf16", 15),
     ("cfg11_split", 1, 5, 9, 9, 64, 96, (3, 3, 3), (1, 1, 1), (0, 1, 1), (1, 1, 1), "f16", 11),
 ]
 
