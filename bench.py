@@ -304,6 +304,32 @@ def run_suite(names):
             tot_fl = sum(v["flops"] for v in stages.values())
             emit({"suite": "resnet50_stack", "batch": batch, "dtype": "f16", "total_ms": tot_ms,
                   "tflops": tot_fl / tot_ms / 1e9, "stages_ms": {k: v["ms"] for k, v in stages.items()}})
+            # the same 53 convs captured once into a HIP graph and replayed: the
+            # GPU time of the stack without the per-call host overhead
+            calls, flops = [], 0.0
+            for case, mult, stage in cw.resnet50_layers(batch):
+                x = case.input().to(dev)
+                w = case.weight().to(dev)
+                plan = cn.plan2d(tuple(x.shape), tuple(w.shape), **case.conv_kwargs(), dtype=x.dtype)
+                ws = torch.empty(max(1, plan.workspace_bytes), dtype=torch.uint8, device=dev)
+                y = cn.conv2d(x, w, **case.conv_kwargs(), plan=plan, workspace=ws)
+                for _ in range(mult):
+                    calls.append((x, w, case, plan, ws, y))
+                    flops += cn.direct_flops(tuple(x.shape), tuple(w.shape), plan)
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.stream(side):
+                for x, w, case, plan, ws, y in calls:
+                    cn.conv2d(x, w, **case.conv_kwargs(), plan=plan, workspace=ws, out=y)
+                torch.cuda.synchronize()
+                with torch.cuda.graph(graph, stream=side):
+                    for x, w, case, plan, ws, y in calls:
+                        cn.conv2d(x, w, **case.conv_kwargs(), plan=plan, workspace=ws, out=y)
+            ms = _time_call(graph.replay)
+            emit({"suite": "resnet50_stack_graph", "batch": batch, "dtype": "f16", "convs": len(calls),
+                  "total_ms": ms, "total_ms_min": _time_call.last_min, "tflops": flops / ms / 1e9})
+            del calls, graph
     if "video" in names:
         for shape in cw.VIDEO3D_SHAPES:
             case = cw.video3d(*shape)

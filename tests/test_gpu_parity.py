@@ -342,3 +342,50 @@ def test_conv1d_parity(spec):
     y = cn.conv1d(_dev(x[:, 0]), _dev(wt[:, 0]), s, p, d)   # [N,OL,O]
     assert y.shape == (n, yr.shape[2], o)
     check_parity(y.cpu().unsqueeze(1), yr, den, y.dtype, case.name)
+
+
+# -------------------------------------------------------------- HIP graphs
+# The forward calls only queue kernels on the caller's stream (no allocation,
+# no synchronisation, no memset), so a caller can capture them into a graph.
+# Each replay must give the eager bits; eager work runs between replays.
+
+def test_graph_capture_replays_bit_identical():
+    cases = [  # (fn, case, kwargs): split-K implicit GEMM, native 3D, Winograd
+        (cn.conv2d, cw.ConvCase("g_l4", 1, 7, 7, 512, 512, 3, 3, (1, 1), (1, 1), (1, 1), "f16",
+                                "normal", "normal", None, 61, 1), {}),
+        (cn.conv3d, cw.ConvCase("g_3d", 2, 8, 9, 64, 48, 3, 3, (1, 1, 1), (1, 1, 1), (1, 1, 1), "bf16",
+                                "normal", "normal", None, 62, 2, nd=3, d=5, kd=3), {}),
+        (cn.conv2d, cw.ConvCase("g_wino", 2, 30, 30, 64, 64, 3, 3, (1, 1), (1, 1), (1, 1), "f32",
+                                "uniform", "normal", None, 63, 3), {"algo": "winograd"}),
+    ]
+    runs = []
+    for fn, case, kw in cases:
+        x, w = _dev(case.input()), _dev(case.weight())
+        mk = cn.plan2d if case.nd == 2 else cn.plan3d
+        plan = mk(tuple(x.shape), tuple(w.shape), **case.conv_kwargs(), dtype=x.dtype, **kw)
+        ws = torch.empty(max(1, plan.workspace_bytes), dtype=torch.uint8, device="cuda")
+        eager = fn(x, w, **case.conv_kwargs(), plan=plan, workspace=ws)
+        out = torch.empty_like(eager)
+        runs.append((fn, case, x, w, plan, ws, eager, out))
+    torch.cuda.synchronize()
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        for fn, case, x, w, plan, ws, eager, out in runs:  # warm up on the capture stream
+            fn(x, w, **case.conv_kwargs(), plan=plan, workspace=ws, out=out)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=stream):
+            for fn, case, x, w, plan, ws, eager, out in runs:
+                fn(x, w, **case.conv_kwargs(), plan=plan, workspace=ws, out=out)
+    for rep in range(3):
+        for *_, out in runs:
+            out.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        for fn, case, x, w, plan, ws, eager, out in runs:
+            assert torch.equal(bits(out), bits(eager)), f"replay {rep}: {case.name} differs from eager"
+        # eager work between replays, on the same buffers
+        fn, case, x, w, plan, ws, eager, out = runs[0]
+        fn(x, w, **case.conv_kwargs(), plan=plan, workspace=ws, out=out)
+        torch.cuda.synchronize()
