@@ -156,7 +156,8 @@ __global__ __launch_bounds__(kResThreads) void wino_gemm_resident_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int rr = (r >> 2) * 8 + (r & 3);
-        if (32 * j + i < O && (full || blk * 32 + h * 4 + rr < rows)) cp[rr * O + 32 * j] = acc[j][r];
+        if (32 * j + i < O && (full || blk * 32 + h * 4 + rr < rows))
+          __builtin_nontemporal_store(acc[j][r], &cp[rr * O + 32 * j]);  // streamed: read once, later
       }
   };
 

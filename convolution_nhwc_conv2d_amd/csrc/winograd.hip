@@ -175,13 +175,14 @@ __global__ __launch_bounds__(256) void wino_output_kernel(const float* __restric
           const int64_t idx = ((n * OH + oh) * OW + ow) * O + o;
           const float v = res[j];
           if (epi == kEpiStore) {
-            y[idx] = from_f32<E, BF16>(v);
+            // y is written once and not read here again: stream it past the caches
+            __builtin_nontemporal_store(from_f32<E, BF16>(v), &y[idx]);
           } else if (epi == kEpiAccFirst) {
             acc[idx] = v;
           } else if (epi == kEpiAccMid) {
             acc[idx] = acc[idx] + v;
           } else {
-            y[idx] = from_f32<E, BF16>(acc[idx] + v);
+            __builtin_nontemporal_store(from_f32<E, BF16>(acc[idx] + v), &y[idx]);
           }
         }
       }
