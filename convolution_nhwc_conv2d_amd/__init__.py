@@ -32,7 +32,8 @@ LIB_PATH = os.path.join(_HERE, "libcnhwc.so")
 F32, F16, BF16 = 0, 1, 2
 _DTYPE_CODE = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}
 
-ALGOS = {"auto": 0, "winograd": 1, "implicit_gemm": 2, "unfold_gemm": 3, "small_kd": 4}
+ALGOS = {"auto": 0, "winograd": 1, "implicit_gemm": 2, "unfold_gemm": 3, "small_kd": 4,
+         "winograd_half": 5}
 ALGO_NAMES = {v: k for k, v in ALGOS.items()}
 
 STATUS = {0: "OK", 1: "INVALID_ARGUMENT", 2: "UNSUPPORTED", 3: "NOT_APPLICABLE", 4: "BUDGET",
@@ -118,7 +119,7 @@ def _load():
                        ctypes.c_int32, P(ctypes.c_int32)]
     lib.cnhwc_launch_count.restype = ctypes.c_int64
     lib.cnhwc_launch_count.argtypes = [P(Desc), P(Plan)]
-    if lib.cnhwc_abi_version() != 2:
+    if lib.cnhwc_abi_version() != 3:
         raise ImportError("libcnhwc.so ABI version mismatch")
     return lib
 
@@ -130,7 +131,8 @@ EXPORTED = ("cnhwc_abi_version", "cnhwc_status_string", "cnhwc_conv_select",
             "cnhwc_launch_count", "cnhwc_conv2d_fwd_timed", "cnhwc_conv3d_fwd_timed")
 
 KERNEL_KINDS = {0: "end", 1: "wino_filter", 2: "wino_input", 3: "wino_gemm", 4: "wino_output",
-                5: "implicit_gemm", 6: "unfold", 7: "unfold_gemm", 8: "splitk_reduce"}
+                5: "implicit_gemm", 6: "unfold", 7: "unfold_gemm", 8: "splitk_reduce",
+                9: "wino_scale"}
 
 
 # ------------------------------------------------------------------ helpers

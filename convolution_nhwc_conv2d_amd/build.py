@@ -14,7 +14,7 @@ ROOT = os.path.dirname(PKG)
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libcnhwc.so")
 OBJDIR = os.path.join(PKG, "_build")
-SOURCES = ["select.cpp", "api.cpp", "gemm.hip", "gemm_lds.hip", "wino_gemm.hip", "winograd.hip", "unfold.hip"]
+SOURCES = ["select.cpp", "api.cpp", "gemm.hip", "gemm_lds.hip", "wino_gemm.hip", "winograd.hip", "winograd_h.hip", "unfold.hip"]
 ARCH = "gfx950"
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,

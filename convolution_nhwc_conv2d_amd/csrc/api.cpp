@@ -9,7 +9,8 @@
 // accelerators", Notes): per row chunk, unfold into the one buffer, then GEMM.
 // 3D (MLX PR "Decompose small kernel-depth 3D convs into 2D convs", Change):
 // per depth tap, a 2D conv on the frame view and the weight depth slice,
-// accumulated in fp32.
+// accumulated in fp32; or the native implicit GEMM; or the half-precision
+// Winograd path with the depth taps summed inside its GEMMs.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -49,7 +50,75 @@ int64_t launches_2d(const cnhwc_plan_t& p, int32_t algo) {
   if (algo == CNHWC_ALGO_IMPLICIT_GEMM) return 1 + reduce;
   if (algo == CNHWC_ALGO_UNFOLD_GEMM) return (2 + reduce) * p.n_chunks;
   if (algo == CNHWC_ALGO_WINOGRAD) return 1 + 3 * p.n_tiles;
+  if (algo == CNHWC_ALGO_WINOGRAD_HALF) return 3 + 3 * p.n_tiles;
   return -1;
+}
+
+// Half-precision Winograd F(4x4,3x3) (2D, or 3D with the depth taps summed in
+// the GEMMs): the max-|element| pass and the scales, the filter transform,
+// then per batch tile the input transform, the 36 tile-position GEMMs (fp16
+// operands, fp32 results) and the output transform.
+cnhwc_status_t run_wino_h(const cnhwc_conv_desc_t& d, const cnhwc_plan_t& p, const void* x,
+                          const void* w, void* y, char* ws, void* stream, Recorder& rec) {
+  const WinoHLayout L = wino_h_layout(d, p.out_d, p.out_h, p.out_w, p.tile_batch);
+  uint32_t* partial = reinterpret_cast<uint32_t*>(ws);
+  float* scales = reinterpret_cast<float*>(ws + kWinoHScaleOff);
+  uint16_t* U = reinterpret_cast<uint16_t*>(ws + L.off_u);
+  uint16_t* V = reinterpret_cast<uint16_t*>(ws + L.off_v);
+  float* Mt = reinterpret_cast<float*>(ws + L.off_m);
+  const int64_t nx = d.n * d.d * d.h * d.w * d.c;
+  const int64_t nw = d.o * d.kd * d.kh * d.kw * d.c;
+  rec.mark(CNHWC_KERNEL_WINO_SCALE);
+  if (wino_h_absmax_launch(d.dtype, x, nx, w, nw, partial, stream) != hipSuccess) return CNHWC_ERR_HIP;
+  rec.mark(CNHWC_KERNEL_WINO_SCALE);
+  if (wino_h_scale_launch(d.dtype, partial, nx, nw, scales, stream) != hipSuccess) return CNHWC_ERR_HIP;
+  rec.mark(CNHWC_KERNEL_WINO_FILTER);
+  if (wino_h_filter_launch(d.dtype, w, d.o, d.kd, d.c, L.cs, scales, U, stream) != hipSuccess)
+    return CNHWC_ERR_HIP;
+
+  GemmParams q;
+  std::memset(&q, 0, sizeof(q));
+  q.dtype = CNHWC_F16;  // the transformed operands are fp16 for either input dtype
+  q.a_mode = kADense;
+  q.epi = kEpiAccFirst;  // fp32 results
+  q.config = p.kernel_config;
+  q.N = d.o;
+  q.K = L.ku;
+  q.lda = L.cs;
+  q.b = U;
+  q.ldb = L.ku;
+  q.out = Mt;  // not written with kEpiAccFirst
+  q.acc = Mt;
+  q.ldc = d.o;
+  q.batch = kWinoHP;
+  q.stride_a = int64_t(L.v_plane);
+  q.stride_b = d.o * L.ku;
+  q.stride_out = int64_t(L.m_plane);
+  if (d.kd > 1) {
+    // tap kd reads the transformed rows kd * dd frames further on
+    q.a_seg_len = L.cs;
+    q.a_seg_jump = (int64_t(d.dil[0]) * L.t - 1) * L.cs;
+  }
+  const uint64_t x_elem = uint64_t(d.d) * d.h * d.w * d.c * 2;              // bytes per element
+  const uint64_t y_elem = uint64_t(p.out_d) * p.out_h * p.out_w * d.o * 2;  // bytes per element
+  for (int64_t n0 = 0; n0 < d.n; n0 += p.tile_batch) {
+    const int64_t nb = n0 + p.tile_batch <= d.n ? p.tile_batch : d.n - n0;
+    rec.mark(CNHWC_KERNEL_WINO_INPUT);
+    if (wino_h_input_launch(d.dtype, static_cast<const char*>(x) + n0 * x_elem, nb, d.d, L.dp,
+                            d.pad[0], d.h, d.w, d.c, L.cs, d.pad[1], d.pad[2], L.tiles_h,
+                            L.tiles_w, scales, V, int64_t(L.v_plane), stream) != hipSuccess)
+      return CNHWC_ERR_HIP;
+    rec.mark(CNHWC_KERNEL_WINO_GEMM);
+    q.M = nb * p.out_d * L.t;
+    q.a = V;
+    if (gemm_launch(q, stream) != hipSuccess) return CNHWC_ERR_HIP;
+    rec.mark(CNHWC_KERNEL_WINO_OUTPUT);
+    if (wino_h_output_launch(d.dtype, Mt, int64_t(L.m_plane), nb * p.out_d, p.out_h, p.out_w, d.o,
+                             L.tiles_h, L.tiles_w, scales, static_cast<char*>(y) + n0 * y_elem,
+                             stream) != hipSuccess)
+      return CNHWC_ERR_HIP;
+  }
+  return CNHWC_OK;
 }
 
 // One 2D conv (a full 2D call or one depth tap of a 3D call).
@@ -223,6 +292,7 @@ cnhwc_status_t validate(const cnhwc_conv_desc_t* desc, const cnhwc_plan_t* plan,
 // Kernels a whole forward call launches (3D: all taps).
 int64_t plan_launch_count(const cnhwc_conv_desc_t& d, const cnhwc_plan_t& p) {
   if (d.nd == 3 && p.algo == CNHWC_ALGO_IMPLICIT_GEMM) return p.split_k > 1 ? 2 : 1;
+  if (p.algo == CNHWC_ALGO_WINOGRAD_HALF) return launches_2d(p, p.algo);
   if (p.algo == CNHWC_ALGO_SMALL_KD) {
     const int64_t per = launches_2d(p, p.inner_algo);
     return per < 0 ? -1 : per * d.kd;
@@ -238,8 +308,11 @@ cnhwc_status_t fwd2d(const cnhwc_conv_desc_t* desc, const cnhwc_plan_t* plan, co
   if (st != CNHWC_OK) return st;
   if (rec.events && plan_launch_count(*desc, *plan) + 1 > rec.n) return CNHWC_ERR_INVALID_ARGUMENT;
   rec.n = 0;
-  const cnhwc_status_t s = run_2d(*desc, *plan, plan->algo, x, w, desc->kh * desc->kw * desc->c, y,
-                                  nullptr, kEpiStore, static_cast<char*>(workspace), stream, rec);
+  const cnhwc_status_t s =
+      plan->algo == CNHWC_ALGO_WINOGRAD_HALF
+          ? run_wino_h(*desc, *plan, x, w, y, static_cast<char*>(workspace), stream, rec)
+          : run_2d(*desc, *plan, plan->algo, x, w, desc->kh * desc->kw * desc->c, y, nullptr,
+                   kEpiStore, static_cast<char*>(workspace), stream, rec);
   if (s == CNHWC_OK) rec.mark(CNHWC_KERNEL_END);
   return s;
 }
@@ -249,11 +322,17 @@ cnhwc_status_t fwd3d(const cnhwc_conv_desc_t* desc, const cnhwc_plan_t* plan, co
                      void* stream, Recorder& rec) {
   const cnhwc_status_t st = validate(desc, plan, 3, x, w, y, workspace, workspace_bytes);
   if (st != CNHWC_OK) return st;
-  if (plan->algo != CNHWC_ALGO_SMALL_KD && plan->algo != CNHWC_ALGO_IMPLICIT_GEMM)
+  if (plan->algo != CNHWC_ALGO_SMALL_KD && plan->algo != CNHWC_ALGO_IMPLICIT_GEMM &&
+      plan->algo != CNHWC_ALGO_WINOGRAD_HALF)
     return CNHWC_ERR_INTERNAL;
   if (rec.events && plan_launch_count(*desc, *plan) + 1 > rec.n) return CNHWC_ERR_INVALID_ARGUMENT;
   rec.n = 0;
   const cnhwc_conv_desc_t& d = *desc;
+  if (plan->algo == CNHWC_ALGO_WINOGRAD_HALF) {
+    const cnhwc_status_t s = run_wino_h(d, *plan, x, w, y, static_cast<char*>(workspace), stream, rec);
+    if (s == CNHWC_OK) rec.mark(CNHWC_KERNEL_END);
+    return s;
+  }
   if (plan->algo == CNHWC_ALGO_IMPLICIT_GEMM) {
     // native 3D implicit GEMM: rows (n, od, oh, ow), k = ((kd*KH + kh)*KW + kw)*C + c
     GemmParams g;

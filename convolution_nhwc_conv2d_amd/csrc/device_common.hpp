@@ -1,5 +1,7 @@
 // Device helpers shared by the gfx950 kernels: vector types, the matrix-core
-// builtins, and conversions between fp32 and the 16-bit storage types.
+// builtins, conversions between fp32 and the 16-bit storage types, the
+// constant-matrix product of the Winograd transforms and the XCD-contiguous
+// workgroup order.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <cstdint>
@@ -54,6 +56,38 @@ __device__ __forceinline__ float to_f32(E v) {
   } else {
     return static_cast<float>(__builtin_bit_cast(_Float16, v));
   }
+}
+
+// out[i] = sum_k Mat[i][k] * in[k] (k ascending), zero coefficients skipped.
+template <int R, int C>
+__device__ __forceinline__ void cmatvec(const float (&mat)[R][C], const float (&in)[C], float (&out)[R]) {
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    float s = 0.0f;
+    bool first = true;
+#pragma unroll
+    for (int k = 0; k < C; ++k) {
+      const float m = mat[i][k];
+      if (m != 0.0f) {
+        const float t = (m == 1.0f) ? in[k] : (m == -1.0f) ? -in[k] : m * in[k];
+        s = first ? t : s + t;
+        first = false;
+      }
+    }
+    out[i] = s;
+  }
+}
+
+// Workgroups are dispatched round-robin over the 8 XCDs (each with its own L2).
+// Remap so that XCD x runs one contiguous range of logical workgroups:
+// neighbouring Winograd tiles, whose input windows overlap by two pixels, then
+// share an L2.  A bijection on [0, gridDim.x) for round-robin dispatch.
+__device__ __forceinline__ int64_t xcd_block(int64_t bid, int64_t nwg) {
+  constexpr int64_t kXcd = 8;
+  const int64_t x = bid % kXcd, k = bid / kXcd;
+  const int64_t q = nwg / kXcd, r = nwg % kXcd;
+  const int64_t start = x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q;
+  return start + k;
 }
 
 }  // namespace cnhwc

@@ -508,6 +508,10 @@ int gemm_launch(const GemmParams& p, void* stream) {
                        p.kchunk <= 0 || p.kchunk % gemm_config_bk(p.config) != 0 ||
                        (p.ksplit - 1) * p.kchunk >= p.K))
     return hipErrorInvalidValue;
+  // segmented dense A: the 256-row tiles only
+  if ((p.a_seg_len != 0 || p.a_seg_jump != 0) && p.config != kCfgH_256x256 &&
+      p.config != kCfgH_256x128L)
+    return hipErrorInvalidValue;
   switch (p.config) {
     case kCfgF32_N32: return launch_cfg<TileCfg<128, 32, 32, 32, false, 2>, false>(p, s);
     case kCfgF32_N64: return launch_cfg<TileCfg<128, 64, 32, 64, false, 1>, false>(p, s);

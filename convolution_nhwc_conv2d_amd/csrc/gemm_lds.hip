@@ -229,6 +229,9 @@ __global__ __launch_bounds__(kThreads, T::OCC) void gemm_lds_kernel(const GemmPa
   // fixed.
   int64_t k_next = 0;
   int32_t t_c = 0, t_kh = 0, t_kw = 0, t_kd = 0;
+  // segmented dense A: K position within the segment, and the row shift of
+  // the segments passed so far (a_seg_len == 0 never wraps)
+  int64_t seg_k = 0, seg_off = 0;
   const gvec_ptr zero = gvec(&g_lds_zero16);
 
   const uint32_t ring_a = lds_base(ring_a_obj<T>()) + wave * (kLoadsA * 64 * 16);
@@ -275,7 +278,7 @@ __global__ __launch_bounds__(kThreads, T::OCC) void gemm_lds_kernel(const GemmPa
       const bool k_in = k_next + kin < K;
 #pragma unroll
       for (int j = 0; j < kLoadsA; ++j) {
-        const gvec_ptr src = (a_off[j] >= 0 && k_in) ? gvec(A + a_off[j] + k_next) : zero;
+        const gvec_ptr src = (a_off[j] >= 0 && k_in) ? gvec(A + a_off[j] + k_next + seg_off) : zero;
         __builtin_amdgcn_global_load_lds(src, lds_addr(sa + j * (64 * 16)), 16, 0, 0);
       }
 #pragma unroll
@@ -283,6 +286,10 @@ __global__ __launch_bounds__(kThreads, T::OCC) void gemm_lds_kernel(const GemmPa
         const gvec_ptr src = (b_off[j] >= 0 && k_in) ? gvec(B + b_off[j] + k_next) : zero;
         __builtin_amdgcn_global_load_lds(src, lds_addr(sb + j * (64 * 16)), 16, 0, 0);
       }
+      seg_k += kBK;
+      const bool sw = seg_k == p.a_seg_len;
+      seg_k = sw ? 0 : seg_k;
+      seg_off += sw ? p.a_seg_jump : 0;
     }
     k_next += kBK;
   };
@@ -506,7 +513,9 @@ bool gemm_lds_ok(const GemmParams& p) {
   const int64_t bn = p.config == kCfgH_256x256 ? 256 : 128;
   if (((p.M + kBM - 1) / kBM) * ((p.N + bn - 1) / bn) * p.batch >= (int64_t(1) << 31)) return false;
   if (p.K % 8 != 0 || p.ldb % 8 != 0) return false;
-  if (p.a_mode == kADense) return p.lda % 8 == 0;
+  if (p.a_seg_len < 0 || p.a_seg_len % kBK != 0) return false;  // a chunk never straddles segments
+  if (p.a_mode == kADense) return p.lda % 8 == 0 && p.a_seg_jump % 8 == 0;
+  if (p.a_seg_len != 0) return false;
   return p.c % kBK == 0;  // a chunk never straddles two taps
 }
 

@@ -21,6 +21,24 @@ constexpr int kWinoP = 64;
 // multiple of 8 so every row is 32-byte aligned (pad channels are zero).
 inline int64_t wino_cs(int64_t c) { return (c + 7) / 8 * 8; }
 
+// Winograd F(4x4,3x3) for fp16/bf16 (winograd_h.hip): 6x6 input tiles at
+// stride 4, 36 tile positions, fp16 transformed operands with power-of-two
+// scales, fp32 GEMM results.
+constexpr int kWinoHM = 4;
+constexpr int kWinoHP = 36;
+// Channel stride of its fp16 rows: C rounded up to 32, one K chunk of the
+// 256-row GEMM tiles, so a 3D tap's K range starts on a chunk.
+inline int64_t wino_h_cs(int64_t c) { return (c + 31) / 32 * 32; }
+// Partial maxima per tensor (one per block of the max-|element| pass).
+constexpr int32_t kWinoHSlots = 1024;
+inline int32_t wino_h_absmax_blocks(int64_t n) {
+  const int64_t b = (n / 8 + 1023) / 1024;  // about four 16-byte vectors per thread
+  return int32_t(b < 1 ? 1 : (b > kWinoHSlots ? kWinoHSlots : b));
+}
+// Workspace head: the partial maxima of x and w, then 4 floats of scales.
+constexpr uint64_t kWinoHScaleOff = 2ull * kWinoHSlots * 4;
+constexpr uint64_t kWinoHHeadBytes = (kWinoHScaleOff + 16 + 255) / 256 * 256;
+
 // ------------------------------------------------------------------ GEMM
 
 // GEMM tile configurations.  Each id fixes the tile shape, the MFMA form and
@@ -96,6 +114,11 @@ struct GemmParams {
   int32_t ksplit;        // 0 or 1: no split
   int64_t kchunk;        // multiple of the configuration's K chunk
   float* part;
+  // segmented dense A (256-row tiles only; a_seg_len = 0: none): element
+  // (m, k) sits at a[m*lda + k + (k / a_seg_len) * a_seg_jump].  The Winograd
+  // depth taps: segment kd reads the rows kd * dd frames further on.
+  int64_t a_seg_len;     // multiple of the 32-element K chunk
+  int64_t a_seg_jump;
 };
 
 int gemm_launch(const GemmParams& p, void* stream);  // returns hipError_t
@@ -140,6 +163,29 @@ int wino_output_launch(int dtype, const float* m, int64_t plane, int64_t nb, int
                        int64_t ow, int64_t o, int64_t tiles_h, int64_t tiles_w, void* y,
                        float* acc, int32_t epi, void* stream);
 
+// Half-precision Winograd F(4x4,3x3) (fp16/bf16 x and w).
+// partial[t][b] = largest |element| bits of block b of tensor t (0: x of nx
+// elements, 1: w of nw), then scales = {sx, sw, 1/sx, 1/sw} (after the
+// partial maxima in the workspace head).
+int wino_h_absmax_launch(int dtype, const void* x, int64_t nx, const void* w, int64_t nw,
+                         uint32_t* partial, void* stream);
+int wino_h_scale_launch(int dtype, const uint32_t* partial, int64_t nx, int64_t nw, float* scales,
+                        void* stream);
+// U[p][o][kd*cs + c] = fp16(sw (G g G^T)_p), g = w[o][kd][kh][kw][c] (KD = kd planes).
+int wino_h_filter_launch(int dtype, const void* w, int64_t o, int64_t kd, int64_t c, int64_t cs,
+                         const float* scales, uint16_t* u, void* stream);
+// V[p][r][c] = fp16(sx (B^T d B)_p) over nb elements of dp frames each (frame
+// f reads input frame f - pd, zero outside [0, d)); plane stride `plane`.
+int wino_h_input_launch(int dtype, const void* x, int64_t nb, int64_t d, int64_t dp, int32_t pd,
+                        int64_t h, int64_t w, int64_t c, int64_t cs, int32_t ph, int32_t pw,
+                        int64_t th, int64_t tw, const float* scales, uint16_t* v, int64_t plane,
+                        void* stream);
+// y = ((A^T M A) / sx) / sw per tile and output channel for nimg output images
+// (or frames), cropped to [oh, ow].
+int wino_h_output_launch(int dtype, const float* m, int64_t plane, int64_t nimg, int64_t oh,
+                         int64_t ow, int64_t o, int64_t th, int64_t tw, const float* scales,
+                         void* y, void* stream);
+
 // ------------------------------------------------------------- Unfold
 
 // buf[r][k] for output rows m0..m0+rows-1 (k = (kh*KW + kw)*C + c, zero outside
@@ -164,6 +210,17 @@ struct WinoLayout {
   uint64_t off_u, off_v, off_m, total;
 };
 WinoLayout wino_layout(const cnhwc_conv_desc_t& d2, int64_t oh, int64_t ow, int64_t tile_batch);
+
+// Half-precision Winograd workspace layout (2D: od = 1, depth pad 0; 3D: one
+// batch element per tile).  Frames per element dp = D + 2 pd; the GEMM K is
+// ku = KD * cs.
+struct WinoHLayout {
+  int64_t tiles_h, tiles_w, t, cs, dp, ku;
+  uint64_t u_bytes, v_plane, m_plane;  // plane strides in elements
+  uint64_t off_u, off_v, off_m, total;
+};
+WinoHLayout wino_h_layout(const cnhwc_conv_desc_t& d, int64_t od, int64_t oh, int64_t ow,
+                          int64_t tile_batch);
 
 cnhwc_status_t select_impl(const cnhwc_conv_desc_t* desc, const cnhwc_select_opts_t* opts,
                            cnhwc_plan_t* plan);

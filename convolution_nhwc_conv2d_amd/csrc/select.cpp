@@ -80,6 +80,46 @@ bool winograd_auto_gate(const cnhwc_conv_desc_t& d) {
          d.dtype == CNHWC_F32;
 }
 
+// Half-precision Winograd F(4x4,3x3): 3x3 taps in the image plane, stride 1 and
+// dilation 1 there, fp16/bf16 only (3D: depth stride 1; any depth, depth pad
+// and depth dilation).  Accuracy limits: the fp16 rounding of a tile's
+// transformed values scales with the whole 6x6 tile, so an output whose 3x3
+// window is mostly padding (image-plane padding of 2 or more: a corner window
+// holds one real pixel of nine) can see errors of 1-3e-2 of its own
+// sum |x||w|; and the rounding errors of fewer than 16 channels do not average
+// down (8 channels with padding 1: up to 9e-3).  Padding <= 1 in the image
+// plane and C >= 16 keep the measured error below 5e-3.
+bool winograd_h_geometry(const cnhwc_conv_desc_t& d) {
+  return d.dtype != CNHWC_F32 && d.kh == 3 && d.kw == 3 && d.stride[1] == 1 &&
+         d.stride[2] == 1 && d.dil[1] == 1 && d.dil[2] == 1 && d.stride[0] == 1 &&
+         d.pad[1] <= 1 && d.pad[2] <= 1 && d.c >= 16;
+}
+
+// AUTO's rule for the half-precision Winograd path.  Not taken yet: it is
+// forceable and parity-tested while its crossover against the implicit GEMM
+// is measured.
+bool winograd_h_auto_gate(const cnhwc_conv_desc_t& d) {
+  (void)d;
+  return false;
+}
+
+// The 256-row GEMM tile for the half-precision Winograd GEMMs (rows x n, batch
+// tile positions): the occupancy model of pick_gemm_config over the two
+// direct-to-LDS tiles.
+int32_t pick_lds_tile(int64_t rows, int64_t n, int64_t batch) {
+  struct Cand { int32_t id; int64_t bn, occ; double eff; };
+  const Cand cands[2] = {{kCfgH_256x256, 256, 1, 1.35}, {kCfgH_256x128L, 128, 2, 1.20}};
+  constexpr int64_t kCUs = 256;
+  int32_t best = kCfgH_256x256;
+  double best_t = 1e300;
+  for (const Cand& c : cands) {
+    const int64_t tiles = ceil_div(rows, 256) * ceil_div(n, c.bn) * batch;
+    const double t = double(ceil_div(tiles, kCUs * c.occ)) * double(256 * c.bn * c.occ) / c.eff;
+    if (t < best_t) { best_t = t; best = c.id; }
+  }
+  return best;
+}
+
 void tile_rule(uint64_t ws_limit, uint64_t own, uint64_t scratch, int64_t n, int64_t rows,
                int64_t force_tile, int64_t* tile, uint64_t* budget, int32_t* fallback) {
   const uint64_t q = three_quarters(ws_limit);
@@ -162,6 +202,46 @@ cnhwc_status_t gemm_config_for(const cnhwc_conv_desc_t& d, int64_t m_rows, bool 
   return CNHWC_OK;
 }
 
+// Plan of the half-precision Winograd path (2D, or 3D with one batch element
+// per tile), forced or under AUTO.  Returns OK with the plan, BUDGET when no
+// batch element fits the budget (AUTO then falls back), NOT_APPLICABLE for a
+// forced GEMM tile other than the two 256-row tiles.
+cnhwc_status_t plan_winograd_h(const cnhwc_conv_desc_t& d, const int64_t out[3],
+                               const cnhwc_select_opts_t& o, bool forced, cnhwc_plan_t* p) {
+  const uint64_t es = dtype_size(d.dtype);
+  const WinoHLayout one = wino_h_layout(d, out[0], out[1], out[2], 1);
+  const uint64_t own = uint64_t(d.n) * d.d * d.h * d.w * d.c * es +
+                       uint64_t(d.n) * out[0] * out[1] * out[2] * d.o * es + kWinoHHeadBytes +
+                       align_up(one.u_bytes, 256);
+  const uint64_t scratch = uint64_t(kWinoHP) * one.t * (one.dp * one.cs * 2 + out[0] * d.o * 4);
+  int64_t tb;
+  uint64_t budget;
+  int32_t fb;
+  // 3D: one element per tile (a GEMM's rows shift by whole frames within one element)
+  const int64_t force_tile = d.nd == 3 ? 1 : o.force_tile_batch;
+  tile_rule(o.ws_limit_bytes, own, scratch, d.n, one.t * out[0], force_tile, &tb, &budget, &fb);
+  if (tb < 1 || (!forced && fb)) return CNHWC_ERR_BUDGET;
+  int32_t cfg = o.force_gemm_config;
+  if (cfg != 0 && cfg != kCfgH_256x256 && cfg != kCfgH_256x128L) return CNHWC_ERR_NOT_APPLICABLE;
+  // the GEMM tile depends on the untiled shape only
+  if (cfg == 0) cfg = pick_lds_tile((d.nd == 3 ? 1 : d.n) * out[0] * one.t, d.o, kWinoHP);
+  const WinoHLayout lay = wino_h_layout(d, out[0], out[1], out[2], tb);
+  p->algo = p->inner_algo = CNHWC_ALGO_WINOGRAD_HALF;
+  p->out_d = out[0];
+  p->out_h = out[1];
+  p->out_w = out[2];
+  p->tile_batch = tb;
+  p->n_tiles = ceil_div(d.n, tb);
+  p->tiles_per_image = lay.t;
+  p->own_bytes = own;
+  p->budget_bytes = budget;
+  p->scratch_per_element = scratch;
+  p->workspace_bytes = lay.total;
+  p->kernel_config = cfg;
+  p->split_k = 1;
+  return CNHWC_OK;
+}
+
 cnhwc_status_t select_2d(const cnhwc_conv_desc_t& d, const int64_t out[3],
                          const cnhwc_select_opts_t& o, int32_t force, cnhwc_plan_t* p) {
   const uint64_t es = dtype_size(d.dtype);
@@ -174,7 +254,8 @@ cnhwc_status_t select_2d(const cnhwc_conv_desc_t& d, const int64_t out[3],
   cnhwc_status_t st = CNHWC_OK;
 
   if (force != CNHWC_ALGO_AUTO && force != CNHWC_ALGO_WINOGRAD &&
-      force != CNHWC_ALGO_IMPLICIT_GEMM && force != CNHWC_ALGO_UNFOLD_GEMM)
+      force != CNHWC_ALGO_IMPLICIT_GEMM && force != CNHWC_ALGO_UNFOLD_GEMM &&
+      force != CNHWC_ALGO_WINOGRAD_HALF)
     return force == CNHWC_ALGO_SMALL_KD ? CNHWC_ERR_NOT_APPLICABLE : CNHWC_ERR_INVALID_ARGUMENT;
 
   // 1. Winograd (gate + budget), or forced.
@@ -204,6 +285,19 @@ cnhwc_status_t select_2d(const cnhwc_conv_desc_t& d, const int64_t out[3],
       // the GEMM configuration depends on (C, O) only, never on the batch tiling
       p->kernel_config = wino_gemm_resident_ok(lay.cs, d.o) ? int32_t(kCfgWinoResident)
                                                             : pick_gemm_config(CNHWC_F32, 0, d.o, false);
+      return CNHWC_OK;
+    }
+  }
+
+  // 1b. Half-precision Winograd F(4x4,3x3), forced or under its AUTO rule.
+  if (force == CNHWC_ALGO_WINOGRAD_HALF) {
+    if (!winograd_h_geometry(d)) return CNHWC_ERR_NOT_APPLICABLE;
+    return plan_winograd_h(d, out, o, true, p);
+  }
+  if (force == CNHWC_ALGO_AUTO && winograd_h_geometry(d) && winograd_h_auto_gate(d)) {
+    cnhwc_plan_t h = *p;
+    if (plan_winograd_h(d, out, o, false, &h) == CNHWC_OK) {
+      *p = h;
       return CNHWC_OK;
     }
   }
@@ -241,15 +335,32 @@ cnhwc_status_t select_3d(const cnhwc_conv_desc_t& d, const int64_t out[3],
                          const cnhwc_select_opts_t& o, cnhwc_plan_t* p) {
   const bool force_kd = o.force_algo == CNHWC_ALGO_SMALL_KD;
   const bool force_native = o.force_algo == CNHWC_ALGO_IMPLICIT_GEMM;
-  if (o.force_algo != CNHWC_ALGO_AUTO && !force_kd && !force_native)
+  const bool force_wh = o.force_algo == CNHWC_ALGO_WINOGRAD_HALF;
+  if (o.force_algo != CNHWC_ALGO_AUTO && !force_kd && !force_native && !force_wh)
     return CNHWC_ERR_NOT_APPLICABLE;
+  if ((force_native || force_wh) && o.force_inner_algo != CNHWC_ALGO_AUTO)
+    return CNHWC_ERR_INVALID_ARGUMENT;
+
+  // 0. Half-precision Winograd with the depth taps summed in the GEMM: forced,
+  // or under its AUTO rule (over budget: fall through).
+  if (force_wh) {
+    if (!winograd_h_geometry(d)) return CNHWC_ERR_NOT_APPLICABLE;
+    return plan_winograd_h(d, out, o, true, p);
+  }
+  if (o.force_algo == CNHWC_ALGO_AUTO && o.force_inner_algo == CNHWC_ALGO_AUTO &&
+      winograd_h_geometry(d) && winograd_h_auto_gate(d)) {
+    cnhwc_plan_t h = *p;
+    if (plan_winograd_h(d, out, o, false, &h) == CNHWC_OK) {
+      *p = h;
+      return CNHWC_OK;
+    }
+  }
   // Structural requirements of the decomposition itself.
   const bool structural = d.n == 1 && d.stride[0] == 1 && d.dil[0] == 1 && d.pad[0] == 0;
   // AUTO guard: also KD <= 7, dilation 1 everywhere, channels multiple of 16.
   const bool guard = structural && d.kd <= 7 && d.dil[1] == 1 && d.dil[2] == 1 &&
                      d.c % 16 == 0 && d.o % 16 == 0;
   if (force_kd && !structural) return CNHWC_ERR_NOT_APPLICABLE;
-  if (force_native && o.force_inner_algo != CNHWC_ALGO_AUTO) return CNHWC_ERR_INVALID_ARGUMENT;
 
   // 1. Depth decomposition (MLX PR "Decompose small kernel-depth 3D convs into
   // 2D convs", Change): forced, or under AUTO when the guard holds and the
@@ -264,6 +375,12 @@ cnhwc_status_t select_3d(const cnhwc_conv_desc_t& d, const int64_t out[3],
     cnhwc_plan_t inner;
     std::memset(&inner, 0, sizeof(inner));
     st = select_2d(f, fo, o, o.force_inner_algo, &inner);
+    if (st == CNHWC_OK && inner.algo == CNHWC_ALGO_WINOGRAD_HALF) {
+      // its output transform has no accumulate epilogue: the frames take the
+      // implicit GEMM instead (the fused 3D form above is the better use)
+      std::memset(&inner, 0, sizeof(inner));
+      st = select_2d(f, fo, o, CNHWC_ALGO_IMPLICIT_GEMM, &inner);
+    }
     if (st != CNHWC_OK) return st;
     if (force_kd || inner.algo == CNHWC_ALGO_WINOGRAD || o.force_inner_algo != CNHWC_ALGO_AUTO) {
       *p = inner;
@@ -315,6 +432,25 @@ WinoLayout wino_layout(const cnhwc_conv_desc_t& d, int64_t oh, int64_t ow, int64
   l.off_v = align_up(l.u_bytes, 256);
   l.off_m = l.off_v + align_up(kWinoP * l.v_plane * 4, 256);
   l.total = l.off_m + align_up(kWinoP * l.m_plane * 4, 256);
+  return l;
+}
+
+WinoHLayout wino_h_layout(const cnhwc_conv_desc_t& d, int64_t od, int64_t oh, int64_t ow,
+                          int64_t tb) {
+  WinoHLayout l{};
+  l.tiles_h = ceil_div(oh, kWinoHM);
+  l.tiles_w = ceil_div(ow, kWinoHM);
+  l.t = l.tiles_h * l.tiles_w;
+  l.cs = wino_h_cs(d.c);
+  l.dp = d.d + 2 * int64_t(d.pad[0]);
+  l.ku = d.kd * l.cs;
+  l.u_bytes = uint64_t(kWinoHP) * d.o * l.ku * 2;
+  l.v_plane = uint64_t(tb) * l.dp * l.t * l.cs;
+  l.m_plane = uint64_t(tb) * od * l.t * d.o;
+  l.off_u = kWinoHHeadBytes;
+  l.off_v = l.off_u + align_up(l.u_bytes, 256);
+  l.off_m = l.off_v + align_up(kWinoHP * l.v_plane * 2, 256);
+  l.total = l.off_m + align_up(kWinoHP * l.m_plane * 4, 256);
   return l;
 }
 
@@ -397,7 +533,7 @@ cnhwc_status_t select_impl(const cnhwc_conv_desc_t* desc, const cnhwc_select_opt
   if (opts->ws_limit_bytes == 0 || opts->force_tile_batch < 0 || opts->force_unfold_rows < 0 ||
       opts->force_gemm_config < 0 || opts->force_split_k < 0)
     return CNHWC_ERR_INVALID_ARGUMENT;
-  if (opts->force_algo < CNHWC_ALGO_AUTO || opts->force_algo > CNHWC_ALGO_SMALL_KD ||
+  if (opts->force_algo < CNHWC_ALGO_AUTO || opts->force_algo > CNHWC_ALGO_WINOGRAD_HALF ||
       opts->force_inner_algo < CNHWC_ALGO_AUTO || opts->force_inner_algo > CNHWC_ALGO_UNFOLD_GEMM)
     return CNHWC_ERR_INVALID_ARGUMENT;
   int64_t out[3];

@@ -28,38 +28,6 @@
 namespace cnhwc {
 namespace {
 
-// out[i] = sum_k Mat[i][k] * in[k] (k ascending), zero coefficients skipped.
-template <int R, int C>
-__device__ __forceinline__ void cmatvec(const float (&mat)[R][C], const float (&in)[C], float (&out)[R]) {
-#pragma unroll
-  for (int i = 0; i < R; ++i) {
-    float s = 0.0f;
-    bool first = true;
-#pragma unroll
-    for (int k = 0; k < C; ++k) {
-      const float m = mat[i][k];
-      if (m != 0.0f) {
-        const float t = (m == 1.0f) ? in[k] : (m == -1.0f) ? -in[k] : m * in[k];
-        s = first ? t : s + t;
-        first = false;
-      }
-    }
-    out[i] = s;
-  }
-}
-
-// Workgroups are dispatched round-robin over the 8 XCDs (each with its own L2).
-// Remap so that XCD x runs one contiguous range of logical workgroups:
-// neighbouring tiles, whose 8x8 windows overlap by two pixels, then share an
-// L2.  A bijection on [0, gridDim.x) for round-robin dispatch.
-__device__ __forceinline__ int64_t xcd_block(int64_t bid, int64_t nwg) {
-  constexpr int64_t kXcd = 8;
-  const int64_t x = bid % kXcd, k = bid / kXcd;
-  const int64_t q = nwg / kXcd, r = nwg % kXcd;
-  const int64_t start = x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q;
-  return start + k;
-}
-
 template <typename E, bool BF16>
 __global__ __launch_bounds__(256) void wino_filter_kernel(const E* __restrict__ w, int64_t ldo,
                                                           int64_t O, int64_t C, int64_t Cs,

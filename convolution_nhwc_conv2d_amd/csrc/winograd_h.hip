@@ -1,0 +1,408 @@
+// Winograd F(4x4,3x3) for fp16/bf16 convs on gfx950: the transforms of the
+// half-precision Winograd path.  The 36 tile-position GEMMs between them run
+// on the fp16 matrix cores (gemm_lds.hip, 256-row tiles, fp32 results).
+//
+// MLX PR "Bound winograd conv2d working set by tiling the batch", Problem:
+// the Winograd conv2d is an input transform into tile-position-major GEMM
+// operands, batched GEMMs over the tile positions and an output transform.
+// MLX PR "Decompose small kernel-depth 3D convs into 2D convs", Change: a 3D
+// conv with a small kernel depth is a sum over its depth taps of per-frame 2D
+// convs.  Here those taps are summed inside the GEMM (K = KD * Cs, the rows of
+// tap kd shifted by kd * dd frames), so a 3D conv runs one output transform.
+//
+// Precision.  Half-precision storage of F(6x6,3x3) operands is too coarse for
+// a 1e-2 relative bound; F(4x4,3x3) with fp16 V and U (11-bit significands)
+// and fp32 M stays well inside it.  fp16's range is the risk: |B^T d B| can
+// reach 100 max|d|.  So the transformed operands are scaled by powers of two
+// picked on the device from max|x| and max|w| (kWino4VBound, kWino4UBound):
+//   V = fp16(sx * B^T d B),  U = fp16(sw * G g G^T),  y = (A^T M A) / (sx sw)
+// with sx * 100 max|x| < 2^15 and sw * max|g| < 2^15, so no transformed value
+// can overflow, for any finite input (bf16 inputs included), and the largest
+// ones use fp16's top binade.  Scaling by a power of two is exact: it changes
+// no bit of a normal result.  The scales
+// come from the whole x and w before the batch loop, so batch tiles see the
+// same scales and tiled runs keep the untiled bits.
+//
+// Workspace (elements): partial maxima, then the scales {sx, sw, 1/sx, 1/sw},
+//   U [36][O][KD*Cs]    fp16, Cs = C rounded up to 32 (zero channels)
+//   V [36][rows][Cs]    fp16, rows = (image or frame) * tiles, frames padded by pd
+//   M [36][rows'][O]    fp32, rows' = output images or frames * tiles
+// Tile (ty, tx) covers input rows 4 ty - ph .. +5 and columns 4 tx - pw .. +5
+// and produces output rows 4 ty .. 4 ty + 3 (cropped).
+#include <hip/hip_runtime.h>
+
+#include "internal.hpp"
+#include "device_common.hpp"
+#include "winograd_f43.h"
+
+namespace cnhwc {
+namespace {
+
+constexpr int kT = kWinoHM + 2;  // 6x6 input tiles
+
+// |h| as integer bits, NaN mapped to 0 (a NaN must not pick the scale; it
+// propagates through the conv itself).  Order of |h| == order of these bits.
+template <bool BF16>
+__device__ __forceinline__ uint32_t abs_bits(uint32_t h) {
+  const uint32_t a = h & 0x7fffu;
+  constexpr uint32_t kInf = BF16 ? 0x7f80u : 0x7c00u;
+  return a > kInf ? 0u : a;
+}
+
+template <bool BF16>
+__device__ __forceinline__ float abs_bits_to_f32(uint32_t a) {
+  if constexpr (BF16) return __builtin_bit_cast(float, a << 16);
+  else return static_cast<float>(__builtin_bit_cast(_Float16, uint16_t(a)));
+}
+
+// Max over the 256 threads of a block; the result is valid in thread 0.
+__device__ __forceinline__ uint32_t block_max(uint32_t v, uint32_t* sm) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = max(v, uint32_t(__shfl_xor(int(v), off)));
+  if ((threadIdx.x & 63) == 0) sm[threadIdx.x >> 6] = v;
+  __syncthreads();
+  if (threadIdx.x == 0) v = max(max(sm[0], sm[1]), max(sm[2], sm[3]));
+  return v;
+}
+
+// blockIdx.y = 0: x, 1: w.  Block b of a tensor's nb blocks strides over its
+// 16-byte vectors and writes the largest |element| (as bits) to partial[y][b].
+template <bool BF16>
+__global__ __launch_bounds__(256) void wino_h_absmax_kernel(const uint16_t* __restrict__ x,
+                                                            int64_t nx, int32_t nbx,
+                                                            const uint16_t* __restrict__ w,
+                                                            int64_t nw, int32_t nbw,
+                                                            uint32_t* __restrict__ partial) {
+  __shared__ uint32_t sm[4];
+  const bool is_w = blockIdx.y == 1;
+  const int32_t nb = is_w ? nbw : nbx;
+  if (int32_t(blockIdx.x) >= nb) return;  // whole block: no barrier is skipped by part of it
+  const uint16_t* __restrict__ src = is_w ? w : x;
+  const int64_t n = is_w ? nw : nx;
+  const int64_t nvec = n / 8;
+  const uint4* __restrict__ vec = reinterpret_cast<const uint4*>(src);
+  uint32_t m = 0;
+  for (int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x; i < nvec; i += int64_t(nb) * 256) {
+    const uint4 q = vec[i];
+    const uint32_t words[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      m = max(m, max(abs_bits<BF16>(words[k] & 0xffffu), abs_bits<BF16>(words[k] >> 16)));
+  }
+  if (blockIdx.x == 0)
+    for (int64_t i = nvec * 8 + threadIdx.x; i < n; i += 256) m = max(m, abs_bits<BF16>(src[i]));
+  m = block_max(m, sm);
+  if (threadIdx.x == 0) partial[blockIdx.y * kWinoHSlots + blockIdx.x] = m;
+}
+
+// Exponent e of the scale 2^e for a tensor with largest |element| a whose
+// transformed values are bounded by bound * a: with a < 2^k and bound <= 2^kb,
+// e = 15 - kb - k gives 2^e * bound * a < 2^15, two below fp16's largest
+// finite value 65504, which leaves room for the rounding of the fp32
+// transform arithmetic.  Zero and non-finite maxima take 2^0.  |e| <= 126
+// keeps 2^e and 2^-e normal fp32 numbers; every finite fp16 or bf16 tensor
+// gets its full scale except bf16 maxima below about 2^-112 (then the top of
+// its range sits lower, still without overflow).
+__device__ __forceinline__ int scale_exp(float a, float bound) {
+  if (!(a > 0.0f) || !(a < __builtin_huge_valf())) return 0;
+  int k, kb;
+  frexpf(a, &k);       // a in [2^(k-1), 2^k)
+  frexpf(bound, &kb);  // bound < 2^kb
+  const int e = 15 - kb - k;
+  return e < -126 ? -126 : (e > 126 ? 126 : e);
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(256) void wino_h_scale_kernel(const uint32_t* __restrict__ partial,
+                                                           int32_t nbx, int32_t nbw,
+                                                           float* __restrict__ scales) {
+  __shared__ uint32_t sm[4];
+  uint32_t mx = 0, mw = 0;
+  for (int i = threadIdx.x; i < nbx; i += 256) mx = max(mx, partial[i]);
+  for (int i = threadIdx.x; i < nbw; i += 256) mw = max(mw, partial[kWinoHSlots + i]);
+  mx = block_max(mx, sm);
+  __syncthreads();  // sm is reused
+  mw = block_max(mw, sm);
+  if (threadIdx.x == 0) {
+    const int ex = scale_exp(abs_bits_to_f32<BF16>(mx), kWino4VBound);
+    const int ew = scale_exp(abs_bits_to_f32<BF16>(mw), kWino4UBound);
+    scales[0] = ldexpf(1.0f, ex);
+    scales[1] = ldexpf(1.0f, ew);
+    scales[2] = ldexpf(1.0f, -ex);  // undone in two exact steps: 2^-(ex+ew) may not be an fp32
+    scales[3] = ldexpf(1.0f, -ew);
+  }
+}
+
+// U[p][o][kd*Cs + c] = fp16(sw * (G g G^T)_p), g = w[o][kd][.][.][c]; zero for c >= C.
+template <bool BF16>
+__global__ __launch_bounds__(256) void wino_h_filter_kernel(const uint16_t* __restrict__ w,
+                                                            int64_t O, int64_t KD, int64_t C,
+                                                            int64_t Cs,
+                                                            const float* __restrict__ scales,
+                                                            uint16_t* __restrict__ U) {
+  const int64_t ku = KD * Cs;
+  const int64_t t = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (t >= O * ku) return;
+  const int64_t o = t / ku, r = t - o * ku;
+  const int64_t kd = r / Cs, c = r - kd * Cs;
+  const uint16_t* __restrict__ g0 = w + (o * KD + kd) * 9 * C + c;
+  float g[3][3];
+#pragma unroll
+  for (int a = 0; a < 3; ++a)
+#pragma unroll
+    for (int b = 0; b < 3; ++b) g[a][b] = c < C ? to_f32<uint16_t, BF16>(g0[(a * 3 + b) * C]) : 0.0f;
+  float t1[kT][3];  // G g
+#pragma unroll
+  for (int b = 0; b < 3; ++b) {
+    const float col[3] = {g[0][b], g[1][b], g[2][b]};
+    float res[kT];
+    cmatvec(kWino4G, col, res);
+#pragma unroll
+    for (int i = 0; i < kT; ++i) t1[i][b] = res[i];
+  }
+  const float s = scales[1];
+  const int64_t plane = O * ku;
+  uint16_t* __restrict__ out = U + o * ku + r;
+#pragma unroll
+  for (int i = 0; i < kT; ++i) {
+    const float row[3] = {t1[i][0], t1[i][1], t1[i][2]};
+    float res[kT];
+    cmatvec(kWino4G, row, res);  // (t1 G^T)[i][j]
+#pragma unroll
+    for (int j = 0; j < kT; ++j) out[(i * kT + j) * plane] = f32_to_f16_bits(s * res[j]);
+  }
+}
+
+// V[p][r][c] = fp16(sx * (B^T d B)_p) for tile row r = (image, ty, tx).  Images
+// are the frames fp of nb elements with Dp frames each; frame fp reads input
+// frame fp - pd (zero outside [0, D)); 2D convs have D = Dp = 1, pd = 0.
+// VEC channels per thread (2 when C is even: 4-byte loads and stores).
+template <bool BF16, int VEC>
+__global__ __launch_bounds__(256) void wino_h_input_kernel(
+    const uint16_t* __restrict__ x, int64_t D, int64_t Dp, int32_t pd, int64_t H, int64_t W,
+    int64_t C, int64_t Cs, int32_t ph, int32_t pw, int64_t TH, int64_t TW,
+    const float* __restrict__ scales, uint16_t* __restrict__ V, int64_t plane, int64_t total) {
+  const int64_t t = xcd_block(blockIdx.x, gridDim.x) * 256 + threadIdx.x;
+  if (t >= total) return;
+  const int64_t groups = Cs / VEC;
+  const int64_t r = t / groups, c = (t - r * groups) * VEC;
+  const int64_t T = TH * TW;
+  const int64_t im = r / T, rr = r - im * T;
+  const int64_t n = im / Dp, f = im - n * Dp - pd;
+  const bool fok = f >= 0 && f < D;
+  const int64_t ty = rr / TW, tx = rr - ty * TW;
+  const int64_t ih0 = ty * kWinoHM - ph, iw0 = tx * kWinoHM - pw;
+  const uint16_t* __restrict__ img = x + (n * D + (fok ? f : 0)) * H * W * C + c;
+  const bool cin = fok && c < C;  // VEC == 2 only for even C: c < C implies c + 1 < C
+  // column transform first: t1[v][a][j] = sum_i BT[a][i] d[i][j]
+  float t1[VEC][kT][kT];
+#pragma unroll
+  for (int j = 0; j < kT; ++j) {
+    const int64_t iw = iw0 + j;
+    const bool wok = cin && iw >= 0 && iw < W;
+    float col[VEC][kT];
+#pragma unroll
+    for (int i = 0; i < kT; ++i) {
+      const int64_t ih = ih0 + i;
+      const bool ok = wok && ih >= 0 && ih < H;
+      if constexpr (VEC == 2) {
+        const uint32_t q = ok ? *reinterpret_cast<const uint32_t*>(img + (ih * W + iw) * C) : 0u;
+        col[0][i] = to_f32<uint16_t, BF16>(uint16_t(q & 0xffffu));
+        col[1][i] = to_f32<uint16_t, BF16>(uint16_t(q >> 16));
+      } else {
+        col[0][i] = ok ? to_f32<uint16_t, BF16>(img[(ih * W + iw) * C]) : 0.0f;
+      }
+    }
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) {
+      float res[kT];
+      cmatvec(kWino4BT, col[v], res);
+#pragma unroll
+      for (int a = 0; a < kT; ++a) t1[v][a][j] = res[a];
+    }
+  }
+  // row transform: v[a][b] = sum_j t1[a][j] BT[b][j], scaled, rounded to fp16
+  const float s = scales[0];
+  uint16_t* __restrict__ out = V + r * Cs + c;
+#pragma unroll
+  for (int a = 0; a < kT; ++a) {
+    float res[VEC][kT];
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) cmatvec(kWino4BT, t1[v][a], res[v]);
+#pragma unroll
+    for (int b = 0; b < kT; ++b) {
+      if constexpr (VEC == 2) {
+        const uint32_t q = uint32_t(f32_to_f16_bits(s * res[0][b])) |
+                           (uint32_t(f32_to_f16_bits(s * res[1][b])) << 16);
+        *reinterpret_cast<uint32_t*>(out + (a * kT + b) * plane) = q;
+      } else {
+        out[(a * kT + b) * plane] = f32_to_f16_bits(s * res[0][b]);
+      }
+    }
+  }
+}
+
+// y[im][oh][ow][o] = ((A^T M A)[oh - 4 ty][ow - 4 tx] / sx) / sw, cropped to
+// [OH, OW], for output image or frame im.  VEC output channels per thread.
+template <bool BF16, int VEC>
+__global__ __launch_bounds__(256) void wino_h_output_kernel(const float* __restrict__ Mt,
+                                                            int64_t plane, int64_t OH,
+                                                            int64_t OW, int64_t O, int64_t TH,
+                                                            int64_t TW,
+                                                            const float* __restrict__ scales,
+                                                            uint16_t* __restrict__ y,
+                                                            int64_t total) {
+  const int64_t t = xcd_block(blockIdx.x, gridDim.x) * 256 + threadIdx.x;
+  if (t >= total) return;
+  const int64_t groups = O / VEC;
+  const int64_t r = t / groups, o = (t - r * groups) * VEC;
+  const int64_t T = TH * TW;
+  const int64_t im = r / T, rr = r - im * T;
+  const int64_t ty = rr / TW, tx = rr - ty * TW;
+  const float* __restrict__ src = Mt + r * O + o;
+  // t1[v][i][b] = sum_a AT[i][a] m[a][b]  (4x6)
+  float t1[VEC][kWinoHM][kT];
+#pragma unroll
+  for (int b = 0; b < kT; ++b) {
+    float col[VEC][kT];
+#pragma unroll
+    for (int a = 0; a < kT; ++a) {
+      if constexpr (VEC == 2) {
+        const float2 q = *reinterpret_cast<const float2*>(src + (a * kT + b) * plane);
+        col[0][a] = q.x;
+        col[1][a] = q.y;
+      } else {
+        col[0][a] = src[(a * kT + b) * plane];
+      }
+    }
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) {
+      float res[kWinoHM];
+      cmatvec(kWino4AT, col[v], res);
+#pragma unroll
+      for (int i = 0; i < kWinoHM; ++i) t1[v][i][b] = res[i];
+    }
+  }
+  const float inv_x = scales[2], inv_w = scales[3];
+#pragma unroll
+  for (int i = 0; i < kWinoHM; ++i) {
+    const int64_t oh = ty * kWinoHM + i;
+    float res[VEC][kWinoHM];
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) {
+      cmatvec(kWino4AT, t1[v][i], res[v]);  // Y[i][j]
+#pragma unroll
+      for (int j = 0; j < kWinoHM; ++j) res[v][j] = (res[v][j] * inv_x) * inv_w;  // exact
+    }
+    if (oh < OH) {
+#pragma unroll
+      for (int j = 0; j < kWinoHM; ++j) {
+        const int64_t ow = tx * kWinoHM + j;
+        if (ow < OW) {
+          uint16_t* dst = y + ((im * OH + oh) * OW + ow) * O + o;
+          // y is written once and not read here again: stream it past the caches
+          if constexpr (VEC == 2) {
+            const uint32_t q = uint32_t(from_f32<uint16_t, BF16>(res[0][j])) |
+                               (uint32_t(from_f32<uint16_t, BF16>(res[1][j])) << 16);
+            __builtin_nontemporal_store(q, reinterpret_cast<uint32_t*>(dst));
+          } else {
+            __builtin_nontemporal_store(from_f32<uint16_t, BF16>(res[0][j]), dst);
+          }
+        }
+      }
+    }
+  }
+}
+
+inline unsigned blocks_for(int64_t total) { return unsigned((total + 255) / 256); }
+
+}  // namespace
+
+int wino_h_absmax_launch(int dtype, const void* x, int64_t nx, const void* w, int64_t nw,
+                         uint32_t* partial, void* stream) {
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int32_t nbx = wino_h_absmax_blocks(nx), nbw = wino_h_absmax_blocks(nw);
+  const dim3 grid{unsigned(nbx > nbw ? nbx : nbw), 2u, 1u};
+  const uint16_t* xs = static_cast<const uint16_t*>(x);
+  const uint16_t* ws = static_cast<const uint16_t*>(w);
+  if (dtype == CNHWC_BF16)
+    hipLaunchKernelGGL((wino_h_absmax_kernel<true>), grid, dim3(256), 0, s, xs, nx, nbx, ws, nw, nbw,
+                       partial);
+  else
+    hipLaunchKernelGGL((wino_h_absmax_kernel<false>), grid, dim3(256), 0, s, xs, nx, nbx, ws, nw, nbw,
+                       partial);
+  return hipGetLastError();
+}
+
+int wino_h_scale_launch(int dtype, const uint32_t* partial, int64_t nx, int64_t nw, float* scales,
+                        void* stream) {
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int32_t nbx = wino_h_absmax_blocks(nx), nbw = wino_h_absmax_blocks(nw);
+  if (dtype == CNHWC_BF16)
+    hipLaunchKernelGGL((wino_h_scale_kernel<true>), dim3(1), dim3(256), 0, s, partial, nbx, nbw, scales);
+  else
+    hipLaunchKernelGGL((wino_h_scale_kernel<false>), dim3(1), dim3(256), 0, s, partial, nbx, nbw, scales);
+  return hipGetLastError();
+}
+
+int wino_h_filter_launch(int dtype, const void* w, int64_t o, int64_t kd, int64_t c, int64_t cs,
+                         const float* scales, uint16_t* u, void* stream) {
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int64_t total = o * kd * cs;
+  const dim3 grid(blocks_for(total));
+  const uint16_t* ws = static_cast<const uint16_t*>(w);
+  if (dtype == CNHWC_BF16)
+    hipLaunchKernelGGL((wino_h_filter_kernel<true>), grid, dim3(256), 0, s, ws, o, kd, c, cs, scales, u);
+  else
+    hipLaunchKernelGGL((wino_h_filter_kernel<false>), grid, dim3(256), 0, s, ws, o, kd, c, cs, scales, u);
+  return hipGetLastError();
+}
+
+int wino_h_input_launch(int dtype, const void* x, int64_t nb, int64_t d, int64_t dp, int32_t pd,
+                        int64_t h, int64_t w, int64_t c, int64_t cs, int32_t ph, int32_t pw,
+                        int64_t th, int64_t tw, const float* scales, uint16_t* v, int64_t plane,
+                        void* stream) {
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int vec = c % 2 == 0 ? 2 : 1;
+  const int64_t total = nb * dp * th * tw * (cs / vec);
+  if (total == 0) return hipSuccess;
+  const dim3 grid(blocks_for(total));
+  const uint16_t* xs = static_cast<const uint16_t*>(x);
+#define CNHWC_WINO_H_INPUT(B, VEC)                                                              \
+  hipLaunchKernelGGL((wino_h_input_kernel<B, VEC>), grid, dim3(256), 0, s, xs, d, dp, pd, h, w, \
+                     c, cs, ph, pw, th, tw, scales, v, plane, total)
+  if (dtype == CNHWC_BF16) {
+    if (vec == 2) CNHWC_WINO_H_INPUT(true, 2);
+    else CNHWC_WINO_H_INPUT(true, 1);
+  } else {
+    if (vec == 2) CNHWC_WINO_H_INPUT(false, 2);
+    else CNHWC_WINO_H_INPUT(false, 1);
+  }
+#undef CNHWC_WINO_H_INPUT
+  return hipGetLastError();
+}
+
+int wino_h_output_launch(int dtype, const float* m, int64_t plane, int64_t nimg, int64_t oh,
+                         int64_t ow, int64_t o, int64_t th, int64_t tw, const float* scales,
+                         void* y, void* stream) {
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int vec = o % 2 == 0 ? 2 : 1;
+  const int64_t total = nimg * th * tw * (o / vec);
+  if (total == 0) return hipSuccess;
+  const dim3 grid(blocks_for(total));
+  uint16_t* ys = static_cast<uint16_t*>(y);
+#define CNHWC_WINO_H_OUTPUT(B, VEC)                                                              \
+  hipLaunchKernelGGL((wino_h_output_kernel<B, VEC>), grid, dim3(256), 0, s, m, plane, oh, ow, o, \
+                     th, tw, scales, ys, total)
+  if (dtype == CNHWC_BF16) {
+    if (vec == 2) CNHWC_WINO_H_OUTPUT(true, 2);
+    else CNHWC_WINO_H_OUTPUT(true, 1);
+  } else {
+    if (vec == 2) CNHWC_WINO_H_OUTPUT(false, 2);
+    else CNHWC_WINO_H_OUTPUT(false, 1);
+  }
+#undef CNHWC_WINO_H_OUTPUT
+  return hipGetLastError();
+}
+
+}  // namespace cnhwc

@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define CNHWC_ABI_VERSION 2
+#define CNHWC_ABI_VERSION 3
 
 /* Fewest GEMM rows (tile_batch * tiles_per_image) a Winograd batch tile may
  * carry when the batch does not fit in one tile; below it AUTO falls back to
@@ -82,7 +82,8 @@ typedef enum {
   CNHWC_ALGO_WINOGRAD = 1,      /* 3x3 stride-1 dilation-1 2D only */
   CNHWC_ALGO_IMPLICIT_GEMM = 2, /* any 2D conv; scratch-free */
   CNHWC_ALGO_UNFOLD_GEMM = 3,   /* any 2D conv; unfold buffer in the workspace */
-  CNHWC_ALGO_SMALL_KD = 4       /* 3D as KD accumulated 2D convs (3D: IMPLICIT_GEMM = native) */
+  CNHWC_ALGO_SMALL_KD = 4,      /* 3D as KD accumulated 2D convs (3D: IMPLICIT_GEMM = native) */
+  CNHWC_ALGO_WINOGRAD_HALF = 5  /* fp16/bf16 Winograd F(4x4,3x3), 2D and 3D (see below) */
 } cnhwc_algo_t;
 
 typedef enum {
@@ -179,12 +180,41 @@ const char* cnhwc_status_string(cnhwc_status_t s);
  *   implicit GEMM, one GEMM with K = KD*KH*KW*C over the NDHWC gather (any
  *   batch, depth stride, padding and dilation; the page's fall-through for
  *   what the guard rejects, and the decomposition with its taps fused).
+ * WINOGRAD_HALF (the half-precision Winograd path; tiling page, Problem: the
+ *   three-stage Winograd structure; 3D page, Change: a 3D conv as a sum of
+ *   per-frame 2D convs over its depth taps).  F(4x4,3x3): 6x6 input tiles at
+ *   stride 4, 36 tile positions.  The transformed input and filter are stored
+ *   as fp16 scaled by powers of two that the device picks from max|x| and
+ *   max|w| over the whole tensors (so no transformed value can overflow fp16,
+ *   and batch tiles keep the untiled bits); the 36 GEMMs accumulate in fp32
+ *   on the fp16 matrix cores into fp32 results, and the output transform
+ *   undoes the scales exactly.  3D: the depth taps are summed inside each
+ *   GEMM (K = KD * Cs, tap kd reading the transformed frames kd * dilation
+ *   further on), then one output transform; any batch (one element per
+ *   batch tile), depth pad and depth dilation, depth stride 1.  Needs dtype
+ *   F16 or BF16, KH = KW = 3, stride 1, dilation 1 and padding <= 1 in the
+ *   image plane, and C >= 16; otherwise NOT_APPLICABLE.  (The fp16 rounding
+ *   of a tile scales with the whole 6x6 tile: with padding 2 a corner window
+ *   holds one real pixel of nine and its error reaches 1-3e-2 of its own
+ *   sum |x||w|; below 16 channels the rounding errors do not average down.)  The batch is tiled by the budget rule with
+ *   scratch_per_element = 36 * tiles * (frames * Cs * 2 + OD * O * 4) bytes
+ *   (Cs = C rounded up to 32); force_tile_batch applies to 2D only.
+ *   force_gemm_config may name 14 or 15 (the 256-row tiles); force_split_k is
+ *   ignored.  AUTO does not take it yet.  Error: |y - conv| stays below
+ *   5e-3 of sum |x||w| on independent, identically distributed data (the fp16
+ *   rounding of the transformed operands; about 1e-3 at C = 256).  Like any
+ *   Winograd form its error scales with the magnitudes in a whole tile, not
+ *   in one window, and an output whose window only holds values below about
+ *   2^-24 of max|x| loses relative precision (fp16 subnormals).
  * Forcing: WINOGRAD needs only 3x3/stride 1/dilation 1 (the channel gates are
  *   skipped); a forced tile size is capped by the budget tile (tiling page,
  *   Testing).  SMALL_KD needs N == 1, depth stride 1, depth dilation 1, depth
  *   pad 0.  For 3D, IMPLICIT_GEMM (the native path) and SMALL_KD can be
- *   forced; WINOGRAD and UNFOLD_GEMM are NOT_APPLICABLE, and force_inner_algo
- *   with the native path is INVALID_ARGUMENT.
+ *   forced, and WINOGRAD_HALF; WINOGRAD and UNFOLD_GEMM are NOT_APPLICABLE,
+ *   and force_inner_algo with the native path or WINOGRAD_HALF is
+ *   INVALID_ARGUMENT (force_inner_algo never names WINOGRAD_HALF: the
+ *   per-frame convs of SMALL_KD accumulate, which its output transform does
+ *   not).
  * Returns OK and fills *plan, or an error (plan untouched). */
 cnhwc_status_t cnhwc_conv_select(const cnhwc_conv_desc_t* desc, const cnhwc_select_opts_t* opts,
                                  cnhwc_plan_t* plan);
@@ -223,7 +253,9 @@ cnhwc_status_t cnhwc_conv2d_fwd(const cnhwc_conv_desc_t* desc, const cnhwc_plan_
  * slice w[:, kd] (a strided view) form a 2D conv with batch OD, computed by the
  * plan's inner algorithm and accumulated in fp32 (in y itself for F32, in the
  * workspace otherwise); the last tap rounds into y once.  KD == 1 gives the
- * same bits as conv2d on the [D,H,W,C] frames. */
+ * same bits as conv2d on the [D,H,W,C] frames.  WINOGRAD_HALF: per batch
+ * element, the input transform of its D + 2*pad frames (pad frames zero), the
+ * 36 GEMMs with the KD taps in K, and one output transform into y. */
 cnhwc_status_t cnhwc_conv3d_fwd(const cnhwc_conv_desc_t* desc, const cnhwc_plan_t* plan,
                                 const void* x, const void* w, void* y, void* workspace,
                                 uint64_t workspace_bytes, void* hip_stream);
@@ -238,7 +270,8 @@ typedef enum {
   CNHWC_KERNEL_IMPLICIT_GEMM = 5,
   CNHWC_KERNEL_UNFOLD = 6,       /* one unfold chunk */
   CNHWC_KERNEL_UNFOLD_GEMM = 7,  /* the dense GEMM of one unfold chunk */
-  CNHWC_KERNEL_SPLITK_REDUCE = 8 /* sum of the K-split partial sums + epilogue */
+  CNHWC_KERNEL_SPLITK_REDUCE = 8, /* sum of the K-split partial sums + epilogue */
+  CNHWC_KERNEL_WINO_SCALE = 9     /* half-precision Winograd: max |x|, |w| and the scales */
 } cnhwc_kernel_kind_t;
 
 /* Number of kernels a forward call with this plan launches (3D: over all

@@ -389,3 +389,111 @@ def test_graph_capture_replays_bit_identical():
         fn, case, x, w, plan, ws, eager, out = runs[0]
         fn(x, w, **case.conv_kwargs(), plan=plan, workspace=ws, out=out)
         torch.cuda.synchronize()
+
+
+# ------------------------------- half-precision Winograd F(4x4,3x3)
+
+# (name, n, h, w, c, o, pad, dtype, gemm tile): ragged 4x4 output tiles, odd
+# channel counts (one channel per thread, padded K), padding 0, the fewest
+# channels the path takes (16), and a case spanning several 256-row GEMM
+# tiles with ragged rows and columns.
+WH2D_CASES = [
+    ("ragged_f16", 3, 21, 19, 64, 96, 1, "f16", 0),
+    ("ragged_bf16", 3, 21, 19, 64, 96, 1, "bf16", 0),
+    ("odd_channels_f16", 2, 13, 15, 37, 45, 1, "f16", 0),
+    ("odd_channels_bf16", 2, 13, 15, 37, 45, 1, "bf16", 0),
+    ("pad0_bf16", 2, 18, 18, 128, 64, 0, "bf16", 0),
+    ("c16_f16", 2, 30, 30, 16, 32, 1, "f16", 0),
+    ("tiles_f16", 4, 64, 60, 256, 320, 1, "f16", 14),
+    ("tiles_bf16", 4, 64, 60, 256, 320, 1, "bf16", 15),
+]
+# fp16 storage of the transformed operands costs about 2e-3 of sum|x||w|; the
+# bf16 output rounding adds up to 2e-3 more.
+WH_BOUND = {torch.float16: 5e-3, torch.bfloat16: 8e-3}
+
+
+@pytest.mark.parametrize("spec", WH2D_CASES, ids=[c[0] for c in WH2D_CASES])
+def test_winograd_half_parity(spec):
+    name, n, h, w, c, o, pad, dt, cfg = spec
+    case = cw.ConvCase(f"wh_{name}", n, h, w, c, o, 3, 3, (1, 1), (pad, pad), (1, 1), dt, "normal", "normal",
+                       None, 61, c + o)
+    x, wt = case.input(), case.weight()
+    yr, den = oracle.conv(to_oracle(x), to_oracle(wt), **case.conv_kwargs())
+    plan = cn.plan2d(case.x_shape(), case.w_shape(), **case.conv_kwargs(), dtype=x.dtype, algo="winograd_half",
+                     gemm_config=cfg or None)
+    assert plan.algo_name == "winograd_half"
+    y = cn.conv2d(_dev(x), _dev(wt), **case.conv_kwargs(), algo="winograd_half", gemm_config=cfg or None,
+                  out=poisoned(yr.shape, x.dtype))
+    err = check_parity(y.cpu(), yr, den, y.dtype, case.name)
+    assert err < WH_BOUND[y.dtype], err
+    if cfg:
+        # the two 256-row tiles sum K in the same order: identical bits
+        other = 29 - cfg
+        y2 = cn.conv2d(_dev(x), _dev(wt), **case.conv_kwargs(), algo="winograd_half", gemm_config=other)
+        assert torch.equal(bits(y2), bits(y))
+
+
+@pytest.mark.parametrize("tile", [1, 2, 3])
+def test_winograd_half_tiled_bit_identical_to_untiled(tile):
+    """The scales come from the whole tensors, so batch tiles keep the untiled bits."""
+    case = cw.ConvCase("wh_tiling", 5, 24, 28, 64, 96, 3, 3, (1, 1), (1, 1), (1, 1), "f16", "normal", "normal",
+                       None, 62, 0)
+    x, w = _dev(case.input()), _dev(case.weight())
+    full = cn.conv2d(x, w, 1, 1, 1, algo="winograd_half")
+    p = cn.plan2d(tuple(x.shape), tuple(w.shape), 1, 1, 1, torch.float16, algo="winograd_half", tile_batch=tile)
+    assert p.tile_batch == tile and p.n_tiles == -(-case.n // tile)
+    tiled = cn.conv2d(x, w, 1, 1, 1, algo="winograd_half", tile_batch=tile, out=poisoned(full.shape, full.dtype))
+    assert torch.equal(bits(tiled), bits(full))
+
+
+@pytest.mark.parametrize("dt,scale", [("f16", 6.0e4), ("f16", 1.0e-3), ("bf16", 1.0e30), ("bf16", 1.0e-30),
+                                      ("f16", 0.0)])
+def test_winograd_half_input_range(dt, scale):
+    """Inputs near the top of fp16's range (|B^T d B| would reach 6e6 unscaled),
+    far outside it (bf16), tiny, and all zero: the power-of-two scales keep
+    every transformed value finite and the result within tolerance.  The
+    weights are small enough (std 0.1/sqrt(K)) that y itself stays in fp16."""
+    case = cw.ConvCase(f"wh_range_{dt}", 2, 14, 13, 64, 40, 3, 3, (1, 1), (1, 1), (1, 1), dt, "uniform", "normal",
+                       0.1 / (9 * 64) ** 0.5, 63, 0)
+    x = (case.input().float() * scale).to(cw.DTYPES[dt])
+    wt = case.weight()
+    yr, den = oracle.conv(to_oracle(x), to_oracle(wt), **case.conv_kwargs())
+    y = cn.conv2d(_dev(x), _dev(wt), **case.conv_kwargs(), algo="winograd_half")
+    err = check_parity(y.cpu(), yr, den, y.dtype, case.name + f"x{scale}")
+    assert err < WH_BOUND[y.dtype], err
+
+
+# (name, n, d, h, w, c, o, kd, pad (d, h, w), dilation (d, h, w), dtype)
+WH3D_CASES = [
+    ("video_like", 1, 7, 16, 20, 64, 64, 3, (0, 1, 1), (1, 1, 1), "bf16"),
+    ("pad_d", 1, 6, 11, 13, 32, 48, 3, (1, 1, 1), (1, 1, 1), "f16"),
+    ("dil_d2_batch2", 2, 9, 10, 12, 64, 40, 3, (1, 0, 1), (2, 1, 1), "bf16"),
+    ("kd5_odd_o", 2, 8, 9, 9, 40, 33, 5, (2, 1, 1), (1, 1, 1), "f16"),
+    ("kd1", 1, 5, 12, 14, 64, 64, 1, (0, 1, 1), (1, 1, 1), "bf16"),
+]
+
+
+@pytest.mark.parametrize("spec", WH3D_CASES, ids=[c[0] for c in WH3D_CASES])
+def test_winograd_half_3d_parity(spec):
+    """The depth taps summed inside the tile-position GEMMs (K = KD * Cs, tap kd
+    reading the transformed frames kd * dilation further on)."""
+    name, n, d, h, w, c, o, kd, pad, dil, dt = spec
+    case = cw.ConvCase(f"wh3d_{name}", n, h, w, c, o, 3, 3, (1, 1, 1), pad, dil, dt, "normal", "normal", None,
+                       64, c + kd, nd=3, d=d, kd=kd)
+    x, wt = case.input(), case.weight()
+    yr, den = oracle.conv(to_oracle(x), to_oracle(wt), **case.conv_kwargs())
+    plan = cn.plan3d(case.x_shape(), case.w_shape(), **case.conv_kwargs(), dtype=x.dtype, algo="winograd_half")
+    assert plan.algo_name == "winograd_half" and plan.n_tiles == n
+    y = cn.conv3d(_dev(x), _dev(wt), **case.conv_kwargs(), algo="winograd_half", out=poisoned(yr.shape, x.dtype))
+    err = check_parity(y.cpu(), yr, den, y.dtype, case.name)
+    assert err < WH_BOUND[y.dtype], err
+
+
+def test_winograd_half_3d_kd1_bit_identical_to_conv2d():
+    """KD = 1: the 3D path is the 2D path over the frames, bit for bit."""
+    case = cw.ConvCase("wh3d_vs_2d", 1, 12, 14, 64, 48, 3, 3, (1, 1, 1), (0, 1, 1), (1, 1, 1), "f16", "normal",
+                       "normal", None, 65, 0, nd=3, d=5, kd=1)
+    x, wt = _dev(case.input()), _dev(case.weight())
+    y3 = cn.conv3d(x, wt, **case.conv_kwargs(), algo="winograd_half")
+    y2 = cn.conv2d(x[0], wt[:, 0], 1, 1, 1, algo="winograd_half")
+    assert torch.equal(bits(y3[0]), bits(y2))

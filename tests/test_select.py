@@ -390,3 +390,105 @@ def test_forced_split_k():
         with pytest.raises(cn.CnhwcError) as e:
             cn.plan2d(xs, ws, 1, 1, 1, F16, **kw)
         assert e.value.name == "NOT_APPLICABLE", kw
+
+
+# ------------------------------------- half-precision Winograd F(4x4,3x3)
+
+BF16 = torch.bfloat16
+HEAD = 8448  # partial maxima of x and w (2 x 1024 words) + 4 scales, 256-aligned
+
+
+def _wh_scratch(t, c, o, frames=1, od=1):
+    cs = -(-c // 32) * 32
+    return 36 * t * (frames * cs * 2 + od * o * 4)
+
+
+def test_winograd_half_2d_plan():
+    xs, ws = (8, 56, 56, 200), (256, 3, 3, 200)
+    p = cn.plan2d(xs, ws, 1, 1, 1, F16, algo="winograd_half", ws_limit=288 * 10**9)
+    t = 14 * 14
+    assert p.algo_name == "winograd_half" and p.tiles_per_image == t
+    assert p.tile_batch == 8 and p.n_tiles == 1 and p.split_k == 1
+    assert p.scratch_per_element == _wh_scratch(t, 200, 256)
+    u = 36 * 256 * 224 * 2
+    assert p.own_bytes == 8 * 56 * 56 * (200 + 256) * 2 + HEAD + u
+    assert p.workspace_bytes >= HEAD + u + 8 * p.scratch_per_element
+    assert p.kernel_config in (14, 15)
+    desc = cn.make_desc(xs, ws, 1, 1, 1, F16)
+    assert cn.lib.cnhwc_launch_count(ctypes.byref(desc), ctypes.byref(p)) == 6
+    # ragged output (OH = 53 -> 14 tile rows), padding 0, bf16
+    q = cn.plan2d((3, 55, 57, 64), (96, 3, 3, 64), 1, 0, 1, BF16, algo="winograd_half")
+    assert q.out_h == 53 and q.out_w == 55 and q.tiles_per_image == 14 * 14
+
+
+def test_winograd_half_geometry_gate():
+    xs = (2, 32, 32, 64)
+    for ws, kw in [((64, 3, 3, 64), dict(dtype=torch.float32)),
+                   ((64, 5, 5, 64), dict(dtype=F16)),
+                   ((64, 3, 3, 64), dict(dtype=F16, stride=2)),
+                   ((64, 3, 3, 64), dict(dtype=F16, dil=2)),
+                   ((64, 3, 3, 64), dict(dtype=F16, pad=2)),       # corner windows mostly padding
+                   ((64, 3, 3, 64), dict(dtype=F16, pad=(1, 2)))]:
+        dt = kw.pop("dtype")
+        with pytest.raises(cn.CnhwcError) as e:
+            cn.plan2d(xs, ws, kw.get("stride", 1), kw.get("pad", 1), kw.get("dil", 1), dt, algo="winograd_half")
+        assert e.value.name == "NOT_APPLICABLE", (ws, dt, kw)
+    with pytest.raises(cn.CnhwcError) as e:                  # too few channels to average rounding
+        cn.plan2d((2, 32, 32, 15), (64, 3, 3, 15), 1, 1, 1, F16, algo="winograd_half")
+    assert e.value.name == "NOT_APPLICABLE"
+    assert cn.plan2d((2, 32, 32, 16), (64, 3, 3, 16), 1, 1, 1, F16, algo="winograd_half").algo_name == "winograd_half"
+    assert cn.plan2d(xs, (64, 3, 3, 64), 1, 0, 1, F16, algo="winograd_half").algo_name == "winograd_half"
+
+
+def test_winograd_half_not_taken_by_auto_yet():
+    for dt in (F16, BF16):
+        p = cn.plan2d((8, 64, 64, 512), (512, 3, 3, 512), 1, 1, 1, dt)
+        assert p.algo_name == "implicit_gemm"
+
+
+def test_winograd_half_budget_tiles_and_over_budget():
+    xs, ws = (16, 64, 64, 128), (128, 3, 3, 128)
+    full = cn.plan2d(xs, ws, 1, 1, 1, F16, algo="winograd_half", ws_limit=288 * 10**9)
+    per = full.scratch_per_element
+    wl = (full.own_bytes + 5 * per) * 4 // 3 + 8
+    p = cn.plan2d(xs, ws, 1, 1, 1, F16, algo="winograd_half", ws_limit=wl)
+    assert p.tile_batch == 5 and p.n_tiles == 4
+    f = cn.plan2d(xs, ws, 1, 1, 1, F16, algo="winograd_half", ws_limit=wl, tile_batch=3)
+    assert f.tile_batch == 3 and f.n_tiles == 6
+    with pytest.raises(cn.CnhwcError) as e:
+        cn.plan2d(xs, ws, 1, 1, 1, F16, algo="winograd_half", ws_limit=10**6)
+    assert e.value.name == "BUDGET"
+
+
+def test_winograd_half_forced_gemm_tiles():
+    xs, ws = (4, 32, 32, 64), (96, 3, 3, 64)
+    for cfg in (14, 15):
+        assert cn.plan2d(xs, ws, 1, 1, 1, F16, algo="winograd_half", gemm_config=cfg).kernel_config == cfg
+    for cfg in (11, 3):
+        with pytest.raises(cn.CnhwcError) as e:
+            cn.plan2d(xs, ws, 1, 1, 1, F16, algo="winograd_half", gemm_config=cfg)
+        assert e.value.name == "NOT_APPLICABLE"
+    assert cn.plan2d(xs, ws, 1, 1, 1, F16, algo="winograd_half", split_k=4).split_k == 1
+
+
+def test_winograd_half_3d_plan():
+    xs, ws = (2, 9, 20, 24, 64), (80, 3, 3, 3, 64)
+    p = cn.plan3d(xs, ws, 1, (1, 1, 1), (2, 1, 1), BF16, algo="winograd_half")
+    # depth: 9 frames + 2 pad = 11, dilation 2 -> OD = 11 - 4 = 7
+    assert p.algo_name == "winograd_half" and p.out_d == 7 and p.out_h == 20 and p.out_w == 24
+    t = 5 * 6
+    assert p.tile_batch == 1 and p.n_tiles == 2 and p.tiles_per_image == t
+    assert p.scratch_per_element == _wh_scratch(t, 64, 80, frames=11, od=7)
+    desc = cn.make_desc(xs, ws, 1, (1, 1, 1), (2, 1, 1), BF16)
+    assert cn.lib.cnhwc_launch_count(ctypes.byref(desc), ctypes.byref(p)) == 3 + 3 * 2
+    # depth stride 2 and spatial 5x5 are not for this path; inner algorithms neither
+    for args in [dict(s=(2, 1, 1), w=ws), dict(s=1, w=(80, 3, 5, 5, 64))]:
+        with pytest.raises(cn.CnhwcError) as e:
+            cn.plan3d(xs, args["w"], args["s"], 1, 1, BF16, algo="winograd_half")
+        assert e.value.name == "NOT_APPLICABLE"
+    with pytest.raises(cn.CnhwcError) as e:
+        cn.plan3d(xs, ws, 1, 1, 1, BF16, algo="winograd_half", inner_algo="implicit_gemm")
+    assert e.value.name == "INVALID_ARGUMENT"
+    with pytest.raises(cn.CnhwcError) as e:
+        cn.plan3d((1,) + xs[1:], ws, 1, (0, 1, 1), 1, BF16, inner_algo="winograd_half")
+    assert e.value.name == "INVALID_ARGUMENT"
