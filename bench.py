@@ -59,7 +59,8 @@ def parse():
                          "with --calib-copy, write profiles/traffic.json, print it and exit")
     ap.add_argument("--suite", default=None,
                     help="instead of the headline line, time other workloads: "
-                         "comma list of small,wide,sweep,resnet,video,conv1d or 'all' (one JSON line each)")
+                         "comma list of small,wide,sweep,wino_half,resnet,video,conv1d or 'all' "
+                         "(one JSON line each)")
     return ap.parse_args()
 
 
@@ -333,10 +334,29 @@ def run_suite(names):
     if "video" in names:
         for shape in cw.VIDEO3D_SHAPES:
             case = cw.video3d(*shape)
-            for inner in ("auto", "implicit_gemm", "unfold_gemm"):
-                r = measure(case, inner=None if inner == "auto" else inner)
+            # AUTO (half-precision Winograd, taps summed in its GEMMs), the native
+            # 3D implicit GEMM, and the per-tap decomposition with each inner path
+            for algo, inner in (("auto", None), ("implicit_gemm", None), ("auto", "implicit_gemm"),
+                                ("auto", "unfold_gemm")):
+                r = measure(case, algo, inner=inner)
                 r["suite"] = "video3d"
                 emit(r)
+    if "wino_half" in names:
+        # half-precision Winograd F(4x4,3x3) against the implicit GEMM around
+        # AUTO's crossover (3x3 s1 p1 on 32x32)
+        for dt in ("f16", "bf16"):
+            for c, o in ((256, 256), (256, 512), (512, 256), (512, 512), (1024, 512), (1024, 1024), (2048, 512)):
+                for n in (16, 64):
+                    case = cw.cout_axis(dt, o, n, c)
+                    res = {a: measure(case, a) for a in ("implicit_gemm", "winograd_half")}
+                    auto = cn.plan2d(case.x_shape(), case.w_shape(), **case.conv_kwargs(),
+                                     dtype=cw.DTYPES[dt]).algo_name
+                    emit({"suite": "wino_half", "dtype": dt, "c_in": c, "c_out": o, "m": n * 1024, "auto": auto,
+                          "implicit_ms": res["implicit_gemm"]["ms"], "wino_half_ms": res["winograd_half"]["ms"],
+                          "implicit_tflops": res["implicit_gemm"]["tflops"],
+                          "wino_half_tflops": res["winograd_half"]["tflops"],
+                          "wino_half_kernels_ms": res["winograd_half"]["kernels_ms"],
+                          "speedup": res["implicit_gemm"]["ms"] / res["winograd_half"]["ms"]})
     if "conv1d" in names:
         # Whisper-large-shaped encoder convs (128 log-mel bins -> 1280, k3 p1;
         # 1280 -> 1280, k3 s2 p1) over 3000 frames, through the 2D path (H = 1)
@@ -356,7 +376,7 @@ def main():
         print(json.dumps(traffic_from(args.traffic_from[0], args.traffic_from[1], args.calib_copy, key), indent=1))
         return
     if args.suite:
-        names = ({"small", "wide", "sweep", "resnet", "video", "conv1d"} if args.suite == "all"
+        names = ({"small", "wide", "sweep", "wino_half", "resnet", "video", "conv1d"} if args.suite == "all"
                  else set(args.suite.split(",")))
         run_suite(names)
         return

@@ -95,18 +95,34 @@ bool winograd_h_geometry(const cnhwc_conv_desc_t& d) {
          d.pad[1] <= 1 && d.pad[2] <= 1 && d.c >= 16;
 }
 
-// AUTO's rule for the half-precision Winograd path.  Not taken yet: it is
-// forceable and parity-tested while its crossover against the implicit GEMM
-// is measured.
-bool winograd_h_auto_gate(const cnhwc_conv_desc_t& d) {
-  (void)d;
-  return false;
+// AUTO's rule for the half-precision Winograd path (on top of its geometry).
+// Per output pixel it moves about 11 C + 20 O bytes more than the implicit
+// GEMM (fp16 V written and read, x read: C side; fp32 M written and read, y
+// written: O side) and saves 13.5 KD C O of the 18 KD C O multiply-adds.  On
+// MI355X (bf16/fp16, 3x3, C, O in 64..2048, 2D and 3D) it was faster in
+// every measured case with KD C >= 384 and KD C O >= 13 (11 C + 20 O), by
+// 1.1-2.6x, and slower in every case with C = 256 in 2D (0.7-0.96x) or
+// 3D 64 -> 128 (0.78x); between 12 and 13 it depends on the implicit GEMM's
+// efficiency at the shape (0.93-1.3x) and is left to the implicit GEMM.
+// Below 512 GEMM rows (N OD tiles) the fixed cost of the scale and filter
+// passes (about 25 us) decides: 0.66-1.02x.
+bool winograd_h_auto_gate(const cnhwc_conv_desc_t& d, const int64_t out[3]) {
+  const double kc = double(d.kd) * double(d.c);
+  const double rows = double(d.n) * double(out[0]) * double(ceil_div(out[1], kWinoHM)) *
+                      double(ceil_div(out[2], kWinoHM));
+  return kc >= 384 && kc * double(d.o) >= 13.0 * (11.0 * double(d.c) + 20.0 * double(d.o)) &&
+         rows >= 512;
 }
 
-// The 256-row GEMM tile for the half-precision Winograd GEMMs (rows x n, batch
-// tile positions): the occupancy model of pick_gemm_config over the two
-// direct-to-LDS tiles.
-int32_t pick_lds_tile(int64_t rows, int64_t n, int64_t batch) {
+// The 256-row GEMM tile for the half-precision Winograd GEMMs (rows x n x k,
+// batch tile positions).  With a short K loop (k <= 1152) and n <= 512 the
+// 256 x 128 tile at two workgroups per CU measured faster on nearly every
+// shape (the other workgroup's MFMAs cover one's fp32 result stores; up to
+// 1.2x); with longer K loops or wider n, the occupancy model of
+// pick_gemm_config over the two direct-to-LDS tiles (the 256 x 256 tile: 5%
+// faster on the 41x120x208 512 -> 512 video conv, K = 1536).
+int32_t pick_lds_tile(int64_t rows, int64_t n, int64_t k, int64_t batch) {
+  if (k <= 1152 && n <= 512) return kCfgH_256x128L;
   struct Cand { int32_t id; int64_t bn, occ; double eff; };
   const Cand cands[2] = {{kCfgH_256x256, 256, 1, 1.35}, {kCfgH_256x128L, 128, 2, 1.20}};
   constexpr int64_t kCUs = 256;
@@ -224,7 +240,7 @@ cnhwc_status_t plan_winograd_h(const cnhwc_conv_desc_t& d, const int64_t out[3],
   int32_t cfg = o.force_gemm_config;
   if (cfg != 0 && cfg != kCfgH_256x256 && cfg != kCfgH_256x128L) return CNHWC_ERR_NOT_APPLICABLE;
   // the GEMM tile depends on the untiled shape only
-  if (cfg == 0) cfg = pick_lds_tile((d.nd == 3 ? 1 : d.n) * out[0] * one.t, d.o, kWinoHP);
+  if (cfg == 0) cfg = pick_lds_tile((d.nd == 3 ? 1 : d.n) * out[0] * one.t, d.o, one.ku, kWinoHP);
   const WinoHLayout lay = wino_h_layout(d, out[0], out[1], out[2], tb);
   p->algo = p->inner_algo = CNHWC_ALGO_WINOGRAD_HALF;
   p->out_d = out[0];
@@ -294,7 +310,7 @@ cnhwc_status_t select_2d(const cnhwc_conv_desc_t& d, const int64_t out[3],
     if (!winograd_h_geometry(d)) return CNHWC_ERR_NOT_APPLICABLE;
     return plan_winograd_h(d, out, o, true, p);
   }
-  if (force == CNHWC_ALGO_AUTO && winograd_h_geometry(d) && winograd_h_auto_gate(d)) {
+  if (force == CNHWC_ALGO_AUTO && winograd_h_geometry(d) && winograd_h_auto_gate(d, out)) {
     cnhwc_plan_t h = *p;
     if (plan_winograd_h(d, out, o, false, &h) == CNHWC_OK) {
       *p = h;
@@ -348,7 +364,7 @@ cnhwc_status_t select_3d(const cnhwc_conv_desc_t& d, const int64_t out[3],
     return plan_winograd_h(d, out, o, true, p);
   }
   if (o.force_algo == CNHWC_ALGO_AUTO && o.force_inner_algo == CNHWC_ALGO_AUTO &&
-      winograd_h_geometry(d) && winograd_h_auto_gate(d)) {
+      winograd_h_geometry(d) && winograd_h_auto_gate(d, out)) {
     cnhwc_plan_t h = *p;
     if (plan_winograd_h(d, out, o, false, &h) == CNHWC_OK) {
       *p = h;

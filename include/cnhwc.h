@@ -170,9 +170,15 @@ const char* cnhwc_status_string(cnhwc_status_t s);
  *     O % 32 == 0, C + O >= 256 and dtype == F32, and the budget rule admits
  *     it: tile = min(N, floor(budget / scratch_per_element)); fall back if
  *     tile < 1, or if tile < N and tile * tiles_per_image < CNHWC_MIN_TILE_ROWS.
+ *  1b. WINOGRAD_HALF for F16/BF16 where its geometry holds (below),
+ *     KD*C >= 384, KD*C*O >= 13*(11*C + 20*O) and
+ *     N * OD * ceil(OH/4) * ceil(OW/4) >= 512 (KD = OD = 1 in 2D), under the
+ *     same budget rule: the measured crossover against the implicit GEMM on
+ *     MI355X (the tiling page runs its Winograd path for half precision too).
  *  2. Unfold + GEMM for F16/BF16 with O >= CNHWC_UNFOLD_MIN_COUT.
  *  3. Implicit GEMM.
- * AUTO, 3D (3D page, Change): SMALL_KD when N == 1, KD <= 7, depth stride 1,
+ * AUTO, 3D: first WINOGRAD_HALF under rule 1b (the depth taps summed in its
+ *   GEMMs).  Then (3D page, Change): SMALL_KD when N == 1, KD <= 7, depth stride 1,
  *   dilation 1 in every dim, depth pad 0, C % 16 == 0 and O % 16 == 0 and the
  *   per-tap 2D algorithm (AUTO-selected on the [OD,H,W,C] frame conv, or
  *   forced by force_inner_algo) is Winograd; the decomposition exists to give
@@ -200,7 +206,7 @@ const char* cnhwc_status_string(cnhwc_status_t s);
  *   scratch_per_element = 36 * tiles * (frames * Cs * 2 + OD * O * 4) bytes
  *   (Cs = C rounded up to 32); force_tile_batch applies to 2D only.
  *   force_gemm_config may name 14 or 15 (the 256-row tiles); force_split_k is
- *   ignored.  AUTO does not take it yet.  Error: |y - conv| stays below
+ *   ignored.  AUTO takes it by rule 1b.  Error: |y - conv| stays below
  *   5e-3 of sum |x||w| on independent, identically distributed data (the fp16
  *   rounding of the transformed operands; about 1e-3 at C = 256).  Like any
  *   Winograd form its error scales with the magnitudes in a whole tile, not

@@ -115,6 +115,8 @@ def _half_case(dtype, c_in, c_out, n, k=3, s=1, d=1, p=None, hw=32):
 
 
 def _check_half(case, algos=("implicit_gemm", "unfold_gemm"), count=512, unfold_rows=None):
+    if (case.kh, case.kw, case.stride, case.dil) == (3, 3, (1, 1), (1, 1)) and max(case.pad) <= 1 and case.c >= 16:
+        algos = tuple(algos) + ("winograd_half",)
     x, w = case.input(), case.weight()
     xg, wg = x.cuda(), w.cuda()
     p0 = cn.plan2d(tuple(x.shape), tuple(w.shape), **case.conv_kwargs(), dtype=x.dtype)
@@ -192,13 +194,13 @@ def test_video3d_bf16(shape):
     case = cw.video3d(t, h, w_, c, o)
     x, w = case.input(), case.weight()
     p = cn.plan3d(tuple(x.shape), tuple(w.shape), **case.conv_kwargs(), dtype=x.dtype)
-    assert p.algo_name == "implicit_gemm"  # native 3D GEMM (bf16 frames would not take Winograd)
+    assert p.algo_name == "winograd_half"  # depth taps summed in the half-precision Winograd GEMMs
     per = p.out_h * p.out_w
     frames = sorted(np.random.default_rng(5).choice(p.out_d, 2, replace=False).tolist())
     rows = np.concatenate([f * per + _rows_for(per, 1024, f) for f in frames]).astype(np.int64)
     yr, den = oracle.conv(to_oracle(x), to_oracle(w), **case.conv_kwargs(), rows=rows)
     xg, wg = x.cuda(), w.cuda()
-    for algo in ("auto", "small_kd"):
+    for algo in ("auto", "implicit_gemm", "small_kd"):
         y = cn.conv3d(xg, wg, **case.conv_kwargs(), algo=algo)
         check_parity(gather_rows(y, rows), yr, den, x.dtype, f"{case.name}/{algo}")
         del y

@@ -249,16 +249,21 @@ def test_invalid_opts_and_groups():
 X3, W3 = (1, 41, 60, 104, 256), (256, 3, 3, 3, 256)
 
 
-def test_3d_video_shapes_take_the_native_gemm():
-    """bf16 video shapes pass the decomposition guard, but the per-frame 2D conv
-    would not take Winograd, so AUTO runs the native 3D GEMM (all taps in one K
-    loop); the decomposition stays available when forced."""
+def test_3d_video_shapes_take_the_half_winograd():
+    """bf16 video shapes: AUTO runs the half-precision Winograd path with the
+    depth taps summed in its GEMMs (rule 1b: KD C = 768 or 1536); the native 3D
+    GEMM and the decomposition stay available when forced."""
     for t, h, w, c, o in ((17, 64, 64, 256, 256), (41, 60, 104, 256, 256), (41, 120, 208, 512, 512)):
         p = cn.plan3d((1, t, h, w, c), (o, 3, 3, 3, c), 1, (0, 1, 1), 1, torch.bfloat16)
-        assert p.algo_name == "implicit_gemm" and p.out_d == t - 2
+        assert p.algo_name == "winograd_half" and p.out_d == t - 2 and p.n_tiles == 1
+        n = cn.plan3d((1, t, h, w, c), (o, 3, 3, 3, c), 1, (0, 1, 1), 1, torch.bfloat16, algo="implicit_gemm")
+        assert n.algo_name == "implicit_gemm"
         q = cn.plan3d((1, t, h, w, c), (o, 3, 3, 3, c), 1, (0, 1, 1), 1, torch.bfloat16, algo="small_kd")
         assert q.algo_name == "small_kd" and q.inner_algo_name in ("implicit_gemm", "unfold_gemm")
         assert q.workspace_bytes >= (t - 2) * h * w * o * 4  # fp32 accumulator
+    # channels too few for rule 1b (KD C = 192): the native 3D GEMM
+    p = cn.plan3d((1, 17, 64, 64, 64), (128, 3, 3, 3, 64), 1, (0, 1, 1), 1, torch.bfloat16)
+    assert p.algo_name == "implicit_gemm"
 
 
 def test_3d_fp32_decomposes_for_winograd():
@@ -267,9 +272,14 @@ def test_3d_fp32_decomposes_for_winograd():
     assert p.algo_name == "small_kd" and p.inner_algo_name == "winograd"
 
 
+# 32 channels: below rule 1b's KD C >= 384 for every change below, so the
+# decomposition guard alone decides.
+X3G, W3G = (1, 9, 20, 24, 32), (32, 3, 3, 3, 32)
+
+
 @pytest.mark.parametrize("change", ["n2", "kd9", "stride_d", "dil_h", "pad_d", "c_mod16", "o_mod16"])
 def test_3d_guard_each_clause(change):
-    xs, ws = list(X3), list(W3)
+    xs, ws = list(X3G), list(W3G)
     s, p, d = [1, 1, 1], [0, 1, 1], [1, 1, 1]
     if change == "n2":
         xs[0] = 2
@@ -282,9 +292,9 @@ def test_3d_guard_each_clause(change):
     elif change == "pad_d":
         p[0] = 1
     elif change == "c_mod16":
-        xs[-1] = ws[-1] = 250
+        xs[-1] = ws[-1] = 40
     elif change == "o_mod16":
-        ws[0] = 250
+        ws[0] = 40
     # what the guard rejects falls through to the native 3D GEMM
     assert cn.plan3d(tuple(xs), tuple(ws), s, p, d, torch.bfloat16).algo_name == "implicit_gemm"
     # a forced inner algorithm needs the decomposition, so it follows the guard
@@ -326,8 +336,9 @@ def test_large_half_convs_take_the_256_tile():
     small ones (a ResNet-50 batch-1 layer) and C % 32 != 0 do not."""
     big = cn.plan2d((64, 32, 32, 256), (4096, 3, 3, 256), 1, 1, 1, F16, algo="implicit_gemm")
     assert big.kernel_config == 14
-    big3 = cn.plan3d((1, 41, 120, 208, 512), (512, 3, 3, 3, 512), 1, (0, 1, 1), 1, torch.bfloat16)
-    assert big3.algo_name == "implicit_gemm" and big3.kernel_config == 14
+    big3 = cn.plan3d((1, 41, 120, 208, 512), (512, 3, 3, 3, 512), 1, (0, 1, 1), 1, torch.bfloat16,
+                     algo="implicit_gemm")
+    assert big3.kernel_config == 14
     small = cn.plan2d((1, 56, 56, 64), (64, 3, 3, 64), 1, 1, 1, F16)
     assert small.kernel_config != 14
     odd = cn.plan2d((64, 32, 32, 120), (4096, 3, 3, 120), 1, 1, 1, F16, algo="implicit_gemm")
@@ -440,10 +451,44 @@ def test_winograd_half_geometry_gate():
     assert cn.plan2d(xs, (64, 3, 3, 64), 1, 0, 1, F16, algo="winograd_half").algo_name == "winograd_half"
 
 
-def test_winograd_half_not_taken_by_auto_yet():
+@pytest.mark.parametrize("xs,ws,pad,expect", [
+    ((16, 32, 32, 512), (512, 3, 3, 512), 1, True),     # 1024 GEMM rows, C O = 16.5 (11C + 20O)
+    ((16, 32, 32, 512), (320, 3, 3, 512), 1, True),     # C O = 13.6 (11C + 20O)
+    ((8, 56, 56, 512), (256, 3, 3, 512), 1, False),     # C O = 12.2 (11C + 20O)
+    ((16, 28, 28, 384), (384, 3, 3, 384), 1, False),    # C O = 12.4 (11C + 20O)
+    ((8, 56, 56, 256), (512, 3, 3, 256), 1, False),     # C = 256 < 384
+    ((64, 32, 32, 256), (4096, 3, 3, 256), 1, False),   # C = 256
+    ((8, 32, 32, 1024), (4096, 3, 3, 1024), 1, True),   # 512 GEMM rows
+    ((8, 14, 14, 512), (512, 3, 3, 512), 1, False),     # 128 GEMM rows
+    ((32, 14, 14, 512), (512, 3, 3, 512), 1, True),     # 512 GEMM rows
+    ((8, 56, 56, 512), (512, 3, 3, 512), 0, True),
+    ((8, 56, 56, 512), (512, 3, 3, 512), 2, False),     # padding 2: not for this path
+])
+def test_winograd_half_auto_rule(xs, ws, pad, expect):
     for dt in (F16, BF16):
-        p = cn.plan2d((8, 64, 64, 512), (512, 3, 3, 512), 1, 1, 1, dt)
-        assert p.algo_name == "implicit_gemm"
+        p = cn.plan2d(xs, ws, 1, pad, 1, dt)
+        assert (p.algo_name == "winograd_half") == expect, (xs, ws, dt, p.algo_name)
+        if not expect:
+            assert p.algo_name == "implicit_gemm"
+    assert cn.plan2d(xs, ws, 1, pad, 1, torch.float32).algo_name != "winograd_half"
+
+
+def test_winograd_half_auto_falls_back_over_budget():
+    xs, ws = (16, 32, 32, 512), (512, 3, 3, 512)
+    assert cn.plan2d(xs, ws, 1, 1, 1, F16, ws_limit=10**6).algo_name == "implicit_gemm"
+
+
+def test_winograd_half_gemm_tile_choice():
+    """K <= 1152 and O <= 512: the 256x128 tile at two workgroups per CU;
+    otherwise the occupancy model (the 256x256 tile on these shapes)."""
+    assert cn.plan2d((16, 32, 32, 512), (512, 3, 3, 512), 1, 1, 1, F16).kernel_config == 15
+    assert cn.plan2d((16, 32, 32, 1024), (512, 3, 3, 1024), 1, 1, 1, F16).kernel_config == 15
+    assert cn.plan2d((16, 32, 32, 512), (1024, 3, 3, 512), 1, 1, 1, F16).kernel_config == 14
+    assert cn.plan2d((16, 32, 32, 2048), (512, 3, 3, 2048), 1, 1, 1, F16).kernel_config == 14
+    v = cn.plan3d((1, 41, 120, 208, 512), (512, 3, 3, 3, 512), 1, (0, 1, 1), 1, BF16)   # K = 1536
+    assert v.algo_name == "winograd_half" and v.kernel_config == 14
+    v = cn.plan3d((1, 41, 60, 104, 256), (256, 3, 3, 3, 256), 1, (0, 1, 1), 1, BF16)    # K = 768
+    assert v.kernel_config == 15
 
 
 def test_winograd_half_budget_tiles_and_over_budget():
