@@ -59,7 +59,7 @@ def parse():
                          "with --calib-copy, write profiles/traffic.json, print it and exit")
     ap.add_argument("--suite", default=None,
                     help="instead of the headline line, time other workloads: "
-                         "comma list of small,wide,sweep,wino_half,resnet,video,conv1d or 'all' "
+                         "comma list of small,wide,sweep,wino_half,resnet,video,video_auto,conv1d or 'all' "
                          "(one JSON line each)")
     return ap.parse_args()
 
@@ -341,6 +341,12 @@ def run_suite(names):
                 r = measure(case, algo, inner=inner)
                 r["suite"] = "video3d"
                 emit(r)
+    if "video_auto" in names:
+        # the AUTO path alone (half-precision Winograd) on the video shapes, for profiles
+        for shape in cw.VIDEO3D_SHAPES:
+            r = measure(cw.video3d(*shape))
+            r["suite"] = "video3d_auto"
+            emit(r)
     if "wino_half" in names:
         # half-precision Winograd F(4x4,3x3) against the implicit GEMM around
         # AUTO's crossover (3x3 s1 p1 on 32x32)

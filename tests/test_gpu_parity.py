@@ -394,9 +394,9 @@ def test_graph_capture_replays_bit_identical():
 # ------------------------------- half-precision Winograd F(4x4,3x3)
 
 # (name, n, h, w, c, o, pad, dtype, gemm tile): ragged 4x4 output tiles, odd
-# channel counts (one channel per thread, padded K), padding 0, the fewest
-# channels the path takes (16), and a case spanning several 256-row GEMM
-# tiles with ragged rows and columns.
+# channel counts (one channel per thread, padded K), C = 2 mod 4 (two per
+# thread), padding 0, the fewest channels the path takes (16), and a case
+# spanning several 256-row GEMM tiles with ragged rows and columns.
 WH2D_CASES = [
     ("ragged_f16", 3, 21, 19, 64, 96, 1, "f16", 0),
     ("ragged_bf16", 3, 21, 19, 64, 96, 1, "bf16", 0),
@@ -404,6 +404,7 @@ WH2D_CASES = [
     ("odd_channels_bf16", 2, 13, 15, 37, 45, 1, "bf16", 0),
     ("pad0_bf16", 2, 18, 18, 128, 64, 0, "bf16", 0),
     ("c16_f16", 2, 30, 30, 16, 32, 1, "f16", 0),
+    ("c50_bf16", 2, 17, 19, 50, 40, 1, "bf16", 0),
     ("tiles_f16", 4, 64, 60, 256, 320, 1, "f16", 14),
     ("tiles_bf16", 4, 64, 60, 256, 320, 1, "bf16", 15),
 ]
