@@ -64,14 +64,19 @@ def parse():
     return ap.parse_args()
 
 
+# The sources the headline workload's kernels (the fp32 Winograd transforms and
+# the resident Winograd GEMM) are compiled from, headers included.
+HEADLINE_SOURCES = ("winograd.hip", "wino_gemm.hip", "device_common.hpp", "internal.hpp", "winograd_f63.h")
+
+
 def csrc_hash():
-    """Hash of the kernel sources (decides whether stored traffic counters still apply)."""
+    """Hash of the headline kernels' sources (decides whether stored traffic
+    counters still apply: a change to any of them voids the counters)."""
     h = hashlib.sha256()
     d = os.path.join(ROOT, "convolution_nhwc_conv2d_amd", "csrc")
-    for f in sorted(os.listdir(d)):
-        if f.endswith((".hip", ".hpp", ".h", ".cpp")):
-            h.update(f.encode())
-            h.update(open(os.path.join(d, f), "rb").read())
+    for f in HEADLINE_SOURCES:
+        h.update(f.encode())
+        h.update(open(os.path.join(d, f), "rb").read())
     return h.hexdigest()[:16]
 
 
