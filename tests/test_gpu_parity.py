@@ -350,13 +350,18 @@ def test_conv1d_parity(spec):
 # Each replay must give the eager bits; eager work runs between replays.
 
 def test_graph_capture_replays_bit_identical():
-    cases = [  # (fn, case, kwargs): split-K implicit GEMM, native 3D, Winograd
+    cases = [  # (fn, case, kwargs): split-K implicit GEMM, native 3D, Winograd, half Winograd 2D/3D
         (cn.conv2d, cw.ConvCase("g_l4", 1, 7, 7, 512, 512, 3, 3, (1, 1), (1, 1), (1, 1), "f16",
                                 "normal", "normal", None, 61, 1), {}),
         (cn.conv3d, cw.ConvCase("g_3d", 2, 8, 9, 64, 48, 3, 3, (1, 1, 1), (1, 1, 1), (1, 1, 1), "bf16",
                                 "normal", "normal", None, 62, 2, nd=3, d=5, kd=3), {}),
         (cn.conv2d, cw.ConvCase("g_wino", 2, 30, 30, 64, 64, 3, 3, (1, 1), (1, 1), (1, 1), "f32",
                                 "uniform", "normal", None, 63, 3), {"algo": "winograd"}),
+        (cn.conv2d, cw.ConvCase("g_wino_half", 2, 30, 30, 64, 64, 3, 3, (1, 1), (1, 1), (1, 1), "f16",
+                                "normal", "normal", None, 64, 4), {"algo": "winograd_half"}),
+        (cn.conv3d, cw.ConvCase("g_wino_half_3d", 1, 12, 14, 64, 48, 3, 3, (1, 1, 1), (1, 1, 1), (1, 1, 1),
+                                "bf16", "normal", "normal", None, 65, 5, nd=3, d=6, kd=3),
+         {"algo": "winograd_half"}),
     ]
     runs = []
     for fn, case, kw in cases:
@@ -488,6 +493,27 @@ def test_winograd_half_3d_parity(spec):
     y = cn.conv3d(_dev(x), _dev(wt), **case.conv_kwargs(), algo="winograd_half", out=poisoned(yr.shape, x.dtype))
     err = check_parity(y.cpu(), yr, den, y.dtype, case.name)
     assert err < WH_BOUND[y.dtype], err
+
+
+def test_winograd_half_scales_follow_the_data():
+    """One workspace, inputs of very different magnitudes in turn: each call
+    picks its own scales (nothing carries over), so each result equals a fresh
+    run's bits and scales with the input exactly."""
+    case = cw.ConvCase("wh_rescale", 2, 20, 22, 64, 48, 3, 3, (1, 1), (1, 1), (1, 1), "bf16", "normal", "normal",
+                       None, 66, 0)
+    x, w = _dev(case.input()), _dev(case.weight())
+    plan = cn.plan2d(tuple(x.shape), tuple(w.shape), 1, 1, 1, torch.bfloat16, algo="winograd_half")
+    ws = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device="cuda")
+    outs = {}
+    for scale in (2.0 ** 40, 1.0, 2.0 ** -40, 1.0):
+        xs = x * scale  # exact: a power of two
+        y = cn.conv2d(xs, w, 1, 1, 1, plan=plan, workspace=ws)
+        fresh = cn.conv2d(xs, w, 1, 1, 1, algo="winograd_half")
+        assert torch.equal(bits(y), bits(fresh)), scale
+        outs[scale] = y
+    # power-of-two input scales move only the scale exponents: the same bits, rescaled
+    assert torch.equal(bits(outs[2.0 ** 40] * 2.0 ** -40), bits(outs[1.0]))
+    assert torch.equal(bits(outs[2.0 ** -40] * 2.0 ** 40), bits(outs[1.0]))
 
 
 def test_winograd_half_3d_kd1_bit_identical_to_conv2d():
