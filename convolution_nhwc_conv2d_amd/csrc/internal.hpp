@@ -165,8 +165,8 @@ int wino_output_launch(int dtype, const float* m, int64_t plane, int64_t nb, int
 
 // Half-precision Winograd F(4x4,3x3) (fp16/bf16 x and w).
 // partial[t][b] = largest |element| bits of block b of tensor t (0: x of nx
-// elements, 1: w of nw), then scales = {sx, sw, 1/sx, 1/sw} (after the
-// partial maxima in the workspace head).
+// elements, 1: w of nw), then scales = {sx, sw, a, b} with a b = 1/(sx sw)
+// (after the partial maxima in the workspace head).
 int wino_h_absmax_launch(int dtype, const void* x, int64_t nx, const void* w, int64_t nw,
                          uint32_t* partial, void* stream);
 int wino_h_scale_launch(int dtype, const uint32_t* partial, int64_t nx, int64_t nw, float* scales,
@@ -180,7 +180,7 @@ int wino_h_input_launch(int dtype, const void* x, int64_t nb, int64_t d, int64_t
                         int64_t h, int64_t w, int64_t c, int64_t cs, int32_t ph, int32_t pw,
                         int64_t th, int64_t tw, const float* scales, uint16_t* v, int64_t plane,
                         void* stream);
-// y = ((A^T M A) / sx) / sw per tile and output channel for nimg output images
+// y = (A^T M A) / (sx sw) per tile and output channel for nimg output images
 // (or frames), cropped to [oh, ow].
 int wino_h_output_launch(int dtype, const float* m, int64_t plane, int64_t nimg, int64_t oh,
                          int64_t ow, int64_t o, int64_t th, int64_t tw, const float* scales,

@@ -15,7 +15,7 @@
 // and fp32 M stays well inside it.  fp16's range is the risk: |B^T d B| can
 // reach 100 max|d|.  So the transformed operands are scaled by powers of two
 // picked on the device from max|x| and max|w| (kWino4VBound, kWino4UBound):
-//   V = fp16(sx * B^T d B),  U = fp16(sw * G g G^T),  y = (A^T M A) / (sx sw)
+//   V = fp16(B^T (sx d) B),  U = fp16(G (sw g) G^T),  y = (A^T M A) / (sx sw)
 // with sx * 100 max|x| < 2^15 and sw * max|g| < 2^15, so no transformed value
 // can overflow, for any finite input (bf16 inputs included), and the largest
 // ones use fp16's top binade.  Scaling by a power of two is exact: it changes
@@ -23,7 +23,8 @@
 // come from the whole x and w before the batch loop, so batch tiles see the
 // same scales and tiled runs keep the untiled bits.
 //
-// Workspace (elements): partial maxima, then the scales {sx, sw, 1/sx, 1/sw},
+// Workspace (elements): partial maxima, then the scales {sx, sw} and 1/(sx sw)
+// as two powers of two,
 //   U [36][O][KD*Cs]    fp16, Cs = C rounded up to 32 (zero channels)
 //   V [36][rows][Cs]    fp16, rows = (image or frame) * tiles, frames padded by pd
 //   M [36][rows'][O]    fp32, rows' = output images or frames * tiles
@@ -128,12 +129,16 @@ __global__ __launch_bounds__(256) void wino_h_scale_kernel(const uint32_t* __res
     const int ew = scale_exp(abs_bits_to_f32<BF16>(mw), kWino4UBound);
     scales[0] = ldexpf(1.0f, ex);
     scales[1] = ldexpf(1.0f, ew);
-    scales[2] = ldexpf(1.0f, -ex);  // undone in two exact steps: 2^-(ex+ew) may not be an fp32
-    scales[3] = ldexpf(1.0f, -ew);
+    // 2^-(ex+ew) is undone in two halves (it may not be an fp32 itself); each
+    // intermediate lies between the GEMM's fp32 result and the final value,
+    // so it overflows only if y does
+    const int et = -(ex + ew), eh = et / 2;
+    scales[2] = ldexpf(1.0f, eh);
+    scales[3] = ldexpf(1.0f, et - eh);
   }
 }
 
-// U[p][o][kd*Cs + c] = fp16(sw * (G g G^T)_p), g = w[o][kd][.][.][c]; zero for c >= C.
+// U[p][o][kd*Cs + c] = fp16((G (sw g) G^T)_p), g = w[o][kd][.][.][c]; zero for c >= C.
 template <bool BF16>
 __global__ __launch_bounds__(256) void wino_h_filter_kernel(const uint16_t* __restrict__ w,
                                                             int64_t O, int64_t KD, int64_t C,
@@ -146,11 +151,13 @@ __global__ __launch_bounds__(256) void wino_h_filter_kernel(const uint16_t* __re
   const int64_t o = t / ku, r = t - o * ku;
   const int64_t kd = r / Cs, c = r - kd * Cs;
   const uint16_t* __restrict__ g0 = w + (o * KD + kd) * 9 * C + c;
+  // scaled as it is loaded (exact): the fp32 transform then stays below 2^15
+  const float s = scales[1];
   float g[3][3];
 #pragma unroll
   for (int a = 0; a < 3; ++a)
 #pragma unroll
-    for (int b = 0; b < 3; ++b) g[a][b] = c < C ? to_f32<uint16_t, BF16>(g0[(a * 3 + b) * C]) : 0.0f;
+    for (int b = 0; b < 3; ++b) g[a][b] = c < C ? s * to_f32<uint16_t, BF16>(g0[(a * 3 + b) * C]) : 0.0f;
   float t1[kT][3];  // G g
 #pragma unroll
   for (int b = 0; b < 3; ++b) {
@@ -160,7 +167,6 @@ __global__ __launch_bounds__(256) void wino_h_filter_kernel(const uint16_t* __re
 #pragma unroll
     for (int i = 0; i < kT; ++i) t1[i][b] = res[i];
   }
-  const float s = scales[1];
   const int64_t plane = O * ku;
   uint16_t* __restrict__ out = U + o * ku + r;
 #pragma unroll
@@ -169,11 +175,11 @@ __global__ __launch_bounds__(256) void wino_h_filter_kernel(const uint16_t* __re
     float res[kT];
     cmatvec(kWino4G, row, res);  // (t1 G^T)[i][j]
 #pragma unroll
-    for (int j = 0; j < kT; ++j) out[(i * kT + j) * plane] = f32_to_f16_bits(s * res[j]);
+    for (int j = 0; j < kT; ++j) out[(i * kT + j) * plane] = f32_to_f16_bits(res[j]);
   }
 }
 
-// V[p][r][c] = fp16(sx * (B^T d B)_p) for tile row r = (image, ty, tx).  Images
+// V[p][r][c] = fp16((B^T (sx d) B)_p) for tile row r = (image, ty, tx).  Images
 // are the frames fp of nb elements with Dp frames each; frame fp reads input
 // frame fp - pd (zero outside [0, D)); 2D convs have D = Dp = 1, pd = 0.
 // VEC channels per thread (4 when C % 4 == 0, 2 when C is even: 8- or 4-byte
@@ -195,6 +201,9 @@ __global__ __launch_bounds__(256) void wino_h_input_kernel(
   const int64_t ih0 = ty * kWinoHM - ph, iw0 = tx * kWinoHM - pw;
   const uint16_t* __restrict__ img = x + (n * D + (fok ? f : 0)) * H * W * C + c;
   const bool cin = fok && c < C;  // VEC > 1 only for C % VEC == 0: c < C implies c + VEC - 1 < C
+  // Inputs are scaled as they are loaded (exact), so the fp32 transform stays
+  // below 2^15 even where 100 max|x| would overflow fp32 (bf16 inputs).
+  const float s = scales[0];
   // column transform first: t1[v][a][j] = sum_i BT[a][i] d[i][j]
   float t1[VEC][kT][kT];
 #pragma unroll
@@ -208,16 +217,16 @@ __global__ __launch_bounds__(256) void wino_h_input_kernel(
       const bool ok = wok && ih >= 0 && ih < H;
       if constexpr (VEC == 4) {
         const uint2 q = ok ? *reinterpret_cast<const uint2*>(img + (ih * W + iw) * C) : make_uint2(0u, 0u);
-        col[0][i] = to_f32<uint16_t, BF16>(uint16_t(q.x & 0xffffu));
-        col[1][i] = to_f32<uint16_t, BF16>(uint16_t(q.x >> 16));
-        col[2][i] = to_f32<uint16_t, BF16>(uint16_t(q.y & 0xffffu));
-        col[3][i] = to_f32<uint16_t, BF16>(uint16_t(q.y >> 16));
+        col[0][i] = s * to_f32<uint16_t, BF16>(uint16_t(q.x & 0xffffu));
+        col[1][i] = s * to_f32<uint16_t, BF16>(uint16_t(q.x >> 16));
+        col[2][i] = s * to_f32<uint16_t, BF16>(uint16_t(q.y & 0xffffu));
+        col[3][i] = s * to_f32<uint16_t, BF16>(uint16_t(q.y >> 16));
       } else if constexpr (VEC == 2) {
         const uint32_t q = ok ? *reinterpret_cast<const uint32_t*>(img + (ih * W + iw) * C) : 0u;
-        col[0][i] = to_f32<uint16_t, BF16>(uint16_t(q & 0xffffu));
-        col[1][i] = to_f32<uint16_t, BF16>(uint16_t(q >> 16));
+        col[0][i] = s * to_f32<uint16_t, BF16>(uint16_t(q & 0xffffu));
+        col[1][i] = s * to_f32<uint16_t, BF16>(uint16_t(q >> 16));
       } else {
-        col[0][i] = ok ? to_f32<uint16_t, BF16>(img[(ih * W + iw) * C]) : 0.0f;
+        col[0][i] = ok ? s * to_f32<uint16_t, BF16>(img[(ih * W + iw) * C]) : 0.0f;
       }
     }
 #pragma unroll
@@ -228,8 +237,7 @@ __global__ __launch_bounds__(256) void wino_h_input_kernel(
       for (int a = 0; a < kT; ++a) t1[v][a][j] = res[a];
     }
   }
-  // row transform: v[a][b] = sum_j t1[a][j] BT[b][j], scaled, rounded to fp16
-  const float s = scales[0];
+  // row transform: v[a][b] = sum_j t1[a][j] BT[b][j], rounded to fp16
   uint16_t* __restrict__ out = V + r * Cs + c;
 #pragma unroll
   for (int a = 0; a < kT; ++a) {
@@ -239,23 +247,23 @@ __global__ __launch_bounds__(256) void wino_h_input_kernel(
 #pragma unroll
     for (int b = 0; b < kT; ++b) {
       if constexpr (VEC == 4) {
-        const uint2 q = make_uint2(uint32_t(f32_to_f16_bits(s * res[0][b])) |
-                                       (uint32_t(f32_to_f16_bits(s * res[1][b])) << 16),
-                                   uint32_t(f32_to_f16_bits(s * res[2][b])) |
-                                       (uint32_t(f32_to_f16_bits(s * res[3][b])) << 16));
+        const uint2 q = make_uint2(uint32_t(f32_to_f16_bits(res[0][b])) |
+                                       (uint32_t(f32_to_f16_bits(res[1][b])) << 16),
+                                   uint32_t(f32_to_f16_bits(res[2][b])) |
+                                       (uint32_t(f32_to_f16_bits(res[3][b])) << 16));
         *reinterpret_cast<uint2*>(out + (a * kT + b) * plane) = q;
       } else if constexpr (VEC == 2) {
-        const uint32_t q = uint32_t(f32_to_f16_bits(s * res[0][b])) |
-                           (uint32_t(f32_to_f16_bits(s * res[1][b])) << 16);
+        const uint32_t q = uint32_t(f32_to_f16_bits(res[0][b])) |
+                           (uint32_t(f32_to_f16_bits(res[1][b])) << 16);
         *reinterpret_cast<uint32_t*>(out + (a * kT + b) * plane) = q;
       } else {
-        out[(a * kT + b) * plane] = f32_to_f16_bits(s * res[0][b]);
+        out[(a * kT + b) * plane] = f32_to_f16_bits(res[0][b]);
       }
     }
   }
 }
 
-// y[im][oh][ow][o] = ((A^T M A)[oh - 4 ty][ow - 4 tx] / sx) / sw, cropped to
+// y[im][oh][ow][o] = (A^T M A)[oh - 4 ty][ow - 4 tx] / (sx sw), cropped to
 // [OH, OW], for output image or frame im.  VEC output channels per thread
 // (2 when O is even).
 template <bool BF16, int VEC>
@@ -297,7 +305,7 @@ __global__ __launch_bounds__(256) void wino_h_output_kernel(const float* __restr
       for (int i = 0; i < kWinoHM; ++i) t1[v][i][b] = res[i];
     }
   }
-  const float inv_x = scales[2], inv_w = scales[3];
+  const float inv_a = scales[2], inv_b = scales[3];
 #pragma unroll
   for (int i = 0; i < kWinoHM; ++i) {
     const int64_t oh = ty * kWinoHM + i;
@@ -306,7 +314,7 @@ __global__ __launch_bounds__(256) void wino_h_output_kernel(const float* __restr
     for (int v = 0; v < VEC; ++v) {
       cmatvec(kWino4AT, t1[v][i], res[v]);  // Y[i][j]
 #pragma unroll
-      for (int j = 0; j < kWinoHM; ++j) res[v][j] = (res[v][j] * inv_x) * inv_w;  // exact
+      for (int j = 0; j < kWinoHM; ++j) res[v][j] = (res[v][j] * inv_a) * inv_b;  // exact
     }
     if (oh < OH) {
 #pragma unroll

@@ -452,13 +452,14 @@ def test_winograd_half_tiled_bit_identical_to_untiled(tile):
     assert torch.equal(bits(tiled), bits(full))
 
 
-@pytest.mark.parametrize("dt,scale", [("f16", 6.0e4), ("f16", 1.0e-3), ("bf16", 1.0e30), ("bf16", 1.0e-30),
-                                      ("f16", 0.0)])
+@pytest.mark.parametrize("dt,scale", [("f16", 6.0e4), ("f16", 1.0e-3), ("bf16", 1.0e30), ("bf16", 1.0e37),
+                                      ("bf16", 1.0e-30), ("f16", 0.0)])
 def test_winograd_half_input_range(dt, scale):
     """Inputs near the top of fp16's range (|B^T d B| would reach 6e6 unscaled),
-    far outside it (bf16), tiny, and all zero: the power-of-two scales keep
-    every transformed value finite and the result within tolerance.  The
-    weights are small enough (std 0.1/sqrt(K)) that y itself stays in fp16."""
+    far outside it (bf16; at 1e37 even the fp32 transform of unscaled inputs
+    would overflow), tiny, and all zero: the power-of-two scales keep every
+    transformed value finite and the result within tolerance.  The weights are
+    small enough (std 0.1/sqrt(K)) that y itself stays in fp16."""
     case = cw.ConvCase(f"wh_range_{dt}", 2, 14, 13, 64, 40, 3, 3, (1, 1), (1, 1), (1, 1), dt, "uniform", "normal",
                        0.1 / (9 * 64) ** 0.5, 63, 0)
     x = (case.input().float() * scale).to(cw.DTYPES[dt])
