@@ -24,6 +24,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -69,14 +70,22 @@ def parse():
 HEADLINE_SOURCES = ("winograd.hip", "wino_gemm.hip", "device_common.hpp", "internal.hpp", "winograd_f63.h")
 
 
+def _code_only(text):
+    """Source text without comments and with whitespace runs collapsed."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def csrc_hash():
-    """Hash of the headline kernels' sources (decides whether stored traffic
-    counters still apply: a change to any of them voids the counters)."""
+    """Hash of the headline kernels' sources, comments and layout aside
+    (decides whether stored traffic counters still apply: a change to the code
+    of any of them voids the counters)."""
     h = hashlib.sha256()
     d = os.path.join(ROOT, "convolution_nhwc_conv2d_amd", "csrc")
     for f in HEADLINE_SOURCES:
         h.update(f.encode())
-        h.update(open(os.path.join(d, f), "rb").read())
+        h.update(_code_only(open(os.path.join(d, f)).read()).encode())
     return h.hexdigest()[:16]
 
 
