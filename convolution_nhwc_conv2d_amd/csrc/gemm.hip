@@ -222,23 +222,33 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_kernel(const GemmParams p) {
           for (int t = 0; t < VE; ++t)
             e[t] = (a_off[j] >= 0 && kk + t < K) ? A[a_off[j] + kk + t] : E(0);
         } else {
+          // the vector's first (kd, kh, kw, c) from one division chain, the rest walked
+          const int64_t tap0 = kk / p.c;
+          const int64_t t2 = tap0 / p.kw;
+          int64_t c = kk - tap0 * p.c;
+          int64_t kw = tap0 - t2 * p.kw;
+          int64_t kd = D3 ? t2 / p.kh : 0;
+          int64_t kh = t2 - kd * p.kh;
 #pragma unroll
           for (int t = 0; t < VE; ++t) {
             e[t] = E(0);
-            const int64_t k = kk + t;
-            if (k < K) {
-              const int64_t tap = k / p.c;
-              const int64_t c = k - tap * p.c;
-              const int64_t t2 = tap / p.kw;
-              const int64_t kw = tap - t2 * p.kw;
-              const int64_t kd = D3 ? t2 / p.kh : 0;
-              const int64_t kh = t2 - kd * p.kh;
+            if (kk + t < K) {
               const int64_t dd_ = kd * p.dd, dh_ = kh * p.dh, dw_ = kw * p.dw;
               const int64_t id = a_id0[j] + dd_;
               const int64_t ih = a_ih0[j] + dh_;
               const int64_t iw = a_iw0[j] + dw_;
               if ((!D3 || (id >= 0 && id < p.d)) && ih >= 0 && ih < p.h && iw >= 0 && iw < p.w)
                 e[t] = A[a_off[j] + ((dd_ * p.h + dh_) * p.w + dw_) * p.c + c];
+            }
+            if (++c == p.c) {
+              c = 0;
+              if (++kw == p.kw) {
+                kw = 0;
+                if (++kh == p.kh) {
+                  kh = 0;
+                  ++kd;
+                }
+              }
             }
           }
         }

@@ -49,26 +49,45 @@ __global__ __launch_bounds__(256) void unfold_vec_kernel(const E* __restrict__ x
   *reinterpret_cast<uint4*>(buf + r * g.kp + k) = val;
 }
 
-// One element per thread (any C).
+// One 16-byte vector of a row per thread for any C (C % VE != 0, e.g. the
+// 3-channel stem): the (tap, channel) of the vector's first element comes from
+// one division chain, the rest are walked from it; the elements are gathered
+// one by one and stored as one vector.
 template <typename E>
-__global__ __launch_bounds__(256) void unfold_scalar_kernel(const E* __restrict__ x, UnfoldGeo g,
+__global__ __launch_bounds__(256) void unfold_gather_kernel(const E* __restrict__ x, UnfoldGeo g,
                                                             E* __restrict__ buf, int64_t total) {
+  constexpr int VE = 16 / sizeof(E);
   const int64_t t = int64_t(blockIdx.x) * 256 + threadIdx.x;
   if (t >= total) return;
-  const int64_t r = t / g.kp, k = t - r * g.kp;
+  const int64_t nv = g.kp / VE;
+  const int64_t r = t / nv, v = t - r * nv;
+  const int64_t k0 = v * VE;
   const int64_t m = g.m0 + r;
   const int64_t hw = g.oh * g.ow;
   const int64_t n = m / hw, rem = m - n * hw;
   const int64_t oh = rem / g.ow, ow = rem - oh * g.ow;
-  const int64_t tap = k / g.c, c = k - tap * g.c;
-  E val = E(0);
-  if (tap < g.kh * g.kw) {
-    const int64_t a = tap / g.kw, b = tap - a * g.kw;
-    const int64_t ih = oh * g.sh - g.ph + a * g.dh;
-    const int64_t iw = ow * g.sw - g.pw + b * g.dw;
-    if (ih >= 0 && ih < g.h && iw >= 0 && iw < g.w) val = x[((n * g.h + ih) * g.w + iw) * g.c + c];
+  const int64_t ih0 = oh * g.sh - g.ph, iw0 = ow * g.sw - g.pw;
+  const E* __restrict__ xn = x + n * g.h * g.w * g.c;
+  int64_t tap = k0 / g.c, c = k0 - tap * g.c;
+  int64_t a = tap / g.kw, b = tap - a * g.kw;  // a >= kh: past K (pad columns)
+  E e[VE];
+#pragma unroll
+  for (int i = 0; i < VE; ++i) {
+    E val = E(0);
+    if (a < g.kh) {
+      const int64_t ih = ih0 + a * g.dh, iw = iw0 + b * g.dw;
+      if (ih >= 0 && ih < g.h && iw >= 0 && iw < g.w) val = xn[(ih * g.w + iw) * g.c + c];
+    }
+    e[i] = val;
+    if (++c == g.c) {
+      c = 0;
+      if (++b == g.kw) {
+        b = 0;
+        ++a;
+      }
+    }
   }
-  buf[r * g.kp + k] = val;
+  *reinterpret_cast<uint4*>(buf + r * g.kp + k0) = *reinterpret_cast<const uint4*>(e);
 }
 
 template <typename E>
@@ -79,8 +98,8 @@ hipError_t launch_unfold_t(const void* x, const UnfoldGeo& g, void* buf, hipStre
     hipLaunchKernelGGL((unfold_vec_kernel<E>), dim3(unsigned((total + 255) / 256)), dim3(256), 0, s,
                        static_cast<const E*>(x), g, static_cast<E*>(buf), total);
   } else {
-    const int64_t total = g.rows * g.kp;
-    hipLaunchKernelGGL((unfold_scalar_kernel<E>), dim3(unsigned((total + 255) / 256)), dim3(256), 0,
+    const int64_t total = g.rows * (g.kp / VE);
+    hipLaunchKernelGGL((unfold_gather_kernel<E>), dim3(unsigned((total + 255) / 256)), dim3(256), 0,
                        s, static_cast<const E*>(x), g, static_cast<E*>(buf), total);
   }
   return hipGetLastError();

@@ -72,7 +72,8 @@ extern "C" {
  * and only for half precision).  On MI355X the measured sweep (C_out 128..4096,
  * M = 1024..65536, K = 1152..9216, fp16 and bf16) never shows unfold+GEMM
  * ahead of the implicit GEMM beyond noise, so the threshold is out of reach:
- * AUTO never unfolds, and CNHWC_ALGO_UNFOLD_GEMM stays available when forced. */
+ * AUTO does not unfold wide convs (it still unfolds convs with C % 8 != 0, see
+ * cnhwc_conv_select), and CNHWC_ALGO_UNFOLD_GEMM stays available when forced. */
 #define CNHWC_UNFOLD_MIN_COUT (1 << 30)
 
 typedef enum { CNHWC_F32 = 0, CNHWC_F16 = 1, CNHWC_BF16 = 2 } cnhwc_dtype_t;
@@ -175,7 +176,12 @@ const char* cnhwc_status_string(cnhwc_status_t s);
  *     N * OD * ceil(OH/4) * ceil(OW/4) >= 512 (KD = OD = 1 in 2D), under the
  *     same budget rule: the measured crossover against the implicit GEMM on
  *     MI355X (the tiling page runs its Winograd path for half precision too).
- *  2. Unfold + GEMM for F16/BF16 with O >= CNHWC_UNFOLD_MIN_COUT.
+ *  2. Unfold + GEMM for F16/BF16 with O >= CNHWC_UNFOLD_MIN_COUT, or with
+ *     C % 8 != 0: the implicit GEMM would then gather its A operand element by
+ *     element for every column tile, while the unfold gathers once and the GEMM
+ *     reads dense 16-byte rows (measured 1.3-1.9x faster on such convs above
+ *     the ~20 us launch floor, e.g. the 3-channel stem; at the floor within a
+ *     few microseconds either way).
  *  3. Implicit GEMM.
  * AUTO, 3D: first WINOGRAD_HALF under rule 1b (the depth taps summed in its
  *   GEMMs).  Then (3D page, Change): SMALL_KD when N == 1, KD <= 7, depth stride 1,

@@ -62,6 +62,21 @@ def test_half_geometry_grid(dtype, c_in):
             check_parity(y.cpu(), yr, den, y.dtype, f"{case.name}/{algo}")
 
 
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("c_in,k,s,p", [(3, 7, 2, 3), (5, 3, 1, 1), (3, 3, 2, 0)])
+def test_half_small_channels(dtype, c_in, k, s, p):
+    """Channel counts below one 16-byte vector (the 3-channel stem): the
+    implicit GEMM and the unfold gather element by element."""
+    h = 30
+    case = cw.ConvCase(f"small_c{c_in}_k{k}s{s}p{p}_{dtype}", 2, h, h + 3, c_in, 40, k, k, (s, s), (p, p), (1, 1),
+                       dtype, "normal", "normal", None, 12, c_in * 10 + k)
+    x, w = case.input(), case.weight()
+    yr, den = oracle.conv(to_oracle(x), to_oracle(w), **case.conv_kwargs())
+    for algo in ("implicit_gemm", "unfold_gemm", "auto"):
+        y = cn.conv2d(_dev(x), _dev(w), **case.conv_kwargs(), algo=algo)
+        check_parity(y.cpu(), yr, den, y.dtype, f"{case.name}/{algo}")
+
+
 @pytest.mark.parametrize("k,s,d,p", [(3, 1, 1, 1), (5, 2, 1, 2), (7, 2, 2, 0), (1, 2, 1, 0), (3, 2, 2, 2)])
 def test_fp32_geometry(k, s, d, p):
     h = (16 - 1) * s + d * (k - 1) + 1 - 2 * p

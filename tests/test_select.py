@@ -537,3 +537,14 @@ def test_winograd_half_3d_plan():
     with pytest.raises(cn.CnhwcError) as e:
         cn.plan3d((1,) + xs[1:], ws, 1, (0, 1, 1), 1, BF16, inner_algo="winograd_half")
     assert e.value.name == "INVALID_ARGUMENT"
+
+
+def test_small_channel_half_convs_unfold():
+    """fp16/bf16 convs with C % 8 != 0 (element-by-element implicit gather) take
+    unfold + GEMM under AUTO; fp32 and C % 8 == 0 keep the implicit GEMM."""
+    stem = ((8, 224, 224, 3), (64, 7, 7, 3), 2, 3, 1)
+    for dt in (F16, BF16):
+        assert cn.plan2d(*stem, dt).algo_name == "unfold_gemm"
+        assert cn.plan2d((8, 56, 56, 12), (64, 3, 3, 12), 1, 1, 1, dt).algo_name == "unfold_gemm"
+        assert cn.plan2d((8, 56, 56, 16), (64, 3, 3, 16), 1, 1, 1, dt).algo_name == "implicit_gemm"
+    assert cn.plan2d(*stem, torch.float32).algo_name == "implicit_gemm"
