@@ -160,7 +160,9 @@ def cpu_baseline(case, seconds):
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"{count} seeded output pixels (x {case.o} channels) of batch elements 0..{elems - 1}, "
                       f"fp64 direct correlation, {dt:.2f} s wall; CPU {cpu}",
-            "seconds": dt, "outputs_per_s": count * case.o / dt}
+            "seconds": dt, "outputs_per_s": count * case.o / dt,
+            # extrapolated, not measured: the sample's rate over all case.n * OH * OW pixels
+            "extrapolated_full_s": dt * (case.n * per) / count}
 
 
 def traffic_from(fetch_csv, write_csv, calib_bytes, workload_key):
@@ -210,16 +212,26 @@ def traffic_from(fetch_csv, write_csv, calib_bytes, workload_key):
     return out
 
 
-def _time_call(fn, reps=15, warmup=3):
+# Bytes written between repetitions of the cold timing variant (twice the
+# 256 MB Infinity Cache), and the GPU spin (clock cycles, about 50 us) that
+# spaces the warm variant.
+COLD_BYTES = 512 << 20
+SPIN_CYCLES = 100_000
+
+
+def _time_call(fn, reps=15, warmup=3, flush=None):
     """Median ms per call of fn() on the current stream (torch events around
     each call), so that a one-off stall of the machine does not move the
-    figure; the minimum is in _time_call.last_min."""
+    figure; the minimum is in _time_call.last_min.  flush, if given, runs
+    before each timed call, outside its events (the cold variant)."""
     import torch
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
     for a, b in ev:
+        if flush is not None:
+            flush()
         a.record()
         fn()
         b.record()
@@ -254,6 +266,8 @@ def run_suite(names):
     def emit(d):
         print(json.dumps(d), flush=True)
 
+    flush_buf = torch.empty(COLD_BYTES, dtype=torch.uint8, device=dev)
+
     def measure(case, algo="auto", inner=None, **kw):
         x = case.input().to(dev)
         w = case.weight().to(dev)
@@ -270,9 +284,20 @@ def run_suite(names):
         ms_min = _time_call.last_min
         split = _kernel_split(call)
         flops = cn.direct_flops(tuple(x.shape), tuple(w.shape), plan)
-        return {"workload": case.name, "dtype": case.dtype, "algo": plan.algo_name,
-                "inner_algo": plan.inner_algo_name, "ms": ms, "ms_min": ms_min, "tflops": flops / ms / 1e9,
-                "kernels_ms": split, "flops": flops}
+        r = {"workload": case.name, "dtype": case.dtype, "algo": plan.algo_name,
+             "inner_algo": plan.inner_algo_name, "ms": ms, "ms_min": ms_min, "tflops": flops / ms / 1e9,
+             "kernels_ms": split, "flops": flops}
+        # Working sets that fit the 256 MB Infinity Cache stay warm across
+        # repeated calls.  Two spaced variants put GPU work before each call,
+        # so the host's launch overhead is hidden in both and only the cache
+        # state differs: a spin that touches no memory (warm) and a 512 MB
+        # write (cold).  "ms" stays the back-to-back figure.
+        working = sum(t.numel() * t.element_size() for t in (x, w, y, ws))
+        if working < COLD_BYTES // 2:
+            r["ms_warm_spaced"] = _time_call(call, flush=lambda: torch.cuda._sleep(SPIN_CYCLES))
+            r["ms_cold"] = _time_call(call, flush=lambda: flush_buf.fill_(1))
+            r["tflops_cold"] = flops / r["ms_cold"] / 1e9
+        return r
 
     if "small" in names:
         for algo in ("winograd", "implicit_gemm", "unfold_gemm", "auto"):
@@ -310,15 +335,22 @@ def run_suite(names):
             stages = {}
             for case, mult, stage in cw.resnet50_layers(batch):
                 r = measure(case)
-                s_ = stages.setdefault(stage, {"ms": 0.0, "flops": 0.0})
+                s_ = stages.setdefault(stage, {"ms": 0.0, "ms_warm_spaced": 0.0, "ms_cold": 0.0, "flops": 0.0})
                 s_["ms"] += r["ms"] * mult
+                s_["ms_warm_spaced"] += r.get("ms_warm_spaced", r["ms"]) * mult
+                s_["ms_cold"] += r.get("ms_cold", r["ms"]) * mult
                 s_["flops"] += r["flops"] * mult
                 emit({"suite": "resnet50_layer", "batch": batch, "layer": case.name, "mult": mult,
-                      "algo": r["algo"], "ms": r["ms"], "tflops": r["tflops"], "kernels_ms": r["kernels_ms"]})
+                      "algo": r["algo"], "ms": r["ms"], "ms_warm_spaced": r.get("ms_warm_spaced"),
+                      "ms_cold": r.get("ms_cold"), "tflops": r["tflops"],
+                      "kernels_ms": r["kernels_ms"]})
             tot_ms = sum(v["ms"] for v in stages.values())
+            tot_cold = sum(v["ms_cold"] for v in stages.values())
+            tot_spaced = sum(v["ms_warm_spaced"] for v in stages.values())
             tot_fl = sum(v["flops"] for v in stages.values())
             emit({"suite": "resnet50_stack", "batch": batch, "dtype": "f16", "total_ms": tot_ms,
-                  "tflops": tot_fl / tot_ms / 1e9, "stages_ms": {k: v["ms"] for k, v in stages.items()}})
+                  "total_ms_warm_spaced": tot_spaced, "total_ms_cold": tot_cold, "tflops": tot_fl / tot_ms / 1e9,
+                  "stages_ms": {k: v["ms"] for k, v in stages.items()}})
             # the same 53 convs captured once into a HIP graph and replayed: the
             # GPU time of the stack without the per-call host overhead
             calls, flops = [], 0.0
