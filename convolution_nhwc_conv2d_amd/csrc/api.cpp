@@ -50,12 +50,13 @@ int64_t launches_2d(const cnhwc_plan_t& p, int32_t algo) {
   if (algo == CNHWC_ALGO_IMPLICIT_GEMM) return 1 + reduce;
   if (algo == CNHWC_ALGO_UNFOLD_GEMM) return (2 + reduce) * p.n_chunks;
   if (algo == CNHWC_ALGO_WINOGRAD) return 1 + 3 * p.n_tiles;
-  if (algo == CNHWC_ALGO_WINOGRAD_HALF) return 3 + 3 * p.n_tiles;
+  if (algo == CNHWC_ALGO_WINOGRAD_HALF) return 2 + 3 * p.n_tiles;
   return -1;
 }
 
 // Half-precision Winograd F(4x4,3x3) (2D, or 3D with the depth taps summed in
-// the GEMMs): the max-|element| pass and the scales, the filter transform,
+// the GEMMs): the max-|element| pass, the filter transform (which also turns
+// the maxima into the scales),
 // then per batch tile the input transform, the 36 tile-position GEMMs (fp16
 // operands, fp32 results) and the output transform.
 cnhwc_status_t run_wino_h(const cnhwc_conv_desc_t& d, const cnhwc_plan_t& p, const void* x,
@@ -70,10 +71,9 @@ cnhwc_status_t run_wino_h(const cnhwc_conv_desc_t& d, const cnhwc_plan_t& p, con
   const int64_t nw = d.o * d.kd * d.kh * d.kw * d.c;
   rec.mark(CNHWC_KERNEL_WINO_SCALE);
   if (wino_h_absmax_launch(d.dtype, x, nx, w, nw, partial, stream) != hipSuccess) return CNHWC_ERR_HIP;
-  rec.mark(CNHWC_KERNEL_WINO_SCALE);
-  if (wino_h_scale_launch(d.dtype, partial, nx, nw, scales, stream) != hipSuccess) return CNHWC_ERR_HIP;
   rec.mark(CNHWC_KERNEL_WINO_FILTER);
-  if (wino_h_filter_launch(d.dtype, w, d.o, d.kd, d.c, L.cs, scales, U, stream) != hipSuccess)
+  if (wino_h_filter_launch(d.dtype, w, d.o, d.kd, d.c, L.cs, partial, nx, nw, scales, U, stream) !=
+      hipSuccess)
     return CNHWC_ERR_HIP;
 
   GemmParams q;

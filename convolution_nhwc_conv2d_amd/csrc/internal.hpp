@@ -165,15 +165,15 @@ int wino_output_launch(int dtype, const float* m, int64_t plane, int64_t nb, int
 
 // Half-precision Winograd F(4x4,3x3) (fp16/bf16 x and w).
 // partial[t][b] = largest |element| bits of block b of tensor t (0: x of nx
-// elements, 1: w of nw), then scales = {sx, sw, a, b} with a b = 1/(sx sw)
-// (after the partial maxima in the workspace head).
+// elements, 1: w of nw).
 int wino_h_absmax_launch(int dtype, const void* x, int64_t nx, const void* w, int64_t nw,
                          uint32_t* partial, void* stream);
-int wino_h_scale_launch(int dtype, const uint32_t* partial, int64_t nx, int64_t nw, float* scales,
-                        void* stream);
-// U[p][o][kd*cs + c] = fp16(sw (G g G^T)_p), g = w[o][kd][kh][kw][c] (KD = kd planes).
+// U[p][o][kd*cs + c] = fp16(G (sw g) G^T)_p, g = w[o][kd][kh][kw][c] (KD = kd planes);
+// the scales come from the partial maxima, and scales = {sx, sw, a, b} with
+// a b = 1/(sx sw) is stored for the transforms that follow.
 int wino_h_filter_launch(int dtype, const void* w, int64_t o, int64_t kd, int64_t c, int64_t cs,
-                         const float* scales, uint16_t* u, void* stream);
+                         const uint32_t* partial, int64_t nx, int64_t nw, float* scales, uint16_t* u,
+                         void* stream);
 // V[p][r][c] = fp16(sx (B^T d B)_p) over nb elements of dp frames each (frame
 // f reads input frame f - pd, zero outside [0, d)); plane stride `plane`.
 int wino_h_input_launch(int dtype, const void* x, int64_t nb, int64_t d, int64_t dp, int32_t pd,

@@ -113,38 +113,50 @@ __device__ __forceinline__ int scale_exp(float a, float bound) {
   return e < -126 ? -126 : (e > 126 ? 126 : e);
 }
 
+// The scales from the partial maxima (every thread of the block takes part;
+// the result is valid in every thread): {sx, sw} and 1/(sx sw) split in two.
 template <bool BF16>
-__global__ __launch_bounds__(256) void wino_h_scale_kernel(const uint32_t* __restrict__ partial,
-                                                           int32_t nbx, int32_t nbw,
-                                                           float* __restrict__ scales) {
-  __shared__ uint32_t sm[4];
+__device__ __forceinline__ void block_scales(const uint32_t* __restrict__ partial, int32_t nbx,
+                                             int32_t nbw, uint32_t* sm, float (&s)[4]) {
   uint32_t mx = 0, mw = 0;
   for (int i = threadIdx.x; i < nbx; i += 256) mx = max(mx, partial[i]);
   for (int i = threadIdx.x; i < nbw; i += 256) mw = max(mw, partial[kWinoHSlots + i]);
   mx = block_max(mx, sm);
   __syncthreads();  // sm is reused
   mw = block_max(mw, sm);
+  __syncthreads();
   if (threadIdx.x == 0) {
     const int ex = scale_exp(abs_bits_to_f32<BF16>(mx), kWino4VBound);
     const int ew = scale_exp(abs_bits_to_f32<BF16>(mw), kWino4UBound);
-    scales[0] = ldexpf(1.0f, ex);
-    scales[1] = ldexpf(1.0f, ew);
     // 2^-(ex+ew) is undone in two halves (it may not be an fp32 itself); each
     // intermediate lies between the GEMM's fp32 result and the final value,
     // so it overflows only if y does
     const int et = -(ex + ew), eh = et / 2;
-    scales[2] = ldexpf(1.0f, eh);
-    scales[3] = ldexpf(1.0f, et - eh);
+    sm[0] = __builtin_bit_cast(uint32_t, ldexpf(1.0f, ex));
+    sm[1] = __builtin_bit_cast(uint32_t, ldexpf(1.0f, ew));
+    sm[2] = __builtin_bit_cast(uint32_t, ldexpf(1.0f, eh));
+    sm[3] = __builtin_bit_cast(uint32_t, ldexpf(1.0f, et - eh));
   }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) s[i] = __builtin_bit_cast(float, sm[i]);
 }
 
 // U[p][o][kd*Cs + c] = fp16((G (sw g) G^T)_p), g = w[o][kd][.][.][c]; zero for c >= C.
+// Every block first reduces the partial maxima to the scales (block 0 also
+// stores them for the input and output transforms, which run after it).
 template <bool BF16>
 __global__ __launch_bounds__(256) void wino_h_filter_kernel(const uint16_t* __restrict__ w,
                                                             int64_t O, int64_t KD, int64_t C,
                                                             int64_t Cs,
-                                                            const float* __restrict__ scales,
+                                                            const uint32_t* __restrict__ partial,
+                                                            int32_t nbx, int32_t nbw,
+                                                            float* __restrict__ scales,
                                                             uint16_t* __restrict__ U) {
+  __shared__ uint32_t sm[4];
+  float sc[4];
+  block_scales<BF16>(partial, nbx, nbw, sm, sc);
+  if (blockIdx.x == 0 && threadIdx.x < 4) scales[threadIdx.x] = sc[threadIdx.x];
   const int64_t ku = KD * Cs;
   const int64_t t = int64_t(blockIdx.x) * 256 + threadIdx.x;
   if (t >= O * ku) return;
@@ -152,7 +164,7 @@ __global__ __launch_bounds__(256) void wino_h_filter_kernel(const uint16_t* __re
   const int64_t kd = r / Cs, c = r - kd * Cs;
   const uint16_t* __restrict__ g0 = w + (o * KD + kd) * 9 * C + c;
   // scaled as it is loaded (exact): the fp32 transform then stays below 2^15
-  const float s = scales[1];
+  const float s = sc[1];
   float g[3][3];
 #pragma unroll
   for (int a = 0; a < 3; ++a)
@@ -356,27 +368,20 @@ int wino_h_absmax_launch(int dtype, const void* x, int64_t nx, const void* w, in
   return hipGetLastError();
 }
 
-int wino_h_scale_launch(int dtype, const uint32_t* partial, int64_t nx, int64_t nw, float* scales,
-                        void* stream) {
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  const int32_t nbx = wino_h_absmax_blocks(nx), nbw = wino_h_absmax_blocks(nw);
-  if (dtype == CNHWC_BF16)
-    hipLaunchKernelGGL((wino_h_scale_kernel<true>), dim3(1), dim3(256), 0, s, partial, nbx, nbw, scales);
-  else
-    hipLaunchKernelGGL((wino_h_scale_kernel<false>), dim3(1), dim3(256), 0, s, partial, nbx, nbw, scales);
-  return hipGetLastError();
-}
-
 int wino_h_filter_launch(int dtype, const void* w, int64_t o, int64_t kd, int64_t c, int64_t cs,
-                         const float* scales, uint16_t* u, void* stream) {
+                         const uint32_t* partial, int64_t nx, int64_t nw, float* scales, uint16_t* u,
+                         void* stream) {
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int64_t total = o * kd * cs;
   const dim3 grid(blocks_for(total));
+  const int32_t nbx = wino_h_absmax_blocks(nx), nbw = wino_h_absmax_blocks(nw);
   const uint16_t* ws = static_cast<const uint16_t*>(w);
   if (dtype == CNHWC_BF16)
-    hipLaunchKernelGGL((wino_h_filter_kernel<true>), grid, dim3(256), 0, s, ws, o, kd, c, cs, scales, u);
+    hipLaunchKernelGGL((wino_h_filter_kernel<true>), grid, dim3(256), 0, s, ws, o, kd, c, cs, partial, nbx,
+                       nbw, scales, u);
   else
-    hipLaunchKernelGGL((wino_h_filter_kernel<false>), grid, dim3(256), 0, s, ws, o, kd, c, cs, scales, u);
+    hipLaunchKernelGGL((wino_h_filter_kernel<false>), grid, dim3(256), 0, s, ws, o, kd, c, cs, partial, nbx,
+                       nbw, scales, u);
   return hipGetLastError();
 }
 

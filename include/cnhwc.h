@@ -283,7 +283,7 @@ typedef enum {
   CNHWC_KERNEL_UNFOLD = 6,       /* one unfold chunk */
   CNHWC_KERNEL_UNFOLD_GEMM = 7,  /* the dense GEMM of one unfold chunk */
   CNHWC_KERNEL_SPLITK_REDUCE = 8, /* sum of the K-split partial sums + epilogue */
-  CNHWC_KERNEL_WINO_SCALE = 9     /* half-precision Winograd: max |x|, |w| and the scales */
+  CNHWC_KERNEL_WINO_SCALE = 9     /* half-precision Winograd: the max |x|, max |w| pass */
 } cnhwc_kernel_kind_t;
 
 /* Number of kernels a forward call with this plan launches (3D: over all
