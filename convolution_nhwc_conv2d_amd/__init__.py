@@ -22,6 +22,7 @@ library as ordinary arguments (MLX PR "Bound winograd conv2d working set by
 tiling the batch", Testing: an injected budget and a forced tile size).
 """
 import ctypes
+import functools
 import os
 
 import torch  # noqa: F401  (load torch's HIP runtime first: the library then binds to it)
@@ -174,13 +175,20 @@ def make_desc(x_shape, w_shape, stride=1, padding=0, dilation=1, dtype=torch.flo
     return d
 
 
+@functools.lru_cache(maxsize=None)
+def _total_memory(index):
+    return int(torch.cuda.get_device_properties(index).total_memory)
+
+
 def default_ws_limit(device=None):
-    """W for the byte budget: CNHWC_WS_LIMIT if set, else the device's total memory."""
+    """W for the byte budget: CNHWC_WS_LIMIT if set, else the device's total
+    memory (a fixed property of the device, looked up once)."""
     env = os.environ.get("CNHWC_WS_LIMIT")
     if env:
         return int(env)
     if torch.cuda.is_available():
-        return int(torch.cuda.get_device_properties(device or 0).total_memory)
+        index = 0 if device is None else torch.device(device).index
+        return _total_memory(torch.cuda.current_device() if index is None else index)
     return 288 * 10**9  # MI355X HBM3E capacity, when planning without a device
 
 
@@ -340,9 +348,11 @@ class KernelTimer:
 def conv2d(x, w, stride=1, padding=0, dilation=1, *, algo="auto", ws_limit=None, tile_batch=None,
            unfold_rows=None, gemm_config=None, split_k=None, out=None, workspace=None, plan=None,
            timer=None):
-    """y[N,OH,OW,O] = channels-last conv2d of x[N,H,W,C] with w[O,KH,KW,C]."""
-    opts = make_opts(ws_limit, algo, "auto", tile_batch, unfold_rows, gemm_config=gemm_config,
-                     split_k=split_k, device=x.device if x.is_cuda else None)
+    """y[N,OH,OW,O] = channels-last conv2d of x[N,H,W,C] with w[O,KH,KW,C].  With
+    a plan, the selection options are the plan's own and the others are unused."""
+    opts = None if plan is not None else make_opts(
+        ws_limit, algo, "auto", tile_batch, unfold_rows, gemm_config=gemm_config, split_k=split_k,
+        device=x.device if x.is_cuda else None)
     fn = lib.cnhwc_conv2d_fwd_timed if timer is not None else lib.cnhwc_conv2d_fwd
     return _run(fn, x, w, stride, padding, dilation, opts, out, workspace, plan, timer)
 
@@ -350,9 +360,11 @@ def conv2d(x, w, stride=1, padding=0, dilation=1, *, algo="auto", ws_limit=None,
 def conv3d(x, w, stride=1, padding=0, dilation=1, *, algo="auto", inner_algo="auto", ws_limit=None,
            tile_batch=None, unfold_rows=None, gemm_config=None, split_k=None, out=None, workspace=None,
            plan=None, timer=None):
-    """y[N,OD,OH,OW,O] = channels-last conv3d of x[N,D,H,W,C] with w[O,KD,KH,KW,C]."""
-    opts = make_opts(ws_limit, algo, inner_algo, tile_batch, unfold_rows, gemm_config=gemm_config,
-                     split_k=split_k, device=x.device if x.is_cuda else None)
+    """y[N,OD,OH,OW,O] = channels-last conv3d of x[N,D,H,W,C] with w[O,KD,KH,KW,C].
+    With a plan, the selection options are the plan's own and the others are unused."""
+    opts = None if plan is not None else make_opts(
+        ws_limit, algo, inner_algo, tile_batch, unfold_rows, gemm_config=gemm_config, split_k=split_k,
+        device=x.device if x.is_cuda else None)
     fn = lib.cnhwc_conv3d_fwd_timed if timer is not None else lib.cnhwc_conv3d_fwd
     return _run(fn, x, w, stride, padding, dilation, opts, out, workspace, plan, timer)
 
