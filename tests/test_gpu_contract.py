@@ -1,0 +1,132 @@
+"""GPU contract tests of the C ABI: run-to-run bit determinism of every
+algorithm, errors that leave y untouched, and stream ordering with a
+consumer op (MLX PR "Bound winograd conv2d working set by tiling the batch",
+Problem: the failure mode there was a dropped error and a silently all-zero
+output; Testing: a tiled output consumed right away)."""
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+import conv_workloads as cw
+import oracle
+from gpu_util import bits, check_parity, poisoned, to_oracle
+
+pytestmark = pytest.mark.gpu
+
+cn = pytest.importorskip("convolution_nhwc_conv2d_amd")
+
+
+def _case2(dt, c=64, o=96, n=3, h=22, w=21, seed=81):
+    return cw.ConvCase(f"contract_{dt}", n, h, w, c, o, 3, 3, (1, 1), (1, 1), (1, 1), dt, "normal", "normal",
+                       None, seed, c + o)
+
+
+# (label, dtype, conv kind, kwargs)
+RUNS = [
+    ("winograd_f32", "f32", 2, dict(algo="winograd")),
+    ("winograd_f32_tiled", "f32", 2, dict(algo="winograd", tile_batch=2)),
+    ("implicit_f32", "f32", 2, dict(algo="implicit_gemm")),
+    ("implicit_f32_split", "f32", 2, dict(algo="implicit_gemm", split_k=3)),
+    ("unfold_f32", "f32", 2, dict(algo="unfold_gemm", unfold_rows=500)),
+    ("implicit_f16", "f16", 2, dict(algo="implicit_gemm")),
+    ("implicit_bf16_tile256", "bf16", 2, dict(algo="implicit_gemm", gemm_config=14)),
+    ("unfold_bf16", "bf16", 2, dict(algo="unfold_gemm")),
+    ("winograd_half_f16", "f16", 2, dict(algo="winograd_half")),
+    ("winograd_half_bf16_tiled", "bf16", 2, dict(algo="winograd_half", tile_batch=2)),
+    ("native3d_bf16", "bf16", 3, dict(algo="implicit_gemm")),
+    ("small_kd_f16", "f16", 3, dict(algo="small_kd")),
+    ("winograd_half_3d_bf16", "bf16", 3, dict(algo="winograd_half")),
+]
+
+
+def _inputs(dt, nd):
+    if nd == 2:
+        case = _case2(dt)
+    else:
+        case = cw.ConvCase(f"contract3d_{dt}", 1, 12, 13, 64, 48, 3, 3, (1, 1, 1), (0, 1, 1), (1, 1, 1), dt,
+                           "normal", "normal", None, 82, 3, nd=3, d=6, kd=3)
+    return case, case.input().cuda(), case.weight().cuda()
+
+
+@pytest.mark.parametrize("label,dt,nd,kw", RUNS, ids=[r[0] for r in RUNS])
+def test_run_to_run_bits(label, dt, nd, kw):
+    """Every algorithm gives the same bits on every call (fresh buffers, reused
+    workspace, and after unrelated work in between), and matches the oracle."""
+    case, x, w = _inputs(dt, nd)
+    fn = cn.conv2d if nd == 2 else cn.conv3d
+    first = fn(x, w, **case.conv_kwargs(), **kw)
+    plan = (cn.plan2d if nd == 2 else cn.plan3d)(tuple(x.shape), tuple(w.shape), **case.conv_kwargs(),
+                                                 dtype=x.dtype, **kw)
+    ws = torch.empty(max(1, plan.workspace_bytes), dtype=torch.uint8, device="cuda")
+    for rep in range(3):
+        junk = torch.randn(1 << 20, device="cuda")  # unrelated work and allocation churn
+        y = fn(x, w, **case.conv_kwargs(), plan=plan, workspace=ws, out=poisoned(first.shape, first.dtype))
+        torch.cuda.synchronize()
+        assert torch.equal(bits(y), bits(first)), f"{label}: call {rep} differs"
+        del junk
+    yr, den = oracle.conv(to_oracle(case.input()), to_oracle(case.weight()), **case.conv_kwargs())
+    check_parity(first.cpu(), yr, den, first.dtype, label)
+
+
+def _st(name):
+    return {v: k for k, v in cn.STATUS.items()}[name]
+
+
+def _raw_call(x, w, y, ws_ptr, ws_len, plan, desc):
+    stream = torch.cuda.current_stream().cuda_stream
+    return cn.lib.cnhwc_conv2d_fwd(ctypes.byref(desc), ctypes.byref(plan), x.data_ptr(), w.data_ptr(),
+                                   y.data_ptr(), ws_ptr, ws_len, stream)
+
+
+@pytest.mark.parametrize("algo", ["winograd", "winograd_half", "unfold_gemm", "implicit_gemm"])
+def test_errors_leave_y_untouched(algo):
+    """A call that fails validation queues nothing: y keeps its NaN fill."""
+    dt = "f16" if algo == "winograd_half" else "f32"
+    case = _case2(dt)
+    x, w = case.input().cuda(), case.weight().cuda()
+    kw = dict(algo=algo, split_k=3) if algo == "implicit_gemm" else dict(algo=algo)
+    plan = cn.plan2d(tuple(x.shape), tuple(w.shape), 1, 1, 1, x.dtype, **kw)
+    desc = cn.make_desc(tuple(x.shape), tuple(w.shape), 1, 1, 1, x.dtype)
+    y = poisoned((case.n, case.h, case.w, case.o), x.dtype)
+    need = int(plan.workspace_bytes)
+    assert need > 0
+    ws = torch.empty(need + 64, dtype=torch.uint8, device="cuda")
+    # workspace one byte too small
+    st = _raw_call(x, w, y, ws.data_ptr(), need - 1, plan, desc)
+    assert st == _st("WORKSPACE_TOO_SMALL")
+    # misaligned workspace and output pointers
+    assert _raw_call(x, w, y, ws.data_ptr() + 8, need, plan, desc) == _st("INVALID_ARGUMENT")
+    y_off = poisoned((case.n * case.h * case.w * case.o + 8,), x.dtype)
+    stream = torch.cuda.current_stream().cuda_stream
+    st = cn.lib.cnhwc_conv2d_fwd(ctypes.byref(desc), ctypes.byref(plan), x.data_ptr(), w.data_ptr(),
+                                 y_off.data_ptr() + 2, ws.data_ptr(), need, stream)
+    assert st == _st("INVALID_ARGUMENT")
+    # a plan that does not match the descriptor
+    other = cn.make_desc((case.n, case.h + 1, case.w, case.c), tuple(w.shape), 1, 1, 1, x.dtype)
+    st = cn.lib.cnhwc_conv2d_fwd(ctypes.byref(other), ctypes.byref(plan), x.data_ptr(), w.data_ptr(),
+                                 y.data_ptr(), ws.data_ptr(), need, stream)
+    assert st == _st("PLAN_MISMATCH")
+    # the workspace overlapping y
+    assert _raw_call(x, w, y, y.data_ptr(), need, plan, desc) == _st("INVALID_ARGUMENT")
+    torch.cuda.synchronize()
+    assert torch.isnan(y.float()).all() and torch.isnan(y_off.float()).all()
+    # and the same call with a valid workspace writes every element
+    assert _raw_call(x, w, y, ws.data_ptr(), need, plan, desc) == 0
+    torch.cuda.synchronize()
+    assert not torch.isnan(y.float()).any()
+
+
+def test_consumer_on_the_same_stream_sees_the_tiled_output():
+    """A torch op queued right after the call, with no synchronisation, reads
+    the finished tiled Winograd output (stream order is the only guarantee)."""
+    case = cw.ConvCase("contract_consumer", 6, 40, 44, 64, 96, 3, 3, (1, 1), (1, 1), (1, 1), "f32", "uniform",
+                       "normal", None, 83, 0)
+    x, w = case.input().cuda(), case.weight().cuda()
+    y = cn.conv2d(x, w, 1, 1, 1, algo="winograd", tile_batch=2, out=poisoned((6, 40, 44, 96), torch.float32))
+    s = y.double().sum(dim=(1, 2, 3))  # consumer, same stream, no sync in between
+    ref = cn.conv2d(x, w, 1, 1, 1, algo="winograd")
+    torch.cuda.synchronize()
+    assert torch.equal(s, ref.double().sum(dim=(1, 2, 3)))
+    assert np.isfinite(s.cpu().numpy()).all()
