@@ -66,8 +66,9 @@ def parse():
 
 
 # The sources the headline workload's kernels (the fp32 Winograd transforms and
-# the resident Winograd GEMM) are compiled from, headers included.
-HEADLINE_SOURCES = ("winograd.hip", "wino_gemm.hip", "device_common.hpp", "internal.hpp", "winograd_f63.h")
+# the resident Winograd GEMM) are compiled from, headers included (and the
+# public header include/cnhwc.h, which they include too).
+HEADLINE_SOURCES = ("winograd.hip", "wino_gemm.hip", "wino_f63_api.hpp", "device_common.hpp", "winograd_f63.h")
 
 
 def _code_only(text):
@@ -86,6 +87,7 @@ def csrc_hash():
     for f in HEADLINE_SOURCES:
         h.update(f.encode())
         h.update(_code_only(open(os.path.join(d, f)).read()).encode())
+    h.update(_code_only(open(os.path.join(ROOT, "include", "cnhwc.h")).read()).encode())
     return h.hexdigest()[:16]
 
 
@@ -146,7 +148,7 @@ def cpu_baseline(case, seconds):
     xs = case.input(list(range(elems))).numpy()
     rows = cw.sample_rows(elems * per, count, 12)
     t0 = time.perf_counter()
-    oracle.conv(xs, w, **kw, rows=rows, threads=threads)
+    yr, den = oracle.conv(xs, w, **kw, rows=rows, threads=threads)
     dt = time.perf_counter() - t0
     flops = 2.0 * count * case.o * case.kh * case.kw * case.c
     cpu = "unknown"
@@ -162,7 +164,9 @@ def cpu_baseline(case, seconds):
                       f"fp64 direct correlation, {dt:.2f} s wall; CPU {cpu}",
             "seconds": dt, "outputs_per_s": count * case.o / dt,
             # extrapolated, not measured: the sample's rate over all case.n * OH * OW pixels
-            "extrapolated_full_s": dt * (case.n * per) / count}
+            "extrapolated_full_s": dt * (case.n * per) / count,
+            # the sample's fp64 results, for the parity check of the GPU output (not printed)
+            "_rows": rows, "_y": yr, "_den": den}
 
 
 def traffic_from(fetch_csv, write_csv, calib_bytes, workload_key):
@@ -516,10 +520,20 @@ def main():
                 "avg_ms": d["avg_ms"], "work_per_launch": d.get("work_per_launch")}
 
     cpu = None
+    check = None
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")
         cpu = cpu_baseline(case, args.cpu_seconds)
         log(f"[bench] oracle {cpu['value']:.4f} TFLOP/s on {cpu['cores']} threads")
+        # the same sample checks the GPU output of the last timed step
+        import numpy as np
+        rows, yr, den = cpu.pop("_rows"), cpu.pop("_y"), cpu.pop("_den")
+        idx = torch.as_tensor(rows, device=dev, dtype=torch.long)
+        yg = out.reshape(-1, case.o).index_select(0, idx).double().cpu().numpy()
+        rel = np.abs(yg - yr) / np.where(den > 0, den, 1.0)
+        check = {"outputs": int(rel.size), "max_err_over_sum_abs": float(rel.max()),
+                 "mean_err_over_sum_abs": float(rel.mean()), "tol": 2e-5, "within_tol": bool(rel.max() <= 2e-5)}
+        log(f"[bench] oracle check: max |y - y_ref| / sum|x||w| = {check['max_err_over_sum_abs']:.3g}")
 
     line = {
         "metric": "conv fwd TFLOP/s (2*N*OH*OW*O*C*KH*KW/s) and % of roofline",
@@ -541,6 +555,7 @@ def main():
         "roofline": roofline,
         "stages": stages,
         "cpu_baseline": cpu,
+        "oracle_check": check,
     }
     print(json.dumps(line), flush=True)
 

@@ -20,10 +20,12 @@ tests, the environment variables ``CNHWC_WS_LIMIT`` (bytes) and
 ``CNHWC_TILE_BATCH`` are read here -- and only here -- and passed to the
 library as ordinary arguments (MLX PR "Bound winograd conv2d working set by
 tiling the batch", Testing: an injected budget and a forced tile size).
+``CNHWC_LOG=1`` prints each call's plan to stderr.
 """
 import ctypes
 import functools
 import os
+import sys
 
 import torch  # noqa: F401  (load torch's HIP runtime first: the library then binds to it)
 
@@ -175,6 +177,10 @@ def make_desc(x_shape, w_shape, stride=1, padding=0, dilation=1, dtype=torch.flo
     return d
 
 
+# CNHWC_LOG=1 prints each call's plan to stderr (read once, at import).
+_LOG = os.environ.get("CNHWC_LOG") == "1"
+
+
 @functools.lru_cache(maxsize=None)
 def _total_memory(index):
     return int(torch.cuda.get_device_properties(index).total_memory)
@@ -250,6 +256,8 @@ def _run(fn, x, w, stride, padding, dilation, opts, out, workspace, plan, timer=
     desc = make_desc(tuple(x.shape), tuple(w.shape), stride, padding, dilation, x.dtype)
     if plan is None:
         plan = select(desc, opts)
+    if _LOG:
+        print(f"[cnhwc] x {tuple(x.shape)} w {tuple(w.shape)} {x.dtype}: {plan}", file=sys.stderr, flush=True)
     oshape = (x.shape[0],) + ((plan.out_d,) if desc.nd == 3 else ()) + (plan.out_h, plan.out_w, w.shape[0])
     if out is None:
         out = torch.empty(oshape, dtype=x.dtype, device=x.device)

@@ -5,21 +5,13 @@
 #include <cstddef>
 
 #include "cnhwc.h"
+#include "wino_f63_api.hpp"
 
 namespace cnhwc {
 
 inline uint64_t dtype_size(int dt) { return dt == CNHWC_F32 ? 4u : 2u; }
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline uint64_t align_up(uint64_t v, uint64_t a) { return (v + a - 1) / a * a; }
-
-// Winograd F(6x6,3x3): 8x8 input tiles at stride 6, 64 tile positions.
-constexpr int kWinoM = 6;
-constexpr int kWinoT = 8;
-constexpr int kWinoP = 64;
-
-// Channel stride of the transformed input/filter rows: C rounded up to a
-// multiple of 8 so every row is 32-byte aligned (pad channels are zero).
-inline int64_t wino_cs(int64_t c) { return (c + 7) / 8 * 8; }
 
 // Winograd F(4x4,3x3) for fp16/bf16 (winograd_h.hip): 6x6 input tiles at
 // stride 4, 36 tile positions, fp16 transformed operands with power-of-two
@@ -71,13 +63,6 @@ enum GemmConfig : int32_t {
 // 256x256 direct-to-LDS tile.
 int32_t pick_gemm_config(int dtype, int64_t m_rows, int64_t n_cols, bool lds_ok);
 
-// Epilogue: how a GEMM / output-transform result r is written.
-enum EpiMode : int32_t {
-  kEpiStore = 0,     // y = round(r)
-  kEpiAccFirst = 1,  // acc = r                (fp32)
-  kEpiAccMid = 2,    // acc = acc + r          (fp32)
-  kEpiAccLast = 3,   // y = round(acc + r)
-};
 
 // A-operand source.
 enum AMode : int32_t {
@@ -140,28 +125,7 @@ inline int64_t gemm_config_bk(int32_t config) {
 bool gemm_lds_ok(const GemmParams& p);
 int gemm_lds_launch(const GemmParams& p, void* stream);  // returns hipError_t
 
-// Persistent Winograd GEMM (all 64 positions): M_p[rows][o] = V_p[rows][cs] * U_p[o][cs]^T.
-// Applicable when U_p fits in LDS (cs <= 192, o <= 96).
-bool wino_gemm_resident_ok(int64_t cs, int64_t o);
-int wino_gemm_resident_launch(const float* v, const float* u, float* m, int64_t rows, int64_t o,
-                              int64_t cs, int64_t v_plane, int64_t m_plane, void* stream);
 
-// ------------------------------------------------------------ Winograd
-
-// U[p][o][c] = (G g G^T)_p, g = w[o*ldo + (kh*3 + kw)*C + c]; zero for c >= C.
-int wino_filter_launch(int dtype, const void* w, int64_t ldo, int64_t o, int64_t c,
-                       int64_t cs, float* u, void* stream);
-
-// V[p][r][c] = (B^T d B)_p for tile r of nb images [nb][h][w][c] (8x8 tiles at
-// stride 6 starting at (-ph, -pw), zero outside); plane stride `plane`.
-int wino_input_launch(int dtype, const void* x, int64_t nb, int64_t h, int64_t w, int64_t c,
-                      int64_t cs, int32_t ph, int32_t pw, int64_t tiles_h, int64_t tiles_w,
-                      float* v, int64_t plane, void* stream);
-
-// Y = A^T M A per tile and output channel, cropped to [oh, ow]; epilogue mode.
-int wino_output_launch(int dtype, const float* m, int64_t plane, int64_t nb, int64_t oh,
-                       int64_t ow, int64_t o, int64_t tiles_h, int64_t tiles_w, void* y,
-                       float* acc, int32_t epi, void* stream);
 
 // Half-precision Winograd F(4x4,3x3) (fp16/bf16 x and w).
 // partial[t][b] = largest |element| bits of block b of tensor t (0: x of nx

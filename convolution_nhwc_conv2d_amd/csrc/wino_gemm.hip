@@ -25,7 +25,7 @@
 
 #include <type_traits>
 
-#include "internal.hpp"
+#include "wino_f63_api.hpp"
 #include "device_common.hpp"
 
 namespace cnhwc {

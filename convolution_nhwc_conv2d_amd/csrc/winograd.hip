@@ -21,7 +21,7 @@
 // depend on how the batch is tiled.
 #include <hip/hip_runtime.h>
 
-#include "internal.hpp"
+#include "wino_f63_api.hpp"
 #include "device_common.hpp"
 #include "winograd_f63.h"
 

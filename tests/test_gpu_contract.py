@@ -50,21 +50,32 @@ def _inputs(dt, nd):
     return case, case.input().cuda(), case.weight().cuda()
 
 
+CANARY = 4096
+
+
 @pytest.mark.parametrize("label,dt,nd,kw", RUNS, ids=[r[0] for r in RUNS])
 def test_run_to_run_bits(label, dt, nd, kw):
     """Every algorithm gives the same bits on every call (fresh buffers, reused
-    workspace, and after unrelated work in between), and matches the oracle."""
+    workspace, and after unrelated work in between), writes nothing past its
+    workspace or its output (canary tails), and matches the oracle."""
     case, x, w = _inputs(dt, nd)
     fn = cn.conv2d if nd == 2 else cn.conv3d
     first = fn(x, w, **case.conv_kwargs(), **kw)
     plan = (cn.plan2d if nd == 2 else cn.plan3d)(tuple(x.shape), tuple(w.shape), **case.conv_kwargs(),
                                                  dtype=x.dtype, **kw)
-    ws = torch.empty(max(1, plan.workspace_bytes), dtype=torch.uint8, device="cuda")
+    # canaries: 4 KB of 0xA5 after the planned workspace, NaN after the output
+    need = int(plan.workspace_bytes)
+    ws_buf = torch.full((need + CANARY,), 0xA5, dtype=torch.uint8, device="cuda")
+    ws = ws_buf[:max(1, need)]
+    numel = first.numel()
     for rep in range(3):
         junk = torch.randn(1 << 20, device="cuda")  # unrelated work and allocation churn
-        y = fn(x, w, **case.conv_kwargs(), plan=plan, workspace=ws, out=poisoned(first.shape, first.dtype))
+        y_buf = poisoned((numel + CANARY,), first.dtype)
+        y = fn(x, w, **case.conv_kwargs(), plan=plan, workspace=ws, out=y_buf[:numel].view(first.shape))
         torch.cuda.synchronize()
         assert torch.equal(bits(y), bits(first)), f"{label}: call {rep} differs"
+        assert bool((ws_buf[max(1, need):] == 0xA5).all()), f"{label}: write past the workspace"
+        assert bool(torch.isnan(y_buf[numel:].float()).all()), f"{label}: write past the output"
         del junk
     yr, den = oracle.conv(to_oracle(case.input()), to_oracle(case.weight()), **case.conv_kwargs())
     check_parity(first.cpu(), yr, den, first.dtype, label)
