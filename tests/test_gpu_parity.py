@@ -93,13 +93,12 @@ def test_fp32_geometry(k, s, d, p):
 # ------------------------------------------- integer data: exact in every dtype
 
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
-@pytest.mark.parametrize("algo", ["implicit_gemm", "unfold_gemm", "winograd"])
+@pytest.mark.parametrize("algo", ["implicit_gemm", "unfold_gemm"])
 def test_integer_data_bit_exact(dtype, algo):
     # entries in {-1,0,1}, K = 3*3*24 = 216 <= 256: every partial sum is an
     # integer of magnitude <= 216, exact in fp32/fp16/bf16 -> results must equal
-    # the oracle exactly (Winograd only for fp32-exact transforms: excluded)
-    if algo == "winograd":
-        pytest.skip("Winograd transforms use fractional coefficients: not exact by construction")
+    # the oracle exactly.  (Not the Winograd paths: their transforms have
+    # fractional coefficients, so they are not exact by construction.)
     case = cw.ConvCase("ternary", 2, 13, 11, 24, 40, 3, 3, (1, 1), (1, 1), (1, 1), dtype, "ternary", "ternary",
                        1.0, 21, 0)
     x, w = case.input(), case.weight()
