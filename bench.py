@@ -60,7 +60,8 @@ def parse():
                          "with --calib-copy, write profiles/traffic.json, print it and exit")
     ap.add_argument("--suite", default=None,
                     help="instead of the headline line, time other workloads: "
-                         "comma list of small,wide,sweep,wino_half,resnet,video,video_auto,conv1d or 'all' "
+                         "comma list of small,wide,sweep,wino_half,resnet,video,video_auto,conv1d,vendor_gemm "
+                         "or 'all' "
                          "(one JSON line each)")
     return ap.parse_args()
 
@@ -423,6 +424,23 @@ def run_suite(names):
                 r = measure(case)
                 r["suite"] = "conv1d"
                 emit(r)
+    if "vendor_gemm" in names:
+        # Reference point for the half-precision GEMM stages, not part of the
+        # path: the vendor GEMM (torch.matmul) on dense operands of the same
+        # M x N x K as the large implicit GEMMs (the C_out and K axes of the
+        # sweep, the largest video conv's per-tap GEMM) and a square 8192^3.
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(7)
+        for dt in (torch.float16, torch.bfloat16):
+            for m, n, k in ((16384, 1024, 9216), (65536, 4096, 2304), (16384, 1024, 2304), (65536, 256, 2304),
+                            (973440, 512, 4608), (8192, 8192, 8192)):
+                a = torch.randn((m, k), device=dev, dtype=dt, generator=gen)
+                b = torch.randn((k, n), device=dev, dtype=dt, generator=gen)
+                c = torch.empty((m, n), device=dev, dtype=dt)
+                ms = _time_call(lambda timer=None: torch.matmul(a, b, out=c))
+                emit({"suite": "vendor_gemm", "dtype": str(dt).replace("torch.", ""), "m": m, "n": n, "k": k,
+                      "ms": ms, "tflops": 2.0 * m * n * k / ms / 1e9})
+                del a, b, c
 
 
 def main():
