@@ -248,11 +248,29 @@ def _check_tensor(t, name):
         raise ValueError(f"{name} must be contiguous")
 
 
+def _empty_batch(x, w, stride, padding, dilation, opts, out):
+    """An empty batch has an empty output and no work; the library's descriptor
+    needs n >= 1, so the descriptor is checked and the output extents taken with
+    n = 1, and nothing is launched."""
+    desc = make_desc((1,) + tuple(x.shape[1:]), tuple(w.shape), stride, padding, dilation, x.dtype)
+    plan = select(desc, opts if opts is not None else make_opts())
+    oshape = (0,) + ((plan.out_d,) if desc.nd == 3 else ()) + (plan.out_h, plan.out_w, w.shape[0])
+    if out is None:
+        return torch.empty(oshape, dtype=x.dtype, device=x.device)
+    _check_tensor(out, "out")
+    if tuple(out.shape) != oshape or out.dtype != x.dtype:
+        raise ValueError("out has the wrong shape or dtype")
+    return out
+
+
 def _run(fn, x, w, stride, padding, dilation, opts, out, workspace, plan, timer=None):
     _check_tensor(x, "x")
     _check_tensor(w, "w")
     if w.dtype != x.dtype or w.device != x.device:
         raise TypeError("x and w must share dtype and device")
+    if x.shape[0] == 0:
+        return _empty_batch(x, w, stride, padding, dilation,
+                            opts if opts is not None or plan is None else plan.opts, out)
     desc = make_desc(tuple(x.shape), tuple(w.shape), stride, padding, dilation, x.dtype)
     if plan is None:
         plan = select(desc, opts)

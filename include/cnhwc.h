@@ -106,7 +106,8 @@ typedef enum {
 typedef struct {
   int32_t nd;        /* 2 or 3 */
   int32_t dtype;     /* cnhwc_dtype_t: element type of x, w and y */
-  int64_t n, d, h, w, c, o, kd, kh, kw;
+  int64_t n, d, h, w, c, o, kd, kh, kw;  /* each in [1, 2^31]; an empty batch (n = 0)
+                                            is INVALID_ARGUMENT: there is no work to plan */
   int32_t stride[3];
   int32_t pad[3];
   int32_t dil[3];

@@ -141,3 +141,27 @@ def test_consumer_on_the_same_stream_sees_the_tiled_output():
     torch.cuda.synchronize()
     assert torch.equal(s, ref.double().sum(dim=(1, 2, 3)))
     assert np.isfinite(s.cpu().numpy()).all()
+
+
+def test_empty_batch_returns_an_empty_output():
+    """N = 0: the binding returns an empty output of the planned shape and
+    launches nothing (the C descriptor needs n >= 1); the rest of the
+    descriptor is still checked."""
+    for dt in (torch.float32, torch.bfloat16):
+        x = torch.empty((0, 12, 10, 32), dtype=dt, device="cuda")
+        w = torch.zeros((48, 3, 3, 32), dtype=dt, device="cuda")
+        y = cn.conv2d(x, w, 2, 1, 1)
+        assert y.shape == (0, 6, 5, 48) and y.dtype == dt
+        out = torch.empty((0, 6, 5, 48), dtype=dt, device="cuda")
+        assert cn.conv2d(x, w, 2, 1, 1, out=out) is out
+        with pytest.raises(ValueError):
+            cn.conv2d(x, w, 1, 1, 1, out=out)
+        with pytest.raises(cn.CnhwcError) as e:
+            cn.conv2d(x, w, 0, 1, 1)
+        assert e.value.name == "INVALID_ARGUMENT"
+    x3 = torch.empty((0, 5, 8, 8, 16), dtype=torch.bfloat16, device="cuda")
+    w3 = torch.zeros((16, 3, 3, 3, 16), dtype=torch.bfloat16, device="cuda")
+    assert cn.conv3d(x3, w3, 1, (0, 1, 1), 1).shape == (0, 3, 8, 8, 16)
+    x1 = torch.empty((0, 50, 16), dtype=torch.float16, device="cuda")
+    w1 = torch.zeros((24, 3, 16), dtype=torch.float16, device="cuda")
+    assert cn.conv1d(x1, w1, 1, 1).shape == (0, 50, 24)
