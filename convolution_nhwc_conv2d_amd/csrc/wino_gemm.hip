@@ -181,8 +181,6 @@ __global__ __launch_bounds__(kResThreads) void wino_gemm_resident_kernel(
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
       // chunk c + 2 of this block, or chunk c + 2 - NCH of the next one(s)
-      constexpr int dummy = 0;
-      (void)dummy;
       const int ahead = c + 2;
       if (ahead < NCH) {
         load_a(rp, ahead, set((ahead + PAR) % 3));
