@@ -279,11 +279,14 @@ cnhwc_status_t validate(const cnhwc_conv_desc_t* desc, const cnhwc_plan_t* plan,
   const uint64_t es = dtype_size(desc->dtype);
   const uint64_t xb = uint64_t(desc->n) * desc->d * desc->h * desc->w * desc->c * es;
   const uint64_t yb = uint64_t(desc->n) * plan->out_d * plan->out_h * plan->out_w * desc->o * es;
-  if (overlaps(x, xb, y, yb)) return CNHWC_ERR_INVALID_ARGUMENT;
+  const uint64_t wb = uint64_t(desc->o) * desc->kd * desc->kh * desc->kw * desc->c * es;
+  // the written buffers (y, the workspace) may not overlap anything else; x and w may share memory
+  if (overlaps(x, xb, y, yb) || overlaps(w, wb, y, yb)) return CNHWC_ERR_INVALID_ARGUMENT;
   if (plan->workspace_bytes > 0) {
     if (ws_bytes < plan->workspace_bytes) return CNHWC_ERR_WORKSPACE_TOO_SMALL;
     if (!ws || !aligned16(ws)) return CNHWC_ERR_INVALID_ARGUMENT;
-    if (overlaps(ws, plan->workspace_bytes, y, yb) || overlaps(ws, plan->workspace_bytes, x, xb))
+    const uint64_t wsb = plan->workspace_bytes;
+    if (overlaps(ws, wsb, y, yb) || overlaps(ws, wsb, x, xb) || overlaps(ws, wsb, w, wb))
       return CNHWC_ERR_INVALID_ARGUMENT;
   }
   return CNHWC_OK;

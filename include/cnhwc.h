@@ -249,7 +249,9 @@ cnhwc_status_t cnhwc_winograd_tile_rule(uint64_t ws_limit, uint64_t own_bytes,
  * this desc; re-derived and compared, CNHWC_ERR_PLAN_MISMATCH otherwise).
  * x, w, y: device pointers, 16-byte aligned, layouts above, not overlapping y.
  * workspace: device pointer, 16-byte aligned, >= plan.workspace_bytes (may be
- * NULL when that is 0); contents on entry are ignored, on exit undefined.
+ * NULL when that is 0), not overlapping x, w or y; contents on entry are
+ * ignored, on exit undefined.  x and w may overlap each other (both are only
+ * read); any other overlap is CNHWC_ERR_INVALID_ARGUMENT.
  * hip_stream: a hipStream_t (NULL = default stream).
  * Winograd runs the batch in plan.n_tiles tiles of plan.tile_batch elements
  * (the last may be shorter) through one workspace; the result is bit-identical

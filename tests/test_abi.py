@@ -73,6 +73,17 @@ def test_null_and_misaligned_pointers():
     assert _call(f, d, p, y=X) == 1  # y overlaps x
 
 
+def test_overlapping_buffers():
+    """y and the workspace may overlap nothing; x and w may share memory."""
+    d, p = _wino()
+    f = cn.lib.cnhwc_conv2d_fwd
+    wb = 96 * 9 * 64 * 4
+    assert _call(f, d, p, y=W + wb - 256) == 1     # y starts inside w
+    assert _call(f, d, p, ws=W + 256) == 1         # workspace inside w
+    assert _call(f, d, p, ws=Y + 256) == 1         # workspace inside y
+    assert _call(f, d, p, ws=X) == 1               # workspace on x
+
+
 def test_plan_mismatch():
     d, p = _wino()
     p.tile_batch = 1
