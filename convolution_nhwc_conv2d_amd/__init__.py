@@ -286,19 +286,30 @@ def _run(fn, x, w, stride, padding, dilation, opts, out, workspace, plan, timer=
     nbytes = int(plan.workspace_bytes)
     if workspace is None and nbytes > 0:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=x.device)
+    if out.device != x.device or (workspace is not None and workspace.device != x.device):
+        raise TypeError("out and workspace must be on x's device")
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
     stream = torch.cuda.current_stream(x.device).cuda_stream
-    if timer is None:
-        st = fn(ctypes.byref(desc), ctypes.byref(plan), x.data_ptr(), w.data_ptr(), out.data_ptr(),
-                ws_ptr, ws_len, stream)
-    else:
+
+    def call():
+        if timer is None:
+            return fn(ctypes.byref(desc), ctypes.byref(plan), x.data_ptr(), w.data_ptr(), out.data_ptr(),
+                      ws_ptr, ws_len, stream)
         n = lib.cnhwc_launch_count(ctypes.byref(desc), ctypes.byref(plan)) + 1
         ev, kinds = timer.slots(n)
-        st = fn(ctypes.byref(desc), ctypes.byref(plan), x.data_ptr(), w.data_ptr(), out.data_ptr(),
-                ws_ptr, ws_len, stream, ev, n, kinds)
-        if st == 0:
+        st_ = fn(ctypes.byref(desc), ctypes.byref(plan), x.data_ptr(), w.data_ptr(), out.data_ptr(),
+                 ws_ptr, ws_len, stream, ev, n, kinds)
+        if st_ == 0:
             timer.recorded(n)
+        return st_
+
+    # kernels launch on the current device, which must be the one the stream and tensors are on
+    if x.device.index != torch.cuda.current_device():
+        with torch.cuda.device(x.device):
+            st = call()
+    else:
+        st = call()
     if st != 0:
         raise CnhwcError(st, fn.__name__)
     return out
