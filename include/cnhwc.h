@@ -215,10 +215,21 @@ const char* cnhwc_status_string(cnhwc_status_t s);
  *   force_gemm_config may name 14 or 15 (the 256-row tiles); force_split_k is
  *   ignored.  AUTO takes it by rule 1b.  Error: |y - conv| stays below
  *   5e-3 of sum |x||w| on independent, identically distributed data (the fp16
- *   rounding of the transformed operands; about 1e-3 at C = 256).  Like any
- *   Winograd form its error scales with the magnitudes in a whole tile, not
- *   in one window, and an output whose window only holds values below about
- *   2^-24 of max|x| loses relative precision (fp16 subnormals).
+ *   rounding of the transformed operands; about 1e-3 at C = 256); see the
+ *   accuracy note below for data with sharp contrast.  An output whose whole
+ *   tile only holds values below about 2^-24 of max|x| also loses relative
+ *   precision (fp16 subnormals).
+ * Accuracy of both Winograd forms: the transforms round a tile's values at
+ *   the scale of the largest ones in it, so the error is bounded relative to
+ *   the tile, |y - conv| <= tol * (largest sum|x||w| among the outputs of the
+ *   same tile: 6x6 outputs for WINOGRAD, 4x4 for WINOGRAD_HALF), with tol
+ *   2e-5 (F32) and 1e-2 (F16/BF16).  Without sharp contrast inside a tile
+ *   that is the per-output bound.  An output whose own window is 100x dimmer
+ *   than the brightest part of its tile exceeds the per-output bound
+ *   (measured: 2.7e-5 of its own sum |x||w| for WINOGRAD, 1.5-1.7e-2 for
+ *   WINOGRAD_HALF; 2.9e-4 and 0.14-0.20 at 1000x).  The implicit and unfold
+ *   GEMMs meet the per-output bound at any contrast.  Selection depends on
+ *   shapes only, so a caller with such data forces IMPLICIT_GEMM.
  * Forcing: WINOGRAD needs only 3x3/stride 1/dilation 1 (the channel gates are
  *   skipped); a forced tile size is capped by the budget tile (tiling page,
  *   Testing).  SMALL_KD needs N == 1, depth stride 1, depth dilation 1, depth

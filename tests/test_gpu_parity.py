@@ -484,6 +484,43 @@ def test_winograd_half_input_range(dt, scale):
     assert err < WH_BOUND[y.dtype], err
 
 
+def _tile_max(den, t):
+    """Per output: the largest den among the outputs of its t x t Winograd tile
+    (same image, same output channel)."""
+    out = np.empty_like(den)
+    for i in range(0, den.shape[1], t):
+        for j in range(0, den.shape[2], t):
+            out[:, i:i + t, j:j + t] = den[:, i:i + t, j:j + t].max(axis=(1, 2), keepdims=True)
+    return out
+
+
+@pytest.mark.parametrize("algo,dt,tile", [("winograd", "f32", 6), ("winograd_half", "f16", 4),
+                                          ("winograd_half", "bf16", 4), ("implicit_gemm", "f32", 1),
+                                          ("implicit_gemm", "bf16", 1)])
+@pytest.mark.parametrize("contrast", [0.1, 1e-3])
+def test_winograd_error_is_tile_relative(algo, dt, tile, contrast):
+    """A sharp edge: the left 11 columns of every image are `contrast` times
+    smaller than the rest.  The Winograd transforms round each tile's values
+    at the scale of the largest ones in it, so an output whose own window is
+    dim but whose tile reaches the bright side carries an error relative to
+    the tile: |err| <= tol * (largest sum|x||w| among its tile's outputs).
+    At 10x contrast that is still within the per-output bound; the implicit
+    GEMM meets the per-output bound at any contrast."""
+    case = cw.ConvCase(f"edge_{algo}_{dt}", 2, 26, 27, 32, 24, 3, 3, (1, 1), (1, 1), (1, 1), dt, "uniform",
+                       "normal", None, 91, 0)
+    x = case.input().float()
+    x[:, :, :11] *= contrast
+    x = x.to(cw.DTYPES[dt])
+    wt = case.weight()
+    yr, den = oracle.conv(to_oracle(x), to_oracle(wt), **case.conv_kwargs())
+    y = cn.conv2d(_dev(x), _dev(wt), **case.conv_kwargs(), algo=algo, out=poisoned(yr.shape, x.dtype))
+    err = np.abs(y.cpu().double().numpy() - yr)
+    tol = TOL[x.dtype]
+    assert np.all(err <= tol * _tile_max(den, tile)), float((err / _tile_max(den, tile)).max())
+    if contrast >= 0.1 or algo == "implicit_gemm":
+        check_parity(y.cpu(), yr, den, x.dtype, case.name)
+
+
 # (name, n, d, h, w, c, o, kd, pad (d, h, w), dilation (d, h, w), dtype)
 WH3D_CASES = [
     ("video_like", 1, 7, 16, 20, 64, 64, 3, (0, 1, 1), (1, 1, 1), "bf16"),
