@@ -90,6 +90,59 @@ def test_fp32_geometry(k, s, d, p):
             check_parity(y.cpu(), yr, den, y.dtype, f"{case.name}/{algo}")
 
 
+# ------------------------------------------------------- degenerate geometries
+
+# (name, n, h, w, c, o, k, stride, pad, dilation)
+DEGENERATE = [
+    ("pixel_1x1", 3, 1, 1, 1, 1, 1, 1, 0, 1),          # a scalar multiply per element
+    ("one_channel_3x3", 2, 5, 7, 1, 1, 3, 1, 1, 1),
+    ("kernel_is_image", 2, 5, 5, 8, 3, 5, 1, 0, 1),     # one output pixel
+    ("stride_past_image", 1, 3, 4, 8, 5, 3, 5, 0, 1),   # OH = OW = 1
+    ("padding_only_windows", 2, 2, 2, 16, 7, 3, 1, 2, 1),  # corner outputs see only padding
+    ("one_output_channel_wide_k", 1, 6, 6, 1000, 1, 3, 1, 1, 1),
+    ("image_1x1_pad1", 2, 1, 1, 16, 20, 3, 1, 1, 1),    # one Winograd tile, 8 of 9 taps padding
+    ("dilated_past_image", 1, 4, 4, 8, 4, 3, 1, 2, 3),  # taps land outside the image
+]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("spec", DEGENERATE, ids=[d[0] for d in DEGENERATE])
+def test_degenerate_geometries(spec, dtype):
+    """Tiny and extreme shapes on every algorithm that accepts them; outputs
+    whose windows hold only padding must be exactly zero."""
+    name, n, h, w, c, o, k, s, p, d = spec
+    case = cw.ConvCase(f"deg_{name}_{dtype}", n, h, w, c, o, k, k, (s, s), (p, p), (d, d), dtype, "normal",
+                       "normal", None, 17, c + o + k)
+    x, wt = case.input(), case.weight()
+    yr, den = oracle.conv(to_oracle(x), to_oracle(wt), **case.conv_kwargs())
+    algos = ["auto", "implicit_gemm", "unfold_gemm"]
+    if k == 3 and s == 1 and d == 1:
+        algos.append("winograd")
+        if dtype != "f32" and p <= 1 and c >= 16:
+            algos.append("winograd_half")
+    for algo in algos:
+        y = cn.conv2d(_dev(x), _dev(wt), **case.conv_kwargs(), algo=algo, out=poisoned(yr.shape, x.dtype))
+        check_parity(y.cpu(), yr, den, y.dtype, f"{case.name}/{algo}")
+
+
+def test_degenerate_conv1d_and_3d():
+    """conv1d of length-1 signals; a 3D conv whose output has one frame."""
+    x1 = torch.randn((3, 1, 24), dtype=torch.float16)
+    w1 = torch.randn((5, 3, 24), dtype=torch.float16) / 8
+    y1 = cn.conv1d(_dev(x1), _dev(w1), 1, 1)
+    yr, den = oracle.conv(to_oracle(x1.unsqueeze(1)), to_oracle(w1.unsqueeze(1)), stride=(1, 1), padding=(0, 1),
+                          dilation=(1, 1))
+    check_parity(y1.unsqueeze(1).cpu(), yr, den, y1.dtype, "conv1d_len1")
+    case = cw.ConvCase("deg3d", 1, 6, 5, 32, 16, 3, 3, (1, 1, 1), (0, 1, 1), (1, 1, 1), "bf16", "normal", "normal",
+                       None, 18, 0, nd=3, d=3, kd=3)
+    x, wt = case.input(), case.weight()
+    yr, den = oracle.conv(to_oracle(x), to_oracle(wt), **case.conv_kwargs())
+    for algo in ("auto", "implicit_gemm", "small_kd", "winograd_half"):
+        y = cn.conv3d(_dev(x), _dev(wt), **case.conv_kwargs(), algo=algo, out=poisoned(yr.shape, x.dtype))
+        assert y.shape[1] == 1
+        check_parity(y.cpu(), yr, den, y.dtype, f"deg3d/{algo}")
+
+
 # ------------------------------------------- integer data: exact in every dtype
 
 @pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
