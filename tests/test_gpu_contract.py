@@ -165,3 +165,26 @@ def test_empty_batch_returns_an_empty_output():
     x1 = torch.empty((0, 50, 16), dtype=torch.float16, device="cuda")
     w1 = torch.zeros((24, 3, 16), dtype=torch.float16, device="cuda")
     assert cn.conv1d(x1, w1, 1, 1).shape == (0, 50, 24)
+
+
+@pytest.mark.parametrize("algo,dt", [("winograd", "f32"), ("winograd_half", "bf16"), ("implicit_gemm", "f16")])
+def test_concurrent_calls_on_two_streams(algo, dt):
+    """The library keeps no mutable state of its own (scales, partial maxima
+    and transformed operands live in the caller's workspace), so calls queued
+    on two streams at once give the bits each gives alone."""
+    cases = [_case2(dt, seed=90 + i) for i in range(2)]
+    xs = [c.input().cuda() for c in cases]
+    ws_ = [c.weight().cuda() for c in cases]
+    alone = [cn.conv2d(x, w, 1, 1, 1, algo=algo) for x, w in zip(xs, ws_)]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    ys = [None, None]
+    ev = torch.cuda.Event()
+    ev.record()
+    for i in range(2):
+        streams[i].wait_event(ev)
+        with torch.cuda.stream(streams[i]):
+            ys[i] = cn.conv2d(xs[i], ws_[i], 1, 1, 1, algo=algo)
+    torch.cuda.synchronize()
+    for y, a in zip(ys, alone):
+        assert torch.equal(bits(y), bits(a))
