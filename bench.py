@@ -60,7 +60,8 @@ def parse():
                          "with --calib-copy, write profiles/traffic.json, print it and exit")
     ap.add_argument("--suite", default=None,
                     help="instead of the headline line, time other workloads: "
-                         "comma list of small,wide,sweep,wino_half,resnet,video,video_auto,conv1d,vendor_gemm "
+                         "comma list of small,wide,sweep,wino_half,resnet,video,video_auto,video_gemm,conv1d,"
+                         "vendor_gemm "
                          "or 'all' "
                          "(one JSON line each)")
     return ap.parse_args()
@@ -391,6 +392,15 @@ def run_suite(names):
                                 ("auto", "unfold_gemm")):
                 r = measure(case, algo, inner=inner)
                 r["suite"] = "video3d"
+                emit(r)
+    if "video_gemm" in names:
+        # the GEMM-only paths on the video shapes, for profiles: the native 3D
+        # implicit GEMM and the per-tap decomposition with each inner path
+        for shape in cw.VIDEO3D_SHAPES:
+            case = cw.video3d(*shape)
+            for algo, inner in (("implicit_gemm", None), ("small_kd", "implicit_gemm"), ("small_kd", "unfold_gemm")):
+                r = measure(case, algo, inner=inner)
+                r["suite"] = "video3d_gemm"
                 emit(r)
     if "video_auto" in names:
         # the AUTO path alone (half-precision Winograd) on the video shapes, for profiles
