@@ -239,7 +239,9 @@ def test_conv3d_kd1_bit_identical_to_conv2d(dtype):
 # ------------------------------- 256x256 tile with direct loads into LDS
 # Shapes chosen to span several row and column tiles with ragged tails, every
 # filter geometry of the half grid, and C = 32 / 64 / 96 / 128 (the tile needs
-# C % 32 == 0 for the implicit gather, K % 8 == 0 for unfold rows).
+# C % 32 == 0 for the implicit gather, K % 8 == 0 for unfold rows; with
+# C % 64 == 0 the 256 x 256 tile gathers in 64-element chunks, so both of its
+# chunk forms are compared with the 128 x 128 tile's bits).
 
 LDS_CASES = [  # name, n, h, w, c, o, k, stride, pad, dil
     ("c64_o300", 2, 20, 20, 64, 300, 3, 1, 1, 1),
