@@ -122,7 +122,10 @@ def _load():
                        ctypes.c_int32, P(ctypes.c_int32)]
     lib.cnhwc_launch_count.restype = ctypes.c_int64
     lib.cnhwc_launch_count.argtypes = [P(Desc), P(Plan)]
-    if lib.cnhwc_abi_version() != 3:
+    lib.cnhwc_conv2d_fwd_noalloc.restype = ctypes.c_int
+    lib.cnhwc_conv2d_fwd_noalloc.argtypes = [P(Desc), P(Plan), ctypes.c_void_p, ctypes.c_void_p,
+                                             ctypes.c_void_p, ctypes.c_void_p]
+    if lib.cnhwc_abi_version() != 4:
         raise ImportError("libcnhwc.so ABI version mismatch")
     return lib
 
@@ -131,7 +134,11 @@ lib = _load()
 
 EXPORTED = ("cnhwc_abi_version", "cnhwc_status_string", "cnhwc_conv_select",
             "cnhwc_winograd_tile_rule", "cnhwc_conv2d_fwd", "cnhwc_conv3d_fwd",
-            "cnhwc_launch_count", "cnhwc_conv2d_fwd_timed", "cnhwc_conv3d_fwd_timed")
+            "cnhwc_launch_count", "cnhwc_conv2d_fwd_timed", "cnhwc_conv3d_fwd_timed",
+            "cnhwc_conv2d_fwd_noalloc")
+
+# Bytes of the fixed device array cnhwc_conv2d_fwd_noalloc uses as its workspace.
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 KERNEL_KINDS = {0: "end", 1: "wino_filter", 2: "wino_input", 3: "wino_gemm", 4: "wino_output",
                 5: "implicit_gemm", 6: "unfold", 7: "unfold_gemm", 8: "splitk_reduce",
@@ -392,6 +399,33 @@ def conv2d(x, w, stride=1, padding=0, dilation=1, *, algo="auto", ws_limit=None,
         device=x.device if x.is_cuda else None)
     fn = lib.cnhwc_conv2d_fwd_timed if timer is not None else lib.cnhwc_conv2d_fwd
     return _run(fn, x, w, stride, padding, dilation, opts, out, workspace, plan, timer)
+
+
+def conv2d_noalloc(x, w, out, stride=1, padding=0, dilation=1, *, plan=None, algo="auto", ws_limit=None,
+                   tile_batch=None, unfold_rows=None, gemm_config=None, split_k=None):
+    """conv2d through cnhwc_conv2d_fwd_noalloc: the library takes the workspace
+    from its fixed per-GPU device array, so nothing is allocated for the call;
+    the caller passes the output ``out`` [N,OH,OW,O].  A plan whose workspace
+    exceeds NOALLOC_SCRATCH_BYTES raises CnhwcError (WORKSPACE_TOO_SMALL)."""
+    for t, name in ((x, "x"), (w, "w"), (out, "out")):
+        _check_tensor(t, name)
+    if w.dtype != x.dtype or out.dtype != x.dtype or w.device != x.device or out.device != x.device:
+        raise TypeError("x, w and out must share dtype and device")
+    desc = make_desc(tuple(x.shape), tuple(w.shape), stride, padding, dilation, x.dtype)
+    if desc.nd != 2:
+        raise ValueError("conv2d_noalloc: x must be 4-D (NHWC)")
+    if plan is None:
+        plan = select(desc, make_opts(ws_limit, algo, "auto", tile_batch, unfold_rows, gemm_config=gemm_config,
+                                      split_k=split_k, device=x.device))
+    if tuple(out.shape) != (x.shape[0], plan.out_h, plan.out_w, w.shape[0]):
+        raise ValueError("out has the wrong shape")
+    with torch.cuda.device(x.device):
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+        st = lib.cnhwc_conv2d_fwd_noalloc(ctypes.byref(desc), ctypes.byref(plan), x.data_ptr(), w.data_ptr(),
+                                          out.data_ptr(), stream)
+    if st != 0:
+        raise CnhwcError(st, "cnhwc_conv2d_fwd_noalloc")
+    return out
 
 
 def conv3d(x, w, stride=1, padding=0, dilation=1, *, algo="auto", inner_algo="auto", ws_limit=None,

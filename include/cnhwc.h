@@ -31,6 +31,8 @@
  * stream; they must stay valid until the work queued on the stream completes.
  * The library allocates no device memory, keeps no global state, never
  * synchronises and reads no environment variable.  Every call is thread-safe.
+ * (The one exception is cnhwc_conv2d_fwd_noalloc, which takes its workspace
+ * from a fixed device array the library holds per GPU; see there.)
  * The forward calls only queue kernels on the given HIP stream (NULL = the
  * default stream); device faults therefore surface at the caller's next
  * synchronisation.
@@ -53,7 +55,7 @@
 extern "C" {
 #endif
 
-#define CNHWC_ABI_VERSION 3
+#define CNHWC_ABI_VERSION 4
 
 /* Fewest GEMM rows (tile_batch * tiles_per_image) a Winograd batch tile may
  * carry when the batch does not fit in one tile; below it AUTO falls back to
@@ -320,6 +322,28 @@ cnhwc_status_t cnhwc_conv3d_fwd_timed(const cnhwc_conv_desc_t* desc, const cnhwc
                                       const void* x, const void* w, void* y, void* workspace,
                                       uint64_t workspace_bytes, void* hip_stream,
                                       void* const* events, int32_t n_events, int32_t* kinds);
+
+/* Bytes of the device array that cnhwc_conv2d_fwd_noalloc takes its workspace
+ * from (one array per GPU). */
+#define CNHWC_NOALLOC_SCRATCH_BYTES (64ull << 20)
+
+/* Allocation-free 2D forward, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation).  Identical work to cnhwc_conv2d_fwd, with the workspace taken
+ * from a CNHWC_NOALLOC_SCRATCH_BYTES device array that the library holds, one
+ * per GPU, until the process ends.  desc, plan, x, w and y follow
+ * cnhwc_conv2d_fwd; hip_stream must belong to the current device
+ * (CNHWC_ERR_INVALID_ARGUMENT otherwise).  A plan with workspace_bytes above
+ * CNHWC_NOALLOC_SCRATCH_BYTES is CNHWC_ERR_WORKSPACE_TOO_SMALL and nothing is
+ * queued: plan such convs with a smaller ws_limit_bytes, tile or unfold row
+ * count.  The call allocates nothing (no hipMalloc or hipFree).  All calls on
+ * one GPU share its array; every kernel writes the scratch it reads within
+ * the same call, so nothing carries over between calls, but calls whose work
+ * overlaps in time on one GPU (two streams or two threads) race on the array:
+ * the caller serialises them.  The first call on a device looks the array's
+ * address up (hipGetSymbolAddress); make it outside graph capture. */
+cnhwc_status_t cnhwc_conv2d_fwd_noalloc(const cnhwc_conv_desc_t* desc, const cnhwc_plan_t* plan,
+                                        const void* x, const void* w, void* y, void* hip_stream);
 
 #ifdef __cplusplus
 }
