@@ -67,13 +67,15 @@ cnhwc_status_t run_wino_h(const cnhwc_conv_desc_t& d, const cnhwc_plan_t& p, con
   uint16_t* U = reinterpret_cast<uint16_t*>(ws + L.off_u);
   uint16_t* V = reinterpret_cast<uint16_t*>(ws + L.off_v);
   float* Mt = reinterpret_cast<float*>(ws + L.off_m);
+  uint32_t* wm = reinterpret_cast<uint32_t*>(ws + L.off_wm);
+  uint64_t* tm = reinterpret_cast<uint64_t*>(ws + L.off_tm);
   const int64_t nx = d.n * d.d * d.h * d.w * d.c;
   const int64_t nw = d.o * d.kd * d.kh * d.kw * d.c;
   rec.mark(CNHWC_KERNEL_WINO_SCALE);
   if (wino_h_absmax_launch(d.dtype, x, nx, w, nw, partial, stream) != hipSuccess) return CNHWC_ERR_HIP;
   rec.mark(CNHWC_KERNEL_WINO_FILTER);
-  if (wino_h_filter_launch(d.dtype, w, d.o, d.kd, d.c, L.cs, partial, nx, nw, scales, U, stream) !=
-      hipSuccess)
+  if (wino_h_filter_launch(d.dtype, w, d.o, d.kd, d.c, L.cs, partial, nx, nw, scales, U, wm,
+                           stream) != hipSuccess)
     return CNHWC_ERR_HIP;
 
   GemmParams q;
@@ -106,7 +108,7 @@ cnhwc_status_t run_wino_h(const cnhwc_conv_desc_t& d, const cnhwc_plan_t& p, con
     rec.mark(CNHWC_KERNEL_WINO_INPUT);
     if (wino_h_input_launch(d.dtype, static_cast<const char*>(x) + n0 * x_elem, nb, d.d, L.dp,
                             d.pad[0], d.h, d.w, d.c, L.cs, d.pad[1], d.pad[2], L.tiles_h,
-                            L.tiles_w, scales, V, int64_t(L.v_plane), stream) != hipSuccess)
+                            L.tiles_w, scales, V, int64_t(L.v_plane), tm, stream) != hipSuccess)
       return CNHWC_ERR_HIP;
     rec.mark(CNHWC_KERNEL_WINO_GEMM);
     q.M = nb * p.out_d * L.t;
@@ -114,8 +116,8 @@ cnhwc_status_t run_wino_h(const cnhwc_conv_desc_t& d, const cnhwc_plan_t& p, con
     if (gemm_launch(q, stream) != hipSuccess) return CNHWC_ERR_HIP;
     rec.mark(CNHWC_KERNEL_WINO_OUTPUT);
     if (wino_h_output_launch(d.dtype, Mt, int64_t(L.m_plane), nb * p.out_d, p.out_h, p.out_w, d.o,
-                             L.tiles_h, L.tiles_w, scales, static_cast<char*>(y) + n0 * y_elem,
-                             stream) != hipSuccess)
+                             L.tiles_h, L.tiles_w, scales, static_cast<char*>(y) + n0 * y_elem, tm,
+                             d.c, L.cs, wm, p.out_d, L.dp, d.kd, d.dil[0], stream) != hipSuccess)
       return CNHWC_ERR_HIP;
   }
   return CNHWC_OK;
@@ -215,8 +217,10 @@ cnhwc_status_t run_2d(const cnhwc_conv_desc_t& d, const cnhwc_plan_t& p, int32_t
     float* U = reinterpret_cast<float*>(ws + L.off_u);
     float* V = reinterpret_cast<float*>(ws + L.off_v);
     float* Mt = reinterpret_cast<float*>(ws + L.off_m);
+    uint32_t* wm = reinterpret_cast<uint32_t*>(ws + L.off_wm);
+    uint64_t* tm = reinterpret_cast<uint64_t*>(ws + L.off_tm);
     rec.mark(CNHWC_KERNEL_WINO_FILTER);
-    int e = wino_filter_launch(d.dtype, w, ldw, d.o, d.c, L.cs, U, stream);
+    int e = wino_filter_launch(d.dtype, w, ldw, d.o, d.c, L.cs, U, wm, stream);
     if (e != hipSuccess) return CNHWC_ERR_HIP;
     const uint64_t x_elem = uint64_t(d.h) * d.w * d.c * es;  // bytes of one image
     const uint64_t y_elem = uint64_t(oh) * ow * d.o;         // elements of one output image
@@ -225,7 +229,7 @@ cnhwc_status_t run_2d(const cnhwc_conv_desc_t& d, const cnhwc_plan_t& p, int32_t
       rec.mark(CNHWC_KERNEL_WINO_INPUT);
       e = wino_input_launch(d.dtype, static_cast<const char*>(x) + n0 * x_elem, nb, d.h, d.w, d.c,
                             L.cs, d.pad[1], d.pad[2], L.tiles_h, L.tiles_w, V, int64_t(L.v_plane),
-                            stream);
+                            tm, stream);
       if (e != hipSuccess) return CNHWC_ERR_HIP;
       rec.mark(CNHWC_KERNEL_WINO_GEMM);
       if (p.kernel_config == kCfgWinoResident) {
@@ -257,7 +261,7 @@ cnhwc_status_t run_2d(const cnhwc_conv_desc_t& d, const cnhwc_plan_t& p, int32_t
       rec.mark(CNHWC_KERNEL_WINO_OUTPUT);
       e = wino_output_launch(d.dtype, Mt, int64_t(L.m_plane), nb, oh, ow, d.o, L.tiles_h,
                              L.tiles_w, static_cast<char*>(y) + n0 * y_elem * es,
-                             acc ? acc + n0 * y_elem : nullptr, epi, stream);
+                             acc ? acc + n0 * y_elem : nullptr, epi, tm, L.cs, wm, stream);
       if (e != hipSuccess) return CNHWC_ERR_HIP;
     }
     return CNHWC_OK;

@@ -21,6 +21,9 @@ constexpr int kWinoHP = 36;
 // Channel stride of its fp16 rows: C rounded up to 32, one K chunk of the
 // 256-row GEMM tiles, so a 3D tap's K range starts on a chunk.
 inline int64_t wino_h_cs(int64_t c) { return (c + 31) / 32 * 32; }
+// Channels per thread of its input transform (4 when C % 4 == 0, 2 when C is
+// even): the transform runs cs / vec threads per tile row.
+inline int64_t wino_h_vec(int64_t c) { return c % 4 == 0 ? 4 : (c % 2 == 0 ? 2 : 1); }
 // Partial maxima per tensor (one per block of the max-|element| pass).
 constexpr int32_t kWinoHSlots = 1024;
 inline int32_t wino_h_absmax_blocks(int64_t n) {
@@ -134,21 +137,27 @@ int wino_h_absmax_launch(int dtype, const void* x, int64_t nx, const void* w, in
                          uint32_t* partial, void* stream);
 // U[p][o][kd*cs + c] = fp16(G (sw g) G^T)_p, g = w[o][kd][kh][kw][c] (KD = kd planes);
 // the scales come from the partial maxima, and scales = {sx, sw, a, b} with
-// a b = 1/(sx sw) is stored for the transforms that follow.
+// a b = 1/(sx sw) is stored for the transforms that follow.  wm[o*kd + k]:
+// bit kh*3 + kw set iff some channel of tap (kh, kw) of slice (o, k) is nonzero.
 int wino_h_filter_launch(int dtype, const void* w, int64_t o, int64_t kd, int64_t c, int64_t cs,
                          const uint32_t* partial, int64_t nx, int64_t nw, float* scales, uint16_t* u,
-                         void* stream);
+                         uint32_t* wm, void* stream);
 // V[p][r][c] = fp16(sx (B^T d B)_p) over nb elements of dp frames each (frame
 // f reads input frame f - pd, zero outside [0, d)); plane stride `plane`.
+// tm[r][wino_mask_parts(cs / wino_h_vec(c))]: the parts of tile r's
+// nonzero-pixel mask.
 int wino_h_input_launch(int dtype, const void* x, int64_t nb, int64_t d, int64_t dp, int32_t pd,
                         int64_t h, int64_t w, int64_t c, int64_t cs, int32_t ph, int32_t pw,
                         int64_t th, int64_t tw, const float* scales, uint16_t* v, int64_t plane,
-                        void* stream);
+                        uint64_t* tm, void* stream);
 // y = (A^T M A) / (sx sw) per tile and output channel for nimg output images
-// (or frames), cropped to [oh, ow].
+// (or frames: od per element, whose taps read dp-frame input rows at depth
+// dilation dd over kd taps), cropped to [oh, ow].  Outputs with no nonzero
+// pixel under a nonzero tap (tm, wm above) take 0.
 int wino_h_output_launch(int dtype, const float* m, int64_t plane, int64_t nimg, int64_t oh,
                          int64_t ow, int64_t o, int64_t th, int64_t tw, const float* scales,
-                         void* y, void* stream);
+                         void* y, const uint64_t* tm, int64_t c, int64_t cs, const uint32_t* wm,
+                         int64_t od, int64_t dp, int64_t kd, int64_t dd, void* stream);
 
 // ------------------------------------------------------------- Unfold
 
@@ -168,20 +177,24 @@ inline int64_t unfold_kp(int64_t k, int dtype) {
 // ------------------------------------------------------------ planner
 
 // Winograd workspace layout for a 2D conv and a tile size.
+// Tap masks (uint32 per output channel) follow U; the tile masks
+// (wino_mask_parts(cs) uint64 per tile row) follow M.
 struct WinoLayout {
-  int64_t tiles_h, tiles_w, t, cs;
-  uint64_t u_bytes, v_plane, m_plane;  // plane strides in elements
-  uint64_t off_u, off_v, off_m, total;
+  int64_t tiles_h, tiles_w, t, cs, mask_parts;
+  uint64_t u_bytes, wm_bytes, v_plane, m_plane;  // plane strides in elements
+  uint64_t off_u, off_wm, off_v, off_m, off_tm, total;
 };
 WinoLayout wino_layout(const cnhwc_conv_desc_t& d2, int64_t oh, int64_t ow, int64_t tile_batch);
 
 // Half-precision Winograd workspace layout (2D: od = 1, depth pad 0; 3D: one
 // batch element per tile).  Frames per element dp = D + 2 pd; the GEMM K is
 // ku = KD * cs.
+// Tap masks (uint32 per (o, kd)) follow U; the tile masks
+// (wino_mask_parts(cs / wino_h_vec(c)) uint64 per input tile row) follow M.
 struct WinoHLayout {
-  int64_t tiles_h, tiles_w, t, cs, dp, ku;
-  uint64_t u_bytes, v_plane, m_plane;  // plane strides in elements
-  uint64_t off_u, off_v, off_m, total;
+  int64_t tiles_h, tiles_w, t, cs, dp, ku, mask_parts;
+  uint64_t u_bytes, wm_bytes, v_plane, m_plane;  // plane strides in elements
+  uint64_t off_u, off_wm, off_v, off_m, off_tm, total;
 };
 WinoHLayout wino_h_layout(const cnhwc_conv_desc_t& d, int64_t od, int64_t oh, int64_t ow,
                           int64_t tile_batch);

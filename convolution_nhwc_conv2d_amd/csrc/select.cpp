@@ -228,8 +228,10 @@ cnhwc_status_t plan_winograd_h(const cnhwc_conv_desc_t& d, const int64_t out[3],
   const WinoHLayout one = wino_h_layout(d, out[0], out[1], out[2], 1);
   const uint64_t own = uint64_t(d.n) * d.d * d.h * d.w * d.c * es +
                        uint64_t(d.n) * out[0] * out[1] * out[2] * d.o * es + kWinoHHeadBytes +
-                       align_up(one.u_bytes, 256);
-  const uint64_t scratch = uint64_t(kWinoHP) * one.t * (one.dp * one.cs * 2 + out[0] * d.o * 4);
+                       align_up(one.u_bytes, 256) + align_up(one.wm_bytes, 256);
+  // V + M + the tile masks of one element
+  const uint64_t scratch = uint64_t(kWinoHP) * one.t * (one.dp * one.cs * 2 + out[0] * d.o * 4) +
+                           uint64_t(one.dp) * one.t * one.mask_parts * 8;
   int64_t tb;
   uint64_t budget;
   int32_t fb;
@@ -280,9 +282,12 @@ cnhwc_status_t select_2d(const cnhwc_conv_desc_t& d, const int64_t out[3],
   if (force == CNHWC_ALGO_WINOGRAD && !winograd_geometry(d)) return CNHWC_ERR_NOT_APPLICABLE;
   if (try_wino) {
     const WinoLayout one = wino_layout(d, out[1], out[2], 1);
+    // own: x, y and the transformed filter (U and its tap masks)
     const uint64_t own = uint64_t(d.n) * d.h * d.w * d.c * es +
-                         uint64_t(m_rows) * d.o * es + one.u_bytes;
-    const uint64_t scratch = uint64_t(kWinoP) * one.t * (one.cs + d.o) * 4;  // V + M of one element
+                         uint64_t(m_rows) * d.o * es + one.u_bytes + one.wm_bytes;
+    // V + M + the tile masks of one element
+    const uint64_t scratch =
+        uint64_t(kWinoP) * one.t * (one.cs + d.o) * 4 + uint64_t(one.t) * one.mask_parts * 8;
     int64_t tb;
     uint64_t budget;
     int32_t fb;
@@ -444,14 +449,18 @@ WinoLayout wino_layout(const cnhwc_conv_desc_t& d, int64_t oh, int64_t ow, int64
   l.tiles_w = ceil_div(ow, kWinoM);
   l.t = l.tiles_h * l.tiles_w;
   l.cs = wino_cs(d.c);
+  l.mask_parts = wino_mask_parts(l.cs);
   const uint64_t rows = uint64_t(tb) * l.t;
   l.u_bytes = uint64_t(kWinoP) * d.o * l.cs * 4;
+  l.wm_bytes = uint64_t(d.o) * 4;
   l.v_plane = rows * l.cs;
   l.m_plane = rows * d.o;
   l.off_u = 0;
-  l.off_v = align_up(l.u_bytes, 256);
+  l.off_wm = align_up(l.u_bytes, 256);
+  l.off_v = l.off_wm + align_up(l.wm_bytes, 256);
   l.off_m = l.off_v + align_up(kWinoP * l.v_plane * 4, 256);
-  l.total = l.off_m + align_up(kWinoP * l.m_plane * 4, 256);
+  l.off_tm = l.off_m + align_up(kWinoP * l.m_plane * 4, 256);
+  l.total = l.off_tm + align_up(rows * l.mask_parts * 8, 256);
   return l;
 }
 
@@ -462,15 +471,20 @@ WinoHLayout wino_h_layout(const cnhwc_conv_desc_t& d, int64_t od, int64_t oh, in
   l.tiles_w = ceil_div(ow, kWinoHM);
   l.t = l.tiles_h * l.tiles_w;
   l.cs = wino_h_cs(d.c);
+  l.mask_parts = wino_mask_parts(l.cs / wino_h_vec(d.c));
   l.dp = d.d + 2 * int64_t(d.pad[0]);
   l.ku = d.kd * l.cs;
   l.u_bytes = uint64_t(kWinoHP) * d.o * l.ku * 2;
-  l.v_plane = uint64_t(tb) * l.dp * l.t * l.cs;
+  l.wm_bytes = uint64_t(d.o) * d.kd * 4;
+  const uint64_t in_rows = uint64_t(tb) * l.dp * l.t;
+  l.v_plane = in_rows * l.cs;
   l.m_plane = uint64_t(tb) * od * l.t * d.o;
   l.off_u = kWinoHHeadBytes;
-  l.off_v = l.off_u + align_up(l.u_bytes, 256);
+  l.off_wm = l.off_u + align_up(l.u_bytes, 256);
+  l.off_v = l.off_wm + align_up(l.wm_bytes, 256);
   l.off_m = l.off_v + align_up(kWinoHP * l.v_plane * 2, 256);
-  l.total = l.off_m + align_up(kWinoHP * l.m_plane * 4, 256);
+  l.off_tm = l.off_m + align_up(kWinoHP * l.m_plane * 4, 256);
+  l.total = l.off_tm + align_up(in_rows * l.mask_parts * 8, 256);
   return l;
 }
 

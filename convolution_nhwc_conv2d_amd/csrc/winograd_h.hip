@@ -28,12 +28,17 @@
 //   U [36][O][KD*Cs]    fp16, Cs = C rounded up to 32 (zero channels)
 //   V [36][rows][Cs]    fp16, rows = (image or frame) * tiles, frames padded by pd
 //   M [36][rows'][O]    fp32, rows' = output images or frames * tiles
+//   tap masks [O][KD]   nonzero 3x3 taps of each (o, kd) filter slice (uint32)
+//   tile masks [rows][P] nonzero pixels of each 6x6 input tile, in parts
+// The masks make an output whose products are all zero exactly zero (see
+// wino_mask.hpp); in 3D an output's window spans the KD frames its taps read.
 // Tile (ty, tx) covers input rows 4 ty - ph .. +5 and columns 4 tx - pw .. +5
 // and produces output rows 4 ty .. 4 ty + 3 (cropped).
 #include <hip/hip_runtime.h>
 
 #include "internal.hpp"
 #include "device_common.hpp"
+#include "wino_mask.hpp"
 #include "winograd_f43.h"
 
 namespace cnhwc {
@@ -145,6 +150,8 @@ __device__ __forceinline__ void block_scales(const uint32_t* __restrict__ partia
 // U[p][o][kd*Cs + c] = fp16((G (sw g) G^T)_p), g = w[o][kd][.][.][c]; zero for c >= C.
 // Every block first reduces the partial maxima to the scales (block 0 also
 // stores them for the input and output transforms, which run after it).
+// Workgroups [0, nfb) transform the filter; the workgroups after them compute
+// the tap masks, one wavefront per (o, kd) slice.
 template <bool BF16>
 __global__ __launch_bounds__(256) void wino_h_filter_kernel(const uint16_t* __restrict__ w,
                                                             int64_t O, int64_t KD, int64_t C,
@@ -152,7 +159,15 @@ __global__ __launch_bounds__(256) void wino_h_filter_kernel(const uint16_t* __re
                                                             const uint32_t* __restrict__ partial,
                                                             int32_t nbx, int32_t nbw,
                                                             float* __restrict__ scales,
-                                                            uint16_t* __restrict__ U) {
+                                                            uint16_t* __restrict__ U, int64_t nfb,
+                                                            uint32_t* __restrict__ wm) {
+  if (int64_t(blockIdx.x) >= nfb) {  // whole workgroups: uniform branch, no barrier below
+    const int64_t sl = (int64_t(blockIdx.x) - nfb) * 4 + (threadIdx.x >> 6);
+    if (sl >= O * KD) return;
+    const uint32_t bits = tap_mask_of(w + sl * 9 * C, C, [](uint16_t v) { return (v & 0x7fffu) != 0u; });
+    if ((threadIdx.x & 63) == 0) wm[sl] = bits;
+    return;
+  }
   __shared__ uint32_t sm[4];
   float sc[4];
   block_scales<BF16>(partial, nbx, nbw, sm, sc);
@@ -195,15 +210,21 @@ __global__ __launch_bounds__(256) void wino_h_filter_kernel(const uint16_t* __re
 // are the frames fp of nb elements with Dp frames each; frame fp reads input
 // frame fp - pd (zero outside [0, D)); 2D convs have D = Dp = 1, pd = 0.
 // VEC channels per thread (4 when C % 4 == 0, 2 when C is even: 8- or 4-byte
-// loads and stores).
-template <bool BF16, int VEC>
+// loads and stores).  Besides V it writes the tile's nonzero-pixel mask (bit
+// i * 6 + j for pixel (i, j)): with WAVE (Cs / VEC % 64 == 0) every wavefront
+// holds channels of one tile and stores its part from ballots; otherwise the
+// workgroup ORs its threads' masks.
+template <bool BF16, int VEC, bool WAVE>
 __global__ __launch_bounds__(256) void wino_h_input_kernel(
     const uint16_t* __restrict__ x, int64_t D, int64_t Dp, int32_t pd, int64_t H, int64_t W,
     int64_t C, int64_t Cs, int32_t ph, int32_t pw, int64_t TH, int64_t TW,
-    const float* __restrict__ scales, uint16_t* __restrict__ V, int64_t plane, int64_t total) {
-  const int64_t t = xcd_block(blockIdx.x, gridDim.x) * 256 + threadIdx.x;
-  if (t >= total) return;
+    const float* __restrict__ scales, uint16_t* __restrict__ V, int64_t plane, int64_t total,
+    uint64_t* __restrict__ tm, int64_t parts) {
+  const int64_t blk = xcd_block(blockIdx.x, gridDim.x);
+  const int64_t t = blk * 256 + threadIdx.x;
   const int64_t groups = Cs / VEC;
+  uint64_t pix = 0;  // WAVE: uniform over the wavefront; else this thread's channels
+  if (t < total) {
   const int64_t r = t / groups, c = (t - r * groups) * VEC;
   const int64_t T = TH * TW;
   const int64_t im = r / T, rr = r - im * T;
@@ -227,18 +248,28 @@ __global__ __launch_bounds__(256) void wino_h_input_kernel(
     for (int i = 0; i < kT; ++i) {
       const int64_t ih = ih0 + i;
       const bool ok = wok && ih >= 0 && ih < H;
+      uint32_t nz;  // nonzero bits of this pixel's VEC channels (sign bits dropped)
       if constexpr (VEC == 4) {
         const uint2 q = ok ? *reinterpret_cast<const uint2*>(img + (ih * W + iw) * C) : make_uint2(0u, 0u);
         col[0][i] = s * to_f32<uint16_t, BF16>(uint16_t(q.x & 0xffffu));
         col[1][i] = s * to_f32<uint16_t, BF16>(uint16_t(q.x >> 16));
         col[2][i] = s * to_f32<uint16_t, BF16>(uint16_t(q.y & 0xffffu));
         col[3][i] = s * to_f32<uint16_t, BF16>(uint16_t(q.y >> 16));
+        nz = (q.x | q.y) & 0x7fff7fffu;
       } else if constexpr (VEC == 2) {
         const uint32_t q = ok ? *reinterpret_cast<const uint32_t*>(img + (ih * W + iw) * C) : 0u;
         col[0][i] = s * to_f32<uint16_t, BF16>(uint16_t(q & 0xffffu));
         col[1][i] = s * to_f32<uint16_t, BF16>(uint16_t(q >> 16));
+        nz = q & 0x7fff7fffu;
       } else {
-        col[0][i] = ok ? s * to_f32<uint16_t, BF16>(img[(ih * W + iw) * C]) : 0.0f;
+        const uint16_t h = ok ? img[(ih * W + iw) * C] : uint16_t(0);
+        col[0][i] = s * to_f32<uint16_t, BF16>(h);
+        nz = h & 0x7fffu;
+      }
+      if constexpr (WAVE) {
+        if (__ballot(nz != 0u) != 0ull) pix |= 1ull << (i * kT + j);
+      } else {
+        pix |= uint64_t(nz != 0u) << (i * kT + j);
       }
     }
 #pragma unroll
@@ -273,11 +304,21 @@ __global__ __launch_bounds__(256) void wino_h_input_kernel(
       }
     }
   }
+  if constexpr (WAVE) {
+    if ((threadIdx.x & 63) == 0) tm[r * parts + (c / VEC) / 64] = pix;
+  }
+  }
+  if constexpr (!WAVE) store_block_masks(pix, t < total, t, blk, groups, total / groups, tm, parts);
 }
 
 // y[im][oh][ow][o] = (A^T M A)[oh - 4 ty][ow - 4 tx] / (sx sw), cropped to
 // [OH, OW], for output image or frame im.  VEC output channels per thread
 // (2 when O is even).
+// Outputs whose window (over the KD frames its taps read) meets no nonzero
+// pixel under a nonzero tap store an exact zero.  Output frame od of element n
+// reads input rows of padded frame od + kd * dd (Dp frames per element); the
+// input transform wrote their masks with g threads per tile row in `parts`
+// parts.  2D: OD = Dp = KD = 1.
 template <bool BF16, int VEC>
 __global__ __launch_bounds__(256) void wino_h_output_kernel(const float* __restrict__ Mt,
                                                             int64_t plane, int64_t OH,
@@ -285,7 +326,12 @@ __global__ __launch_bounds__(256) void wino_h_output_kernel(const float* __restr
                                                             int64_t TW,
                                                             const float* __restrict__ scales,
                                                             uint16_t* __restrict__ y,
-                                                            int64_t total) {
+                                                            int64_t total,
+                                                            const uint64_t* __restrict__ tm,
+                                                            int64_t g, int64_t parts,
+                                                            const uint32_t* __restrict__ wm,
+                                                            int64_t OD, int64_t Dp, int64_t KD,
+                                                            int64_t dd) {
   const int64_t t = xcd_block(blockIdx.x, gridDim.x) * 256 + threadIdx.x;
   if (t >= total) return;
   const int64_t groups = O / VEC;
@@ -293,6 +339,18 @@ __global__ __launch_bounds__(256) void wino_h_output_kernel(const float* __restr
   const int64_t T = TH * TW;
   const int64_t im = r / T, rr = r - im * T;
   const int64_t ty = rr / TW, tx = rr - ty * TW;
+  uint64_t hits[VEC];
+#pragma unroll
+  for (int v = 0; v < VEC; ++v) hits[v] = 0;
+  {
+    const int64_t n = im / OD, od = im - n * OD;
+    const bool wave = g % 64 == 0;
+    for (int64_t kd = 0; kd < KD; ++kd) {
+      const uint64_t pm = load_tile_mask(tm, (n * Dp + od + kd * dd) * T + rr, g, wave, parts);
+#pragma unroll
+      for (int v = 0; v < VEC; ++v) hits[v] |= window_hits<kT>(pm, wm[(o + v) * KD + kd]);
+    }
+  }
   const float* __restrict__ src = Mt + r * O + o;
   // t1[v][i][b] = sum_a AT[i][a] m[a][b]  (4x6)
   float t1[VEC][kWinoHM][kT];
@@ -326,7 +384,8 @@ __global__ __launch_bounds__(256) void wino_h_output_kernel(const float* __restr
     for (int v = 0; v < VEC; ++v) {
       cmatvec(kWino4AT, t1[v][i], res[v]);  // Y[i][j]
 #pragma unroll
-      for (int j = 0; j < kWinoHM; ++j) res[v][j] = (res[v][j] * inv_a) * inv_b;  // exact
+      for (int j = 0; j < kWinoHM; ++j)
+        res[v][j] = (hits[v] >> (i * kT + j)) & 1u ? (res[v][j] * inv_a) * inv_b : 0.0f;  // exact
     }
     if (oh < OH) {
 #pragma unroll
@@ -370,59 +429,72 @@ int wino_h_absmax_launch(int dtype, const void* x, int64_t nx, const void* w, in
 
 int wino_h_filter_launch(int dtype, const void* w, int64_t o, int64_t kd, int64_t c, int64_t cs,
                          const uint32_t* partial, int64_t nx, int64_t nw, float* scales, uint16_t* u,
-                         void* stream) {
+                         uint32_t* wm, void* stream) {
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int64_t total = o * kd * cs;
-  const dim3 grid(blocks_for(total));
+  const int64_t nfb = int64_t(blocks_for(total));
+  const dim3 grid(unsigned(nfb + (o * kd + 3) / 4));
   const int32_t nbx = wino_h_absmax_blocks(nx), nbw = wino_h_absmax_blocks(nw);
   const uint16_t* ws = static_cast<const uint16_t*>(w);
   if (dtype == CNHWC_BF16)
     hipLaunchKernelGGL((wino_h_filter_kernel<true>), grid, dim3(256), 0, s, ws, o, kd, c, cs, partial, nbx,
-                       nbw, scales, u);
+                       nbw, scales, u, nfb, wm);
   else
     hipLaunchKernelGGL((wino_h_filter_kernel<false>), grid, dim3(256), 0, s, ws, o, kd, c, cs, partial, nbx,
-                       nbw, scales, u);
+                       nbw, scales, u, nfb, wm);
   return hipGetLastError();
 }
 
 int wino_h_input_launch(int dtype, const void* x, int64_t nb, int64_t d, int64_t dp, int32_t pd,
                         int64_t h, int64_t w, int64_t c, int64_t cs, int32_t ph, int32_t pw,
                         int64_t th, int64_t tw, const float* scales, uint16_t* v, int64_t plane,
-                        void* stream) {
+                        uint64_t* tm, void* stream) {
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  const int vec = c % 4 == 0 ? 4 : (c % 2 == 0 ? 2 : 1);
-  const int64_t total = nb * dp * th * tw * (cs / vec);
+  const int vec = int(wino_h_vec(c));
+  const int64_t g = cs / vec;
+  const int64_t total = nb * dp * th * tw * g;
   if (total == 0) return hipSuccess;
   const dim3 grid(blocks_for(total));
+  const int64_t parts = wino_mask_parts(g);
+  const bool wave = g % 64 == 0;
   const uint16_t* xs = static_cast<const uint16_t*>(x);
-#define CNHWC_WINO_H_INPUT(B, VEC)                                                              \
-  hipLaunchKernelGGL((wino_h_input_kernel<B, VEC>), grid, dim3(256), 0, s, xs, d, dp, pd, h, w, \
-                     c, cs, ph, pw, th, tw, scales, v, plane, total)
+#define CNHWC_WINO_H_INPUT(B, VEC, WAVE)                                                        \
+  hipLaunchKernelGGL((wino_h_input_kernel<B, VEC, WAVE>), grid, dim3(256), 0, s, xs, d, dp, pd, \
+                     h, w, c, cs, ph, pw, th, tw, scales, v, plane, total, tm, parts)
+#define CNHWC_WINO_H_INPUT_W(B, VEC)         \
+  do {                                       \
+    if (wave) CNHWC_WINO_H_INPUT(B, VEC, true); \
+    else CNHWC_WINO_H_INPUT(B, VEC, false);   \
+  } while (0)
   if (dtype == CNHWC_BF16) {
-    if (vec == 4) CNHWC_WINO_H_INPUT(true, 4);
-    else if (vec == 2) CNHWC_WINO_H_INPUT(true, 2);
-    else CNHWC_WINO_H_INPUT(true, 1);
+    if (vec == 4) CNHWC_WINO_H_INPUT_W(true, 4);
+    else if (vec == 2) CNHWC_WINO_H_INPUT_W(true, 2);
+    else CNHWC_WINO_H_INPUT_W(true, 1);
   } else {
-    if (vec == 4) CNHWC_WINO_H_INPUT(false, 4);
-    else if (vec == 2) CNHWC_WINO_H_INPUT(false, 2);
-    else CNHWC_WINO_H_INPUT(false, 1);
+    if (vec == 4) CNHWC_WINO_H_INPUT_W(false, 4);
+    else if (vec == 2) CNHWC_WINO_H_INPUT_W(false, 2);
+    else CNHWC_WINO_H_INPUT_W(false, 1);
   }
+#undef CNHWC_WINO_H_INPUT_W
 #undef CNHWC_WINO_H_INPUT
   return hipGetLastError();
 }
 
 int wino_h_output_launch(int dtype, const float* m, int64_t plane, int64_t nimg, int64_t oh,
                          int64_t ow, int64_t o, int64_t th, int64_t tw, const float* scales,
-                         void* y, void* stream) {
+                         void* y, const uint64_t* tm, int64_t c, int64_t cs, const uint32_t* wm,
+                         int64_t od, int64_t dp, int64_t kd, int64_t dd, void* stream) {
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const int vec = o % 2 == 0 ? 2 : 1;  // 4 per thread measured 3-15% slower (fewer waves in flight)
   const int64_t total = nimg * th * tw * (o / vec);
   if (total == 0) return hipSuccess;
   const dim3 grid(blocks_for(total));
+  const int64_t g = cs / wino_h_vec(c);  // threads per tile row of the input transform
+  const int64_t parts = wino_mask_parts(g);
   uint16_t* ys = static_cast<uint16_t*>(y);
 #define CNHWC_WINO_H_OUTPUT(B, VEC)                                                              \
   hipLaunchKernelGGL((wino_h_output_kernel<B, VEC>), grid, dim3(256), 0, s, m, plane, oh, ow, o, \
-                     th, tw, scales, ys, total)
+                     th, tw, scales, ys, total, tm, g, parts, wm, od, dp, kd, dd)
   if (dtype == CNHWC_BF16) {
     if (vec == 2) CNHWC_WINO_H_OUTPUT(true, 2);
     else CNHWC_WINO_H_OUTPUT(true, 1);

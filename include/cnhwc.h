@@ -232,6 +232,14 @@ const char* cnhwc_status_string(cnhwc_status_t s);
  *   WINOGRAD_HALF; 2.9e-4 and 0.14-0.20 at 1000x).  The implicit and unfold
  *   GEMMs meet the per-output bound at any contrast.  Selection depends on
  *   shapes only, so a caller with such data forces IMPLICIT_GEMM.
+ *   Exact zeros: an output whose window meets no nonzero input pixel (any
+ *   channel; padding counts as zero) under a nonzero filter tap (any channel)
+ *   is exactly 0 on both forms, as on the GEMM paths: the input transform
+ *   records which pixels of each tile are nonzero, the filter transform which
+ *   taps of each filter are, and the output transform stores 0 for such
+ *   outputs (3D: over every depth tap).  An output whose products vanish only
+ *   because its pixels' and its taps' nonzero channels never coincide is not
+ *   detected and keeps the tile-relative bound.
  * Forcing: WINOGRAD needs only 3x3/stride 1/dilation 1 (the channel gates are
  *   skipped); a forced tile size is capped by the budget tile (tiling page,
  *   Testing).  SMALL_KD needs N == 1, depth stride 1, depth dilation 1, depth

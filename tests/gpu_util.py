@@ -58,3 +58,30 @@ def bits(t):
     if t.dtype == torch.float32:
         return t.view(torch.int32)
     return t.view(torch.int16)
+
+
+def tile_max(den, t):
+    """Per output: the largest den among the outputs of its t x t Winograd tile
+    (same image or frame, same output channel).  den is [N,(D,)OH,OW,O]."""
+    d = den.reshape((-1,) + den.shape[-3:])
+    out = np.empty_like(d)
+    for i in range(0, d.shape[1], t):
+        for j in range(0, d.shape[2], t):
+            out[:, i:i + t, j:j + t] = d[:, i:i + t, j:j + t].max(axis=(1, 2), keepdims=True)
+    return out.reshape(den.shape)
+
+
+def check_tile_relative(y_gpu, y_ref, den, dtype, t, where=""):
+    """The Winograd paths' bound: exact zero where den == 0, and
+    |y_gpu - y| <= tol * (largest den among the outputs of the same t x t
+    tile) elsewhere.  Returns the worst error over that tile maximum."""
+    y = y_gpu.detach().to("cpu").double().numpy().reshape(y_ref.shape)
+    err = np.abs(y - y_ref)
+    zero = den == 0
+    assert np.all(np.isfinite(y)), f"{where}: non-finite output"
+    assert np.all(y[zero] == 0), f"{where}: nonzero output where every product is zero"
+    tm = tile_max(den, t)
+    bad = err > TOL[dtype] * tm
+    assert not np.any(bad), f"{where}: {int(bad.sum())} elements beyond the tile-relative bound"
+    nz = tm > 0
+    return float(np.max(err[nz] / tm[nz])) if np.any(nz) else 0.0

@@ -13,7 +13,7 @@ import torch
 
 import conv_workloads as cw
 import oracle
-from gpu_util import TOL, bits, check_parity, gather_rows, poisoned, to_oracle
+from gpu_util import TOL, bits, check_parity, gather_rows, poisoned, tile_max, to_oracle
 
 pytestmark = pytest.mark.gpu
 
@@ -98,7 +98,8 @@ DEGENERATE = [
     ("one_channel_3x3", 2, 5, 7, 1, 1, 3, 1, 1, 1),
     ("kernel_is_image", 2, 5, 5, 8, 3, 5, 1, 0, 1),     # one output pixel
     ("stride_past_image", 1, 3, 4, 8, 5, 3, 5, 0, 1),   # OH = OW = 1
-    ("padding_only_windows", 2, 2, 2, 16, 7, 3, 1, 2, 1),  # corner outputs see only padding
+    ("padding_only_windows", 2, 2, 2, 16, 7, 3, 1, 3, 1),  # corner outputs see only padding
+    ("padding_ring_1x1", 2, 3, 3, 16, 5, 1, 1, 2, 1),   # the outer two rings see only padding
     ("one_output_channel_wide_k", 1, 6, 6, 1000, 1, 3, 1, 1, 1),
     ("image_1x1_pad1", 2, 1, 1, 16, 20, 3, 1, 1, 1),    # one Winograd tile, 8 of 9 taps padding
     ("dilated_past_image", 1, 4, 4, 8, 4, 3, 1, 2, 3),  # taps land outside the image
@@ -539,16 +540,6 @@ def test_winograd_half_input_range(dt, scale):
     assert err < WH_BOUND[y.dtype], err
 
 
-def _tile_max(den, t):
-    """Per output: the largest den among the outputs of its t x t Winograd tile
-    (same image, same output channel)."""
-    out = np.empty_like(den)
-    for i in range(0, den.shape[1], t):
-        for j in range(0, den.shape[2], t):
-            out[:, i:i + t, j:j + t] = den[:, i:i + t, j:j + t].max(axis=(1, 2), keepdims=True)
-    return out
-
-
 @pytest.mark.parametrize("algo,dt,tile", [("winograd", "f32", 6), ("winograd_half", "f16", 4),
                                           ("winograd_half", "bf16", 4), ("implicit_gemm", "f32", 1),
                                           ("implicit_gemm", "bf16", 1)])
@@ -571,7 +562,7 @@ def test_winograd_error_is_tile_relative(algo, dt, tile, contrast):
     y = cn.conv2d(_dev(x), _dev(wt), **case.conv_kwargs(), algo=algo, out=poisoned(yr.shape, x.dtype))
     err = np.abs(y.cpu().double().numpy() - yr)
     tol = TOL[x.dtype]
-    assert np.all(err <= tol * _tile_max(den, tile)), float((err / _tile_max(den, tile)).max())
+    assert np.all(err <= tol * tile_max(den, tile)), float((err / tile_max(den, tile)).max())
     if contrast >= 0.1 or algo == "implicit_gemm":
         check_parity(y.cpu(), yr, den, x.dtype, case.name)
 

@@ -119,8 +119,10 @@ def test_wide_fp32_full_budget_is_untiled_winograd():
     p = _p((40, 512, 512, 192), C2W, ws_limit=288 * 10**9)
     assert p.algo_name == "winograd" and p.tile_batch == 40 and p.n_tiles == 1
     assert p.tiles_per_image == 86 * 86
-    assert p.scratch_per_element == 64 * 7396 * (192 + 96) * 4
-    assert p.own_bytes == 40 * 512 * 512 * (192 + 96) * 4 + 64 * 96 * 192 * 4
+    # V + M + the tile masks (192 channel threads per tile: three 8-byte parts)
+    assert p.scratch_per_element == 64 * 7396 * (192 + 96) * 4 + 7396 * 3 * 8
+    # x + y + U + the tap masks (one 32-bit word per output channel)
+    assert p.own_bytes == 40 * 512 * 512 * (192 + 96) * 4 + 64 * 96 * 192 * 4 + 96 * 4
     assert p.workspace_bytes >= 64 * 96 * 192 * 4 + 40 * p.scratch_per_element
     assert p.budget_bytes == 288 * 10**9 // 4 * 3 - p.own_bytes
 
@@ -136,8 +138,8 @@ def test_wide_fp32_small_budgets_fall_back(n, wl):
 def test_wide_fp32_m4pro_class_budget_tiles(n):
     wl = 40_200_000_000
     p = _p((n, 512, 512, 192), C2W, ws_limit=wl)
-    own = n * 512 * 512 * (192 + 96) * 4 + 64 * 96 * 192 * 4
-    scratch = 64 * 7396 * (192 + 96) * 4
+    own = n * 512 * 512 * (192 + 96) * 4 + 64 * 96 * 192 * 4 + 96 * 4
+    scratch = 64 * 7396 * (192 + 96) * 4 + 7396 * 3 * 8
     tb = min(n, (wl * 3 // 4 - own) // scratch)
     assert p.algo_name == "winograd" and p.tile_batch == tb and p.n_tiles == -(-n // tb)
 
@@ -409,9 +411,17 @@ BF16 = torch.bfloat16
 HEAD = 8448  # partial maxima of x and w (2 x 1024 words) + 4 scales, 256-aligned
 
 
+def _mask_parts(g):
+    """8-byte parts of one tile's nonzero-pixel mask for g input-transform
+    threads per tile: one per wavefront of 64, else at most one per workgroup
+    of 256 that the tile's threads touch."""
+    return g // 64 if g % 64 == 0 else (g - 1) // 256 + 2
+
+
 def _wh_scratch(t, c, o, frames=1, od=1):
     cs = -(-c // 32) * 32
-    return 36 * t * (frames * cs * 2 + od * o * 4)
+    vec = 4 if c % 4 == 0 else (2 if c % 2 == 0 else 1)
+    return 36 * t * (frames * cs * 2 + od * o * 4) + frames * t * _mask_parts(cs // vec) * 8
 
 
 def test_winograd_half_2d_plan():
@@ -422,7 +432,7 @@ def test_winograd_half_2d_plan():
     assert p.tile_batch == 8 and p.n_tiles == 1 and p.split_k == 1
     assert p.scratch_per_element == _wh_scratch(t, 200, 256)
     u = 36 * 256 * 224 * 2
-    assert p.own_bytes == 8 * 56 * 56 * (200 + 256) * 2 + HEAD + u
+    assert p.own_bytes == 8 * 56 * 56 * (200 + 256) * 2 + HEAD + u + 256 * 4  # + the tap masks
     assert p.workspace_bytes >= HEAD + u + 8 * p.scratch_per_element
     assert p.kernel_config in (14, 15)
     desc = cn.make_desc(xs, ws, 1, 1, 1, F16)
