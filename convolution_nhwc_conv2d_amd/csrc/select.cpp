@@ -39,6 +39,13 @@ uint64_t three_quarters(uint64_t w) { return (w / 4) * 3 + ((w % 4) * 3) / 4; }
 // Bound on element counts so every byte size below fits comfortably in 63 bits.
 constexpr int64_t kMaxDim = int64_t(1) << 31;
 constexpr uint64_t kMaxElems = uint64_t(1) << 56;
+// The implicit-GEMM gathers hold a window's origin (o * stride - pad), a tap's
+// offset ((k - 1) * dil at most) and their sum in 32-bit integers, and mark
+// rows past the end with an origin of -2^30.  With in + 2 * pad <= 2^30 on
+// every axis all of them lie in (-2^31, 2^31) and a marked row stays out of
+// range; C <= 2^30 keeps the channel position of a K chunk (at most C - 1 plus
+// one chunk) in range too.  Larger convs are UNSUPPORTED.
+constexpr int64_t kMaxSpan = int64_t(1) << 30;
 
 cnhwc_status_t check_desc(const cnhwc_conv_desc_t& d, int64_t out[3]) {
   if (d.nd != 2 && d.nd != 3) return CNHWC_ERR_INVALID_ARGUMENT;
@@ -54,6 +61,10 @@ cnhwc_status_t check_desc(const cnhwc_conv_desc_t& d, int64_t out[3]) {
   if (d.groups != 1) return d.groups < 1 ? CNHWC_ERR_INVALID_ARGUMENT : CNHWC_ERR_UNSUPPORTED;
   if (d.nd == 2 && (d.d != 1 || d.kd != 1 || d.stride[0] != 1 || d.pad[0] != 0 || d.dil[0] != 1))
     return CNHWC_ERR_INVALID_ARGUMENT;
+  const int64_t ins[3] = {d.d, d.h, d.w};
+  for (int i = 0; i < 3; ++i)
+    if (ins[i] + 2 * int64_t(d.pad[i]) > kMaxSpan) return CNHWC_ERR_UNSUPPORTED;
+  if (d.c > kMaxSpan) return CNHWC_ERR_UNSUPPORTED;
   out[0] = out_extent(d.d, d.kd, d.stride[0], d.pad[0], d.dil[0]);
   out[1] = out_extent(d.h, d.kh, d.stride[1], d.pad[1], d.dil[1]);
   out[2] = out_extent(d.w, d.kw, d.stride[2], d.pad[2], d.dil[2]);

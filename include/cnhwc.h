@@ -109,7 +109,10 @@ typedef struct {
   int32_t nd;        /* 2 or 3 */
   int32_t dtype;     /* cnhwc_dtype_t: element type of x, w and y */
   int64_t n, d, h, w, c, o, kd, kh, kw;  /* each in [1, 2^31]; an empty batch (n = 0)
-                                            is INVALID_ARGUMENT: there is no work to plan */
+                                            is INVALID_ARGUMENT: there is no work to plan.
+                                            d + 2*pad[0], h + 2*pad[1], w + 2*pad[2]
+                                            and c above 2^30 are UNSUPPORTED (the
+                                            gathers index in 32-bit integers). */
   int32_t stride[3];
   int32_t pad[3];
   int32_t dil[3];
@@ -161,10 +164,14 @@ typedef struct {
   cnhwc_select_opts_t opts;  /* the options this plan was made from */
 } cnhwc_plan_t;
 
-/* Returns CNHWC_ABI_VERSION. */
+/* Returns CNHWC_ABI_VERSION.  No page passage defines it: it versions this
+ * header's structs and entry points for the caller's binding. */
 int cnhwc_abi_version(void);
 
-/* Human-readable name of a status (static storage; never NULL). */
+/* Human-readable name of a status (static storage; never NULL).  Every call
+ * returns a status because of the failure the tiling page's Problem section
+ * describes: a command-buffer error that was dropped left a silent all-zero
+ * output.  This names the status; it implements no conv operation. */
 const char* cnhwc_status_string(cnhwc_status_t s);
 
 /* Algorithm selection and memory planning (host only, no device call).

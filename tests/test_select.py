@@ -235,6 +235,43 @@ def test_invalid_descriptors(xs, ws, s, p, d, err):
     assert e.value.name == err
 
 
+SPAN = 2**30  # largest in + 2 * pad per axis, and largest C, the 32-bit gathers index
+
+
+@pytest.mark.parametrize("axis", ["h", "w"])
+def test_spatial_span_bound_both_sides(axis):
+    """in + 2 * pad up to 2^30 plans; one more is UNSUPPORTED (the gathers hold
+    window origins and tap offsets in 32-bit integers)."""
+    def shapes(n_in, k):
+        return ((1, 1, n_in, 1), (1, 1, k, 1)) if axis == "w" else ((1, n_in, 1, 1), (1, k, 1, 1))
+    pad = (0, 1) if axis == "w" else (1, 0)
+    xs, ws = shapes(SPAN - 2, 3)
+    p = _p(xs, ws, 1, pad, 1, algo="implicit_gemm")
+    assert (p.out_w if axis == "w" else p.out_h) == SPAN - 2
+    xs, ws = shapes(SPAN - 1, 3)
+    with pytest.raises(cn.CnhwcError) as e:
+        _p(xs, ws, 1, pad, 1)
+    assert e.value.name == "UNSUPPORTED"
+    # a long dilated filter whose span reaches past 2^31 in 32 bits
+    xs, ws = shapes(2**31, 2049)
+    dil = (1, 2**20) if axis == "w" else (2**20, 1)
+    with pytest.raises(cn.CnhwcError) as e:
+        _p(xs, ws, 1, pad, dil)
+    assert e.value.name == "UNSUPPORTED"
+
+
+def test_depth_and_channel_span_bounds():
+    ok = cn.plan3d((1, SPAN - 4, 1, 1, 1), (1, 3, 1, 1, 1), 1, (2, 0, 0), 1, torch.float16, algo="implicit_gemm")
+    assert ok.out_d == SPAN - 2
+    with pytest.raises(cn.CnhwcError) as e:
+        cn.plan3d((1, SPAN - 3, 1, 1, 1), (1, 3, 1, 1, 1), 1, (2, 0, 0), 1, torch.float16)
+    assert e.value.name == "UNSUPPORTED"
+    assert _p((1, 1, 1, SPAN), (1, 1, 1, SPAN), 1, 0, 1, algo="implicit_gemm").algo_name == "implicit_gemm"
+    with pytest.raises(cn.CnhwcError) as e:
+        _p((1, 1, 1, SPAN + 1), (1, 1, 1, SPAN + 1), 1, 0, 1)
+    assert e.value.name == "UNSUPPORTED"
+
+
 def test_invalid_opts_and_groups():
     d = cn.make_desc((1, 8, 8, 8), (8, 3, 3, 8), 1, 1, 1)
     with pytest.raises(cn.CnhwcError) as e:
