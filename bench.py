@@ -51,6 +51,8 @@ def parse():
     ap.add_argument("--ws-limit", type=int, default=None)
     ap.add_argument("--tile-batch", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other workloads (small fp32, budgets, half sweep, ResNet-50 stack, video 3D)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--calib-copy", type=int, default=0,
                     help="also run one plain device copy of this many bytes (fp32 -> fp32) before the "
@@ -453,6 +455,191 @@ def run_suite(names):
                 del a, b, c
 
 
+def _gemm_work(kind, plan, case):
+    """Algorithmic flops of all launches of a GEMM kernel kind in one call (None
+    if the kind is not a GEMM stage)."""
+    k3 = case.kd * case.kh * case.kw * case.c
+    m = case.n * plan.out_d * plan.out_h * plan.out_w
+    if kind in ("implicit_gemm", "unfold_gemm"):
+        return 2.0 * m * case.o * k3
+    if kind == "wino_gemm":
+        if plan.algo_name == "winograd_half":
+            cs = -(-case.c // 32) * 32
+            return 2.0 * 36 * case.n * plan.out_d * plan.tiles_per_image * case.o * case.kd * cs
+        return 2.0 * 64 * case.n * plan.tiles_per_image * case.c * case.o
+    return None
+
+
+def _gemm_peak(plan, dtype):
+    """MFMA peak of the GEMM stages' operand type: the half Winograd path runs
+    fp16 operands for bf16 inputs too; the fp32 Winograd path fp32 operands."""
+    if plan.algo_name == "winograd" or plan.inner_algo_name == "winograd" or dtype == "f32":
+        return PEAK["mfma_tflops"]["f32"]
+    return PEAK["mfma_tflops"]["f16"]
+
+
+def _oracle_sample(case, x, w, y, count, seed, threads):
+    """The GPU output against the fp64 oracle on `count` seeded output rows
+    (all O channels each)."""
+    import numpy as np
+    import torch
+    import conv_workloads as cw
+    import oracle
+    o = y.shape[-1]
+    total = y.numel() // o
+    rows = cw.sample_rows(total, count, seed)
+    yr, den = oracle.conv(x.float().numpy(), w.float().numpy(), **case.conv_kwargs(), rows=rows, threads=threads)
+    idx = torch.as_tensor(rows, device=y.device, dtype=torch.long)
+    yg = y.reshape(-1, o).index_select(0, idx).double().cpu().numpy()
+    tol = 2e-5 if case.dtype == "f32" else 1e-2
+    err = np.abs(yg - yr)
+    zero = den == 0
+    rel = err[~zero] / den[~zero]
+    ok = bool(np.all(yg[zero] == 0) and np.all(err[~zero] <= tol * den[~zero]))
+    return {"outputs": int(yr.size), "max_err_over_sum_abs": float(rel.max()) if rel.size else 0.0,
+            "tol": tol, "within_tol": ok}
+
+
+def run_configs(dev, head):
+    """The other four workloads (and the headline's budget variants), each with
+    median and min ms over 15 back-to-back calls, the direct-equivalent rate,
+    the dominant kernel against its roofline and an oracle check on a seeded
+    sample of output rows."""
+    import torch
+    import conv_workloads as cw
+    import convolution_nhwc_conv2d_amd as cn
+    threads = len(os.sched_getaffinity(0))
+    out = {}
+
+    def timed(case, x, w, algo="auto", plan=None, y=None, **kw):
+        fn = cn.conv2d if case.nd == 2 else cn.conv3d
+        if plan is None:
+            plan = (cn.plan2d if case.nd == 2 else cn.plan3d)(tuple(x.shape), tuple(w.shape), **case.conv_kwargs(),
+                                                              dtype=x.dtype, algo=algo, **kw)
+        oshape = (x.shape[0],) + ((plan.out_d,) if case.nd == 3 else ()) + (plan.out_h, plan.out_w, case.o)
+        y = torch.empty(oshape, dtype=x.dtype, device=dev) if y is None else y
+        ws = torch.empty(max(1, plan.workspace_bytes), dtype=torch.uint8, device=dev)
+        call = lambda timer=None: fn(x, w, **case.conv_kwargs(), plan=plan, out=y, workspace=ws, timer=timer)
+        ms = _time_call(call)
+        ms_min = _time_call.last_min
+        split = _kernel_split(call)
+        flops = cn.direct_flops(tuple(x.shape), tuple(w.shape), plan)
+        gemms = [k for k in split if _gemm_work(k, plan, case) is not None]
+        dom = max(gemms, key=split.get) if gemms else None
+        work = _gemm_work(dom, plan, case) if dom else None
+        ent = {"algo": plan.algo_name, "ms_median": ms, "ms_min": ms_min, "tflops": flops / ms / 1e9,
+               "kernels_ms": split}
+        if work is not None:
+            peak = _gemm_peak(plan, case.dtype)
+            ach = work / (split[dom] / 1e3) / 1e12
+            ent["dominant"] = {"kernel": dom, "bound": "mfma", "achieved": ach, "peak": peak, "unit": "TFLOP/s",
+                               "frac": ach / peak}
+        del ws
+        return ent, y, plan
+
+    # small fp32 (latency-bound: microseconds)
+    case = cw.small_fp32()
+    x, w = case.input(), case.weight()
+    xg, wg = x.to(dev), w.to(dev)
+    ents = []
+    for algo in ("winograd", "implicit_gemm", "auto"):
+        e, y, _ = timed(case, xg, wg, algo)
+        e = {"algo": e["algo"], "forced": algo != "auto", "us_median": e["ms_median"] * 1e3,
+             "us_min": e["ms_min"] * 1e3, "kernels_ms": e["kernels_ms"],
+             "oracle_check": _oracle_sample(case, x, w, y, 256, 21, threads)}
+        ents.append(e)
+    out["small_fp32"] = {"workload": "conv2d fp32 NHWC N=1, 16x16, 32->32, 3x3, stride 1, pad 1",
+                         "bound": "latency", "entries": ents}
+    log("[bench] configs: small fp32 done")
+
+    # the headline conv under the injected budgets: 40.2e9 (batch tiles) and 512 MB (fallback)
+    hcase, hx, hw, hy = head
+    ents = []
+    for wl in (40_200_000_000, 512 * 10**6):
+        e, y, plan = timed(hcase, hx, hw, ws_limit=wl, y=hy)
+        e.update(ws_limit_bytes=wl, tile_batch=plan.tile_batch, n_tiles=plan.n_tiles,
+                 oracle_check=_oracle_sample(hcase, hcase.input([0]), hcase.weight(), y[:1], 256, 22, threads))
+        ents.append(e)
+    out["wide_fp32_budgets"] = {"workload": f"conv2d fp32 NHWC N={hcase.n}, 512x512, 192->96, 3x3, s1, p1",
+                                "entries": ents}
+    log("[bench] configs: wide fp32 budgets done")
+
+    # half-precision sweep: the widest C_out at the largest M, both dtypes, and an unaligned C_in
+    ents = []
+    for dt, c_out, n, c_in in (("f16", 4096, 64, 256), ("bf16", 4096, 64, 256), ("f16", 1024, 16, 1000)):
+        case = cw.cout_axis(dt, c_out, n, c_in)
+        x, w = case.input(), case.weight()
+        xg, wg = x.to(dev), w.to(dev)
+        for algo in ("auto", "unfold_gemm"):
+            e, y, _ = timed(case, xg, wg, algo)
+            e.update(workload=f"{dt} 32x32 {c_in}->{c_out} 3x3 s1 p1, M={n * 1024}, K={9 * c_in}",
+                     oracle_check=_oracle_sample(case, x, w, y, 256, 23, threads))
+            ents.append(e)
+        del xg, wg
+    out["half_sweep"] = {"workload": "conv2d fp16/bf16 C_out axis and unaligned C_in", "entries": ents}
+    log("[bench] configs: half sweep done")
+
+    # the ResNet-50 conv stack: each conv eager, and the whole stack replayed as one HIP graph
+    ents = []
+    for batch in (1, 8):
+        calls, flops, eager_ms, gemm_flops, gemm_ms, worst = [], 0.0, 0.0, 0.0, 0.0, 0.0
+        ok = True
+        for case, mult, stage in cw.resnet50_layers(batch):
+            x, w = case.input(), case.weight()
+            xg, wg = x.to(dev), w.to(dev)
+            e, y, plan = timed(case, xg, wg)
+            chk = _oracle_sample(case, x, w, y, 64, 24, threads)
+            ok = ok and chk["within_tol"]
+            worst = max(worst, chk["max_err_over_sum_abs"])
+            eager_ms += e["ms_median"] * mult
+            for kind, kms in e["kernels_ms"].items():
+                g = _gemm_work(kind, plan, case)
+                if g is not None:
+                    gemm_flops += g * mult
+                    gemm_ms += kms * mult
+            ws = torch.empty(max(1, plan.workspace_bytes), dtype=torch.uint8, device=dev)
+            for _ in range(mult):
+                calls.append((xg, wg, case, plan, ws, y))
+                flops += cn.direct_flops(tuple(xg.shape), tuple(wg.shape), plan)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(side):
+            for x_, w_, case, plan, ws, y in calls:
+                cn.conv2d(x_, w_, **case.conv_kwargs(), plan=plan, workspace=ws, out=y)
+            torch.cuda.synchronize()
+            with torch.cuda.graph(graph, stream=side):
+                for x_, w_, case, plan, ws, y in calls:
+                    cn.conv2d(x_, w_, **case.conv_kwargs(), plan=plan, workspace=ws, out=y)
+        gms = _time_call(graph.replay)
+        ents.append({"batch": batch, "convs": len(calls), "eager_ms_sum_of_medians": eager_ms,
+                     "graph_ms_median": gms, "graph_ms_min": _time_call.last_min, "tflops_graph": flops / gms / 1e9,
+                     "bound": "latency",
+                     "gemm_kernels": {"achieved": gemm_flops / (gemm_ms / 1e3) / 1e12,
+                                      "peak": PEAK["mfma_tflops"]["f16"], "unit": "TFLOP/s",
+                                      "frac": gemm_flops / (gemm_ms / 1e3) / 1e12 / PEAK["mfma_tflops"]["f16"]},
+                     "oracle_check": {"outputs": "64 seeded rows x O of each of the 23 convs",
+                                      "max_err_over_sum_abs": worst, "tol": 1e-2, "within_tol": ok}})
+        del calls, graph
+    out["resnet50_fp16"] = {"workload": "ResNet-50 v1.5 conv stack fp16, 224x224x3, 53 convs", "entries": ents}
+    log("[bench] configs: resnet50 stack done")
+
+    # video conv3d bf16 on AUTO (half-precision Winograd with the depth taps in its GEMMs)
+    ents = []
+    for shape in cw.VIDEO3D_SHAPES:
+        case = cw.video3d(*shape)
+        x, w = case.input(), case.weight()
+        xg, wg = x.to(dev), w.to(dev)
+        e, y, _ = timed(case, xg, wg)
+        e.update(workload=f"bf16 {shape[0]}x{shape[1]}x{shape[2]} {shape[3]}->{shape[4]} 3x3x3 pad (0,1,1)",
+                 oracle_check=_oracle_sample(case, x, w, y, 256, 25, threads))
+        ents.append(e)
+        del xg, wg, y, x
+    out["video3d_bf16"] = {"workload": "conv3d bf16 NDHWC N=1, 3x3x3, stride 1, pad (0,1,1)", "entries": ents}
+    log("[bench] configs: video 3D done")
+    return out
+
+
 def main():
     args = parse()
     if args.traffic_from:
@@ -521,7 +708,9 @@ def main():
     log(f"[bench] {ms:.3f} ms/step, {value:.2f} TFLOP/s direct-equivalent")
 
     per_kind = {}
-    for kind, kms in timer.durations():
+    durations = timer.durations()
+    spans = sorted(timer.call_ms)
+    for kind, kms in durations:
         e = per_kind.setdefault(kind, [0, 0.0])
         e[0] += 1
         e[1] += kms
@@ -563,6 +752,11 @@ def main():
                  "mean_err_over_sum_abs": float(rel.mean()), "tol": 2e-5, "within_tol": bool(rel.max() <= 2e-5)}
         log(f"[bench] oracle check: max |y - y_ref| / sum|x||w| = {check['max_err_over_sum_abs']:.3g}")
 
+    configs = None
+    if not args.no_configs:
+        log("[bench] timing the other workloads")
+        configs = run_configs(dev, (case, x, w, out))
+
     line = {
         "metric": "conv fwd TFLOP/s (2*N*OH*OW*O*C*KH*KW/s) and % of roofline",
         "value": value,
@@ -571,9 +765,16 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms,
+        # GPU span of each timed step (first kernel to the end of the last), from the library's events
+        "ms_per_step_median": spans[len(spans) // 2],
+        "ms_per_step_min": spans[0],
         "higher_is_better": True,
         "scaling": "weak",
-        "vs_baseline": value / PAGE_BASELINE_TFLOPS,
+        # against the reported baseline: the fp64 oracle timed on this host's cores in the same run
+        "vs_baseline": value / cpu["value"] if cpu else None,
+        "vs_baseline_basis": "cpu_baseline (the fp64 oracle on this host, same run)",
+        # the tiling page's ~310 ms Winograd time for this conv on an M2 Max: another machine's, context only
+        "context": {"page_m2_max_tflops": PAGE_BASELINE_TFLOPS, "ratio": value / PAGE_BASELINE_TFLOPS},
         "dtype": "f32",
         "data": "synthetic (seeded numpy PCG64: x ~ U[-1,1], w ~ N(0, 1/(9C)))",
         "config": {"workload": f"conv2d fp32 NHWC N={case.n}, 512x512, C=192 -> O=96, 3x3, stride 1, pad 1",
@@ -584,6 +785,7 @@ def main():
         "stages": stages,
         "cpu_baseline": cpu,
         "oracle_check": check,
+        "configs": configs,
     }
     print(json.dumps(line), flush=True)
 

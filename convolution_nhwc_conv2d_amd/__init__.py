@@ -343,11 +343,14 @@ class KernelTimer:
     on the launch stream right before each kernel (cnhwc_conv*_fwd_timed).
 
     Pass as ``timer=`` to conv2d/conv3d; after a synchronize, ``durations()``
-    returns [(kind_name, ms), ...] for every kernel of every timed call."""
+    returns [(kind_name, ms), ...] for every kernel of every timed call, and
+    ``call_ms`` then holds each call's span (first kernel's start event to the
+    event after its last kernel), in call order."""
 
     def __init__(self):
         self._pending = []   # (events array, kinds array, n)
         self._pool = []
+        self.call_ms = []
 
     def slots(self, n):
         hip = _Hip.get()
@@ -371,6 +374,7 @@ class KernelTimer:
     def durations(self):
         hip = _Hip.get()
         out = []
+        self.call_ms = []
         for ev, kinds, n in self._pending:
             hip.hipEventSynchronize(ev[n - 1])
             for i in range(n - 1):
@@ -378,6 +382,10 @@ class KernelTimer:
                 if hip.hipEventElapsedTime(ctypes.byref(ms), ev[i], ev[i + 1]) != 0:
                     raise RuntimeError("hipEventElapsedTime failed")
                 out.append((KERNEL_KINDS[kinds[i]], float(ms.value)))
+            span = ctypes.c_float()
+            if hip.hipEventElapsedTime(ctypes.byref(span), ev[0], ev[n - 1]) != 0:
+                raise RuntimeError("hipEventElapsedTime failed")
+            self.call_ms.append(float(span.value))
             self._pool.extend(ev[i] for i in range(n))
         self._pending = []
         return out

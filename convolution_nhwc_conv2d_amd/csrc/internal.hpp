@@ -137,8 +137,8 @@ int wino_h_absmax_launch(int dtype, const void* x, int64_t nx, const void* w, in
                          uint32_t* partial, void* stream);
 // U[p][o][kd*cs + c] = fp16(G (sw g) G^T)_p, g = w[o][kd][kh][kw][c] (KD = kd planes);
 // the scales come from the partial maxima, and scales = {sx, sw, a, b} with
-// a b = 1/(sx sw) is stored for the transforms that follow.  wm[o*kd + k]:
-// bit kh*3 + kw set iff some channel of tap (kh, kw) of slice (o, k) is nonzero.
+// a b = 1/(sx sw) is stored for the transforms that follow.  wm[k*o + oc]:
+// bit kh*3 + kw set iff some channel of tap (kh, kw) of slice (oc, k) is nonzero.
 int wino_h_filter_launch(int dtype, const void* w, int64_t o, int64_t kd, int64_t c, int64_t cs,
                          const uint32_t* partial, int64_t nx, int64_t nw, float* scales, uint16_t* u,
                          uint32_t* wm, void* stream);
@@ -189,7 +189,7 @@ WinoLayout wino_layout(const cnhwc_conv_desc_t& d2, int64_t oh, int64_t ow, int6
 // Half-precision Winograd workspace layout (2D: od = 1, depth pad 0; 3D: one
 // batch element per tile).  Frames per element dp = D + 2 pd; the GEMM K is
 // ku = KD * cs.
-// Tap masks (uint32 per (o, kd)) follow U; the tile masks
+// Tap masks (uint32 per (kd, o)) follow U; the tile masks
 // (wino_mask_parts(cs / wino_h_vec(c)) uint64 per input tile row) follow M.
 struct WinoHLayout {
   int64_t tiles_h, tiles_w, t, cs, dp, ku, mask_parts;

@@ -14,10 +14,13 @@
 // is not caught; it keeps the tile-relative rounding error.)
 //
 // Tile masks are written in parts, with neither atomics nor a clearing pass:
-// the G threads of a tile row (launch threads r * G .. r * G + G - 1) either
-// fill whole wavefronts (G % 64 == 0: each wavefront writes part (t % G) / 64)
-// or share workgroups of 256 (each workgroup holding some of the row's
-// threads writes part b - (r * G) / 256, b the workgroup).  The output
+// every thread builds the mask of its own channels (one bit per pixel, no
+// cross-lane step inside the load loop, so the loads stay free to overlap),
+// and the G threads of a tile row (launch threads r * G .. r * G + G - 1)
+// either fill whole wavefronts (G % 64 == 0: each wavefront ORs its lanes
+// and writes part (t % G) / 64) or share workgroups of 256 (each workgroup
+// holding some of the row's threads ORs them in LDS and writes part
+// b - (r * G) / 256, b the workgroup).  The output
 // transform ORs exactly the parts that were written.
 #pragma once
 #include <hip/hip_runtime.h>
@@ -39,6 +42,18 @@ __device__ __forceinline__ uint64_t load_tile_mask(const uint64_t* __restrict__ 
   uint64_t m = 0;
   for (int64_t q = 0; q < n; ++q) m |= src[q];
   return m;
+}
+
+// OR of a per-thread mask over the 64 lanes of the wavefront (every lane
+// gets the result).
+__device__ __forceinline__ uint64_t wave_or(uint64_t m) {
+  uint32_t lo = uint32_t(m), hi = uint32_t(m >> 32);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    lo |= uint32_t(__shfl_xor(int(lo), off));
+    hi |= uint32_t(__shfl_xor(int(hi), off));
+  }
+  return (uint64_t(hi) << 32) | lo;
 }
 
 // Workgroup mode: OR the per-thread masks of each tile row among the 256

@@ -33,6 +33,11 @@
 namespace cnhwc {
 namespace {
 
+// Loads outside the image read this zero word instead, so every load of the
+// input transform is issued unconditionally (no branch per pixel: the
+// compiler can put all of a thread's loads in flight at once).
+__device__ __align__(16) uint32_t g_wino_zero[4] = {0u, 0u, 0u, 0u};
+
 // Workgroups [0, nfb) transform the filter, one thread per (o, c); the
 // workgroups after them compute the tap masks, one wavefront per o.
 template <typename E, bool BF16>
@@ -79,8 +84,9 @@ __global__ __launch_bounds__(256) void wino_filter_kernel(const E* __restrict__ 
 
 // One thread per (tile r, channel c), channels fastest.  Besides V it writes
 // the tile's nonzero-pixel mask (bit i * 8 + j for pixel (i, j)): with WAVE
-// (Cs % 64 == 0) every wavefront holds 64 channels of one tile and stores its
-// part from ballots; otherwise the workgroup ORs its threads' masks.
+// (Cs % 64 == 0) every wavefront holds 64 channels of one tile and builds its
+// part from one ballot per pixel; otherwise the workgroup ORs its threads'
+// masks.
 template <typename E, bool BF16, bool WAVE>
 __global__ __launch_bounds__(256) void wino_input_kernel(const E* __restrict__ x, int64_t H,
                                                          int64_t W, int64_t C, int64_t Cs,
@@ -91,7 +97,7 @@ __global__ __launch_bounds__(256) void wino_input_kernel(const E* __restrict__ x
   const int64_t b = xcd_block(blockIdx.x, gridDim.x);
   const int64_t t = b * 256 + threadIdx.x;
   const bool live = t < total;
-  uint64_t pix = 0;  // WAVE: uniform over the wavefront; else this thread's channel
+  uint64_t pix = 0;  // nonzero pixels (WAVE: of the wavefront's channels, uniform; else this thread's)
   if (live) {
     const int64_t r = t / Cs, c = t - r * Cs;
     const int64_t T = TH * TW;
@@ -100,25 +106,31 @@ __global__ __launch_bounds__(256) void wino_input_kernel(const E* __restrict__ x
     const int64_t ih0 = ty * 6 - ph, iw0 = tx * 6 - pw;
     const E* __restrict__ img = x + n * H * W * C + c;
     const bool cin = c < C;
-    // column transform first: t1[a][j] = sum_i BT[a][i] d[i][j]
-    float t1[8][8];
+    // every load first (unconditional: outside the image they read a zero
+    // word), so that all of them are in flight before the first is used
+    E raw[8][8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int64_t iw = iw0 + j;
       const bool wok = cin && iw >= 0 && iw < W;
-      float col[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int64_t ih = ih0 + i;
-        col[i] = (wok && ih >= 0 && ih < H) ? to_f32<E, BF16>(img[(ih * W + iw) * C]) : 0.0f;
+        raw[i][j] = *((wok && ih >= 0 && ih < H) ? img + (ih * W + iw) * C
+                                                 : reinterpret_cast<const E*>(g_wino_zero));
       }
+    }
+    // column transform first: t1[a][j] = sum_i BT[a][i] d[i][j]
+    float t1[8][8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      float col[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        if constexpr (WAVE) {
-          if (__ballot(col[i] != 0.0f) != 0ull) pix |= 1ull << (i * 8 + j);
-        } else {
-          pix |= uint64_t(col[i] != 0.0f) << (i * 8 + j);
-        }
+        col[i] = to_f32<E, BF16>(raw[i][j]);
+        // WAVE: one ballot per pixel (the mask stays in scalar registers)
+        if constexpr (WAVE) pix |= uint64_t(__ballot(col[i] != 0.0f) != 0ull) << (i * 8 + j);
+        else pix |= uint64_t(col[i] != 0.0f) << (i * 8 + j);
       }
       float res[8];
       cmatvec(kWinoBT, col, res);
@@ -160,7 +172,6 @@ __global__ __launch_bounds__(256) void wino_output_kernel(const float* __restric
   const int64_t T = TH * TW;
   const int64_t n = r / T, rr = r - n * T;
   const int64_t ty = rr / TW, tx = rr - ty * TW;
-  const uint64_t hits = window_hits<8>(load_tile_mask(tm, r, g, g % 64 == 0, parts), wm[o]);
   const float* __restrict__ src = Mt + r * O + o;
   // t1[i][b] = sum_a AT[i][a] m[a][b]  (6x8)
   float t1[6][8];
@@ -174,6 +185,8 @@ __global__ __launch_bounds__(256) void wino_output_kernel(const float* __restric
 #pragma unroll
     for (int i = 0; i < 6; ++i) t1[i][b] = res[i];
   }
+  // the masks after the M loads are issued (their loop would hold the loads back)
+  const uint64_t hits = window_hits<8>(load_tile_mask(tm, r, g, g % 64 == 0, parts), wm[o]);
 #pragma unroll
   for (int i = 0; i < 6; ++i) {
     const int64_t oh = ty * 6 + i;

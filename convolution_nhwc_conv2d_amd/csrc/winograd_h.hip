@@ -28,13 +28,15 @@
 //   U [36][O][KD*Cs]    fp16, Cs = C rounded up to 32 (zero channels)
 //   V [36][rows][Cs]    fp16, rows = (image or frame) * tiles, frames padded by pd
 //   M [36][rows'][O]    fp32, rows' = output images or frames * tiles
-//   tap masks [O][KD]   nonzero 3x3 taps of each (o, kd) filter slice (uint32)
+//   tap masks [KD][O]   nonzero 3x3 taps of each (o, kd) filter slice (uint32)
 //   tile masks [rows][P] nonzero pixels of each 6x6 input tile, in parts
 // The masks make an output whose products are all zero exactly zero (see
 // wino_mask.hpp); in 3D an output's window spans the KD frames its taps read.
 // Tile (ty, tx) covers input rows 4 ty - ph .. +5 and columns 4 tx - pw .. +5
 // and produces output rows 4 ty .. 4 ty + 3 (cropped).
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 
 #include "internal.hpp"
 #include "device_common.hpp"
@@ -45,6 +47,11 @@ namespace cnhwc {
 namespace {
 
 constexpr int kT = kWinoHM + 2;  // 6x6 input tiles
+
+// Loads outside the image read this zero block instead, so every load of the
+// input transform is issued unconditionally (no branch per pixel: the
+// compiler can put all of a thread's loads in flight at once).
+__device__ __align__(16) uint32_t g_wino_h_zero[4] = {0u, 0u, 0u, 0u};
 
 // |h| as integer bits, NaN mapped to 0 (a NaN must not pick the scale; it
 // propagates through the conv itself).  Order of |h| == order of these bits.
@@ -162,10 +169,11 @@ __global__ __launch_bounds__(256) void wino_h_filter_kernel(const uint16_t* __re
                                                             uint16_t* __restrict__ U, int64_t nfb,
                                                             uint32_t* __restrict__ wm) {
   if (int64_t(blockIdx.x) >= nfb) {  // whole workgroups: uniform branch, no barrier below
-    const int64_t sl = (int64_t(blockIdx.x) - nfb) * 4 + (threadIdx.x >> 6);
+    const int64_t sl = (int64_t(blockIdx.x) - nfb) * 4 + (threadIdx.x >> 6);  // o * KD + kd
     if (sl >= O * KD) return;
     const uint32_t bits = tap_mask_of(w + sl * 9 * C, C, [](uint16_t v) { return (v & 0x7fffu) != 0u; });
-    if ((threadIdx.x & 63) == 0) wm[sl] = bits;
+    const int64_t o = sl / KD, kd = sl - o * KD;
+    if ((threadIdx.x & 63) == 0) wm[kd * O + o] = bits;
     return;
   }
   __shared__ uint32_t sm[4];
@@ -212,10 +220,10 @@ __global__ __launch_bounds__(256) void wino_h_filter_kernel(const uint16_t* __re
 // VEC channels per thread (4 when C % 4 == 0, 2 when C is even: 8- or 4-byte
 // loads and stores).  Besides V it writes the tile's nonzero-pixel mask (bit
 // i * 6 + j for pixel (i, j)): with WAVE (Cs / VEC % 64 == 0) every wavefront
-// holds channels of one tile and stores its part from ballots; otherwise the
-// workgroup ORs its threads' masks.
+// holds channels of one tile and builds its part from one ballot per pixel;
+// otherwise the workgroup ORs its threads' masks.
 template <bool BF16, int VEC, bool WAVE>
-__global__ __launch_bounds__(256) void wino_h_input_kernel(
+__global__ __launch_bounds__(256, 3) void wino_h_input_kernel(
     const uint16_t* __restrict__ x, int64_t D, int64_t Dp, int32_t pd, int64_t H, int64_t W,
     int64_t C, int64_t Cs, int32_t ph, int32_t pw, int64_t TH, int64_t TW,
     const float* __restrict__ scales, uint16_t* __restrict__ V, int64_t plane, int64_t total,
@@ -223,7 +231,7 @@ __global__ __launch_bounds__(256) void wino_h_input_kernel(
   const int64_t blk = xcd_block(blockIdx.x, gridDim.x);
   const int64_t t = blk * 256 + threadIdx.x;
   const int64_t groups = Cs / VEC;
-  uint64_t pix = 0;  // WAVE: uniform over the wavefront; else this thread's channels
+  uint64_t pix = 0;  // nonzero pixels (WAVE: of the wavefront's channels, uniform; else this thread's)
   if (t < total) {
   const int64_t r = t / groups, c = (t - r * groups) * VEC;
   const int64_t T = TH * TW;
@@ -237,40 +245,51 @@ __global__ __launch_bounds__(256) void wino_h_input_kernel(
   // Inputs are scaled as they are loaded (exact), so the fp32 transform stays
   // below 2^15 even where 100 max|x| would overflow fp32 (bf16 inputs).
   const float s = scales[0];
-  // column transform first: t1[v][a][j] = sum_i BT[a][i] d[i][j]
-  float t1[VEC][kT][kT];
+  // every load first (unconditional: outside the image they read a zero
+  // block), so that all of them are in flight before the first is used
+  using Raw = typename std::conditional<VEC == 4, uint2, typename std::conditional<VEC == 2, uint32_t,
+                                                                                   uint16_t>::type>::type;
+  Raw raw[kT][kT];
 #pragma unroll
   for (int j = 0; j < kT; ++j) {
     const int64_t iw = iw0 + j;
     const bool wok = cin && iw >= 0 && iw < W;
-    float col[VEC][kT];
 #pragma unroll
     for (int i = 0; i < kT; ++i) {
       const int64_t ih = ih0 + i;
       const bool ok = wok && ih >= 0 && ih < H;
+      raw[i][j] = *reinterpret_cast<const Raw*>(ok ? img + (ih * W + iw) * C
+                                                   : reinterpret_cast<const uint16_t*>(g_wino_h_zero));
+    }
+  }
+  // column transform first: t1[v][a][j] = sum_i BT[a][i] d[i][j]
+  float t1[VEC][kT][kT];
+#pragma unroll
+  for (int j = 0; j < kT; ++j) {
+    float col[VEC][kT];
+#pragma unroll
+    for (int i = 0; i < kT; ++i) {
       uint32_t nz;  // nonzero bits of this pixel's VEC channels (sign bits dropped)
       if constexpr (VEC == 4) {
-        const uint2 q = ok ? *reinterpret_cast<const uint2*>(img + (ih * W + iw) * C) : make_uint2(0u, 0u);
+        const uint2 q = raw[i][j];
         col[0][i] = s * to_f32<uint16_t, BF16>(uint16_t(q.x & 0xffffu));
         col[1][i] = s * to_f32<uint16_t, BF16>(uint16_t(q.x >> 16));
         col[2][i] = s * to_f32<uint16_t, BF16>(uint16_t(q.y & 0xffffu));
         col[3][i] = s * to_f32<uint16_t, BF16>(uint16_t(q.y >> 16));
         nz = (q.x | q.y) & 0x7fff7fffu;
       } else if constexpr (VEC == 2) {
-        const uint32_t q = ok ? *reinterpret_cast<const uint32_t*>(img + (ih * W + iw) * C) : 0u;
+        const uint32_t q = raw[i][j];
         col[0][i] = s * to_f32<uint16_t, BF16>(uint16_t(q & 0xffffu));
         col[1][i] = s * to_f32<uint16_t, BF16>(uint16_t(q >> 16));
         nz = q & 0x7fff7fffu;
       } else {
-        const uint16_t h = ok ? img[(ih * W + iw) * C] : uint16_t(0);
+        const uint16_t h = raw[i][j];
         col[0][i] = s * to_f32<uint16_t, BF16>(h);
         nz = h & 0x7fffu;
       }
-      if constexpr (WAVE) {
-        if (__ballot(nz != 0u) != 0ull) pix |= 1ull << (i * kT + j);
-      } else {
-        pix |= uint64_t(nz != 0u) << (i * kT + j);
-      }
+      // WAVE: one ballot per pixel (the mask stays in scalar registers)
+      if constexpr (WAVE) pix |= uint64_t(__ballot(nz != 0u) != 0ull) << (i * kT + j);
+      else pix |= uint64_t(nz != 0u) << (i * kT + j);
     }
 #pragma unroll
     for (int v = 0; v < VEC; ++v) {
@@ -340,15 +359,25 @@ __global__ __launch_bounds__(256) void wino_h_output_kernel(const float* __restr
   const int64_t im = r / T, rr = r - im * T;
   const int64_t ty = rr / TW, tx = rr - ty * TW;
   uint64_t hits[VEC];
-#pragma unroll
-  for (int v = 0; v < VEC; ++v) hits[v] = 0;
   {
     const int64_t n = im / OD, od = im - n * OD;
     const bool wave = g % 64 == 0;
-    for (int64_t kd = 0; kd < KD; ++kd) {
-      const uint64_t pm = load_tile_mask(tm, (n * Dp + od + kd * dd) * T + rr, g, wave, parts);
+    // a tile whose pixels are all nonzero in every frame the taps read (the
+    // usual case away from padding and zero regions): every output sees a
+    // nonzero pixel under each nonzero tap, and an all-zero filter yields an
+    // exact zero through U = 0 anyway, so the tap masks are not needed
+    uint64_t all = ~0ull;
+    for (int64_t kd = 0; kd < KD; ++kd)
+      all &= load_tile_mask(tm, (n * Dp + od + kd * dd) * T + rr, g, wave, parts);
+    constexpr uint64_t kFull = (1ull << (kT * kT)) - 1;
 #pragma unroll
-      for (int v = 0; v < VEC; ++v) hits[v] |= window_hits<kT>(pm, wm[(o + v) * KD + kd]);
+    for (int v = 0; v < VEC; ++v) hits[v] = (all & kFull) == kFull ? ~0ull : 0ull;
+    if ((all & kFull) != kFull) {
+      for (int64_t kd = 0; kd < KD; ++kd) {
+        const uint64_t m = load_tile_mask(tm, (n * Dp + od + kd * dd) * T + rr, g, wave, parts);
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) hits[v] |= window_hits<kT>(m, wm[kd * O + o + v]);
+      }
     }
   }
   const float* __restrict__ src = Mt + r * O + o;
