@@ -514,7 +514,7 @@ int gemm_launch(const GemmParams& p, void* stream) {
   const bool f32cfg = p.config >= kCfgF32_N32 && p.config <= kCfgF32_N128;
   if (f32cfg != (p.dtype == CNHWC_F32)) return hipErrorInvalidValue;
   if (p.ksplit > 1 && (p.batch != 1 || !p.part || p.config == kCfgH_256x256 ||
-                       p.config == kCfgH_256x128L ||
+                       p.config == kCfgH_256x128L || p.config == kCfgH_Patch ||
                        p.kchunk <= 0 || p.kchunk % gemm_config_bk(p.config) != 0 ||
                        (p.ksplit - 1) * p.kchunk >= p.K))
     return hipErrorInvalidValue;
@@ -533,6 +533,7 @@ int gemm_launch(const GemmParams& p, void* stream) {
     case kCfgH_128x256: return launch_half<TileCfg<128, 256, 64, 128, true, 1>>(p, s);
     case kCfgH_256x256:
     case kCfgH_256x128L: return gemm_lds_launch(p, stream);
+    case kCfgH_Patch: return gemm_patch_launch(p, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -55,6 +55,9 @@ enum GemmConfig : int32_t {
   // workgroup per CU, 256 x 128 at two
   kCfgH_256x256 = 14,
   kCfgH_256x128L = 15,
+  // 3x3 stride-1 implicit GEMM with the input patch of a 256-pixel block
+  // staged in LDS once per 64-channel chunk (gemm_patch.hip): 256 x 256 tiles
+  kCfgH_Patch = 16,
   // Winograd tile-position GEMMs: persistent fp32 kernel with U_p resident in LDS
   kCfgWinoResident = 20,
 };
@@ -65,6 +68,9 @@ enum GemmConfig : int32_t {
 // simple occupancy model over the 256 compute units; lds_ok admits the
 // 256x256 direct-to-LDS tile.
 int32_t pick_gemm_config(int dtype, int64_t m_rows, int64_t n_cols, bool lds_ok);
+// The occupancy model's time estimate for one half-precision configuration
+// (1e300 for fp32 and for configurations outside the model).
+double gemm_config_time(int dtype, int32_t cfg, int64_t m_rows, int64_t n_cols);
 
 
 // A-operand source.
@@ -121,6 +127,27 @@ constexpr int64_t kMaxSplitK = 16;
 inline int64_t gemm_config_bk(int32_t config) {
   return config >= kCfgH_128x64 && config != kCfgH_256x256 && config != kCfgH_256x128L ? 64 : 32;
 }
+
+// fp16/bf16 implicit GEMM of a 3x3, stride-1, dilation-1 conv (2D, or 3D with
+// any depth geometry) with C % 64 == 0, from input patches staged in LDS
+// (kCfgH_Patch).  Row tiles are BH x BW pixel blocks of one output image or
+// frame, BH * BW = 256, BW from patch_block_w (the least padded of 8, 16, 32).
+inline int64_t patch_block_w(int64_t oh, int64_t ow) {
+  int64_t best = 16, best_area = -1;
+  const int64_t cand[3] = {16, 32, 8};
+  for (int64_t bw : cand) {
+    const int64_t bh = 256 / bw;
+    const int64_t area = ((oh + bh - 1) / bh) * bh * ((ow + bw - 1) / bw) * bw;
+    if (best_area < 0 || area < best_area) { best = bw; best_area = area; }
+  }
+  return best;
+}
+inline int64_t patch_row_tiles(int64_t frames, int64_t oh, int64_t ow) {
+  const int64_t bw = patch_block_w(oh, ow), bh = 256 / bw;
+  return frames * ((oh + bh - 1) / bh) * ((ow + bw - 1) / bw);
+}
+bool gemm_patch_ok(const GemmParams& p);
+int gemm_patch_launch(const GemmParams& p, void* stream);  // returns hipError_t
 
 // fp16/bf16 256 x 256 tile GEMM with direct global -> LDS operand loads.
 // Applicable for dense A (lda, ldb, K multiples of 8) and for implicit A with

@@ -199,7 +199,8 @@ cnhwc_status_t split_k_for(int32_t cfg, int64_t m, int64_t n, int64_t k, int32_t
     return CNHWC_OK;
   }
   const int64_t nk = ceil_div(k, gemm_config_bk(cfg));
-  if (cfg == kCfgH_256x256 || cfg == kCfgH_256x128L || force > nk) return CNHWC_ERR_NOT_APPLICABLE;
+  if (cfg == kCfgH_256x256 || cfg == kCfgH_256x128L || cfg == kCfgH_Patch || force > nk)
+    return CNHWC_ERR_NOT_APPLICABLE;
   *splits = int32_t(ceil_div(nk, ceil_div(nk, int64_t(force))));
   return CNHWC_OK;
 }
@@ -212,18 +213,41 @@ uint64_t split_k_bytes(int32_t splits, int64_t rows, int64_t o) {
 // Tile configuration of the implicit / unfold GEMM: forced, or picked.  The
 // direct-to-LDS tiles need C % 32 == 0 (implicit: a K chunk never
 // straddles two taps) or K % 8 == 0 (unfold rows).
-cnhwc_status_t gemm_config_for(const cnhwc_conv_desc_t& d, int64_t m_rows, bool implicit,
-                               int32_t force, int32_t* cfg) {
+// The patch-staged implicit GEMM (gemm_patch.hip): 3x3 taps in the image
+// plane at stride 1 and dilation 1 (any depth geometry), fp16/bf16, C % 64 ==
+// 0, and 32-bit element offsets within one input frame.
+bool patch_ok(const cnhwc_conv_desc_t& d) {
+  return d.dtype != CNHWC_F32 && d.kh == 3 && d.kw == 3 && d.stride[1] == 1 && d.stride[2] == 1 &&
+         d.dil[1] == 1 && d.dil[2] == 1 && d.c % 64 == 0 && d.h * d.w * d.c < (int64_t(1) << 31);
+}
+
+// Relative throughput of the patch-staged tile against the 128x128 tile's
+// (the occupancy model of pick_gemm_config): measured on the C_out axis and
+// video shapes of the sweeps.
+constexpr double kPatchEff = 1.8;
+
+cnhwc_status_t gemm_config_for(const cnhwc_conv_desc_t& d, const int64_t out[3], int64_t m_rows,
+                               bool implicit, int32_t force, int32_t* cfg) {
   const int64_t k = d.kh * d.kw * d.c;
   const bool lds_ok = d.dtype != CNHWC_F32 && (implicit ? d.c % 32 == 0 : k % 8 == 0);
+  const bool pok = implicit && patch_ok(d);
   if (force == 0) {
     *cfg = pick_gemm_config(d.dtype, m_rows, d.o, lds_ok);
+    if (pok) {
+      // the patch tile against the model's pick, by the same waves-of-256-CUs estimate
+      constexpr int64_t kCUs = 256;
+      const int64_t frames = m_rows / (out[1] * out[2]);
+      const int64_t tiles = patch_row_tiles(frames, out[1], out[2]) * ceil_div(d.o, 256);
+      const double t_patch = double(ceil_div(tiles, kCUs)) * 256.0 * 256.0 / kPatchEff;
+      if (t_patch <= gemm_config_time(d.dtype, *cfg, m_rows, d.o)) *cfg = kCfgH_Patch;
+    }
     return CNHWC_OK;
   }
   const bool f32 = force >= kCfgF32_N32 && force <= kCfgF32_N128;
-  const bool half = force >= kCfgH_128x64 && force <= kCfgH_256x128L;
+  const bool half = force >= kCfgH_128x64 && force <= kCfgH_Patch;
   const bool lds = force == kCfgH_256x256 || force == kCfgH_256x128L;
-  if ((d.dtype == CNHWC_F32 && !f32) || (d.dtype != CNHWC_F32 && !half) || (lds && !lds_ok))
+  if ((d.dtype == CNHWC_F32 && !f32) || (d.dtype != CNHWC_F32 && !half) || (lds && !lds_ok) ||
+      (force == kCfgH_Patch && !pok))
     return CNHWC_ERR_NOT_APPLICABLE;
   *cfg = force;
   return CNHWC_OK;
@@ -349,7 +373,7 @@ cnhwc_status_t select_2d(const cnhwc_conv_desc_t& d, const int64_t out[3],
     p->algo = p->inner_algo = CNHWC_ALGO_UNFOLD_GEMM;
     p->unfold_rows = rows;
     p->n_chunks = ceil_div(m_rows, rows);
-    st = gemm_config_for(d, m_rows, false, o.force_gemm_config, &p->kernel_config);
+    st = gemm_config_for(d, out, m_rows, false, o.force_gemm_config, &p->kernel_config);
     if (st != CNHWC_OK) return st;
     st = split_k_for(p->kernel_config, m_rows, d.o, k, o.force_split_k, &p->split_k);
     if (st != CNHWC_OK) return st;
@@ -359,7 +383,7 @@ cnhwc_status_t select_2d(const cnhwc_conv_desc_t& d, const int64_t out[3],
 
   // 3. Implicit GEMM (scratch-free).
   p->algo = p->inner_algo = CNHWC_ALGO_IMPLICIT_GEMM;
-  st = gemm_config_for(d, m_rows, true, o.force_gemm_config, &p->kernel_config);
+  st = gemm_config_for(d, out, m_rows, true, o.force_gemm_config, &p->kernel_config);
   if (st != CNHWC_OK) return st;
   st = split_k_for(p->kernel_config, m_rows, d.o, k, o.force_split_k, &p->split_k);
   if (st != CNHWC_OK) return st;
@@ -444,7 +468,7 @@ cnhwc_status_t select_3d(const cnhwc_conv_desc_t& d, const int64_t out[3],
   p->out_h = out[1];
   p->out_w = out[2];
   p->split_k = 1;
-  cnhwc_status_t st = gemm_config_for(d, m_rows, true, o.force_gemm_config, &p->kernel_config);
+  cnhwc_status_t st = gemm_config_for(d, out, m_rows, true, o.force_gemm_config, &p->kernel_config);
   if (st != CNHWC_OK) return st;
   st = split_k_for(p->kernel_config, m_rows, d.o, k, o.force_split_k, &p->split_k);
   if (st != CNHWC_OK) return st;
@@ -511,6 +535,20 @@ cnhwc_conv_desc_t frame_desc(const cnhwc_conv_desc_t& d3, int64_t od) {
   return f;
 }
 
+namespace {
+// The half-precision candidates of the occupancy model (see pick_gemm_config).
+struct HalfCand { int32_t id; int64_t bm, bn, occ; double eff; };
+constexpr HalfCand kHalfCands[6] = {{kCfgH_128x128, 128, 128, 2, 1.00}, {kCfgH_128x256, 128, 256, 1, 0.85},
+                                    {kCfgH_256x128, 256, 128, 1, 0.80}, {kCfgH_128x64, 128, 64, 2, 0.70},
+                                    {kCfgH_256x256, 256, 256, 1, 1.35}, {kCfgH_256x128L, 256, 128, 2, 1.20}};
+double half_cand_time(const HalfCand& c, int64_t m_rows, int64_t n_cols) {
+  constexpr int64_t kCUs = 256;
+  const int64_t tiles = ceil_div(m_rows, c.bm) * ceil_div(n_cols, c.bn);
+  const int64_t waves = ceil_div(tiles, kCUs * c.occ);
+  return double(waves) * double(c.bm * c.bn * c.occ) / c.eff;
+}
+}  // namespace
+
 int32_t pick_gemm_config(int dtype, int64_t m_rows, int64_t n_cols, bool lds_ok) {
   if (dtype == CNHWC_F32) {
     if (n_cols <= 32) return kCfgF32_N32;
@@ -536,22 +574,21 @@ int32_t pick_gemm_config(int dtype, int64_t m_rows, int64_t n_cols, bool lds_ok)
   // sweep, 1.32-1.47x (256x256, one workgroup per CU) and 1.13-1.40x (256x128,
   // two per CU) the 128x128 rate; the 256x128 tile wastes less when O is not
   // a multiple of 256.
-  struct Cand { int32_t id; int64_t bm, bn, occ; double eff; };
-  const Cand cands[6] = {{kCfgH_128x128, 128, 128, 2, 1.00}, {kCfgH_128x256, 128, 256, 1, 0.85},
-                         {kCfgH_256x128, 256, 128, 1, 0.80}, {kCfgH_128x64, 128, 64, 2, 0.70},
-                         {kCfgH_256x256, 256, 256, 1, 1.35}, {kCfgH_256x128L, 256, 128, 2, 1.20}};
-  constexpr int64_t kCUs = 256;
   int32_t best = kCfgH_128x128;
   double best_t = 1e300;
-  for (const Cand& c : cands) {
+  for (const HalfCand& c : kHalfCands) {
     if ((c.id == kCfgH_256x256 || c.id == kCfgH_256x128L) && !lds_ok) continue;
-    const int64_t tiles = ceil_div(m_rows, c.bm) * ceil_div(n_cols, c.bn);
-    const int64_t slots = kCUs * c.occ;
-    const int64_t waves = ceil_div(tiles, slots);
-    const double t = double(waves) * double(c.bm * c.bn * c.occ) / c.eff;
+    const double t = half_cand_time(c, m_rows, n_cols);
     if (t < best_t) { best_t = t; best = c.id; }
   }
   return best;
+}
+
+double gemm_config_time(int dtype, int32_t cfg, int64_t m_rows, int64_t n_cols) {
+  if (dtype == CNHWC_F32) return 1e300;
+  for (const HalfCand& c : kHalfCands)
+    if (c.id == cfg) return half_cand_time(c, m_rows, n_cols);
+  return 1e300;
 }
 
 bool plan_equal(const cnhwc_plan_t& a, const cnhwc_plan_t& b) {

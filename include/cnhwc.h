@@ -130,14 +130,17 @@ typedef struct {
   int64_t force_tile_batch;  /* Winograd: 0 = budget rule; else min(value, budget tile) */
   int64_t force_unfold_rows; /* Unfold: 0 = the fixed byte cap; else rows per chunk */
   int32_t force_gemm_config; /* 0 = select; else a GEMM tile configuration id for the
-                                implicit / unfold GEMM (fp16/bf16: 10..14; fp32: 1..4).
-                                An id that does not suit the dtype or the shape is
-                                CNHWC_ERR_NOT_APPLICABLE. */
+                                implicit / unfold GEMM (fp16/bf16: 10..16; fp32: 1..4).
+                                16 is the implicit GEMM of 3x3 stride-1 dilation-1
+                                convs with C % 64 == 0 that stages each input patch
+                                in LDS once per 64 channels (K ordered depth tap,
+                                64-channel chunk, kh, kw).  An id that does not suit
+                                the dtype or the shape is CNHWC_ERR_NOT_APPLICABLE. */
   int32_t force_split_k;     /* implicit / unfold GEMM: 0 = select, 1 = no K split,
                                 s > 1 = s splits of whole K chunks (trailing empty
-                                splits dropped).  NOT_APPLICABLE with the 256x256
-                                tile or for more splits than K chunks.  Winograd
-                                ignores it. */
+                                splits dropped).  NOT_APPLICABLE with the 256-row
+                                tiles (14, 15, 16) or for more splits than K chunks.
+                                Winograd ignores it. */
 } cnhwc_select_opts_t;
 
 /* A plan: a plain value, a pure function of (descriptor, options). */

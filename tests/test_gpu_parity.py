@@ -291,6 +291,81 @@ def test_lds_tile_3d_accumulating_epilogue(dtype):
     assert torch.equal(bits(y), bits(y11))
 
 
+# ------------------------------- implicit GEMM from input patches staged in LDS
+# Config 16: 3x3 stride-1 convs with C % 64 == 0; each 256-pixel block's input
+# patch is loaded once per 64 channels and all nine taps read it.  Shapes span
+# several blocks and column tiles with ragged tails, all three block widths
+# (16 x 16, 8 x 32 for wide images, 32 x 8 for narrow ones), padding 0 and 1,
+# images smaller than one block, and 3D with depth padding, stride and dilation.
+
+PATCH_CASES = [  # name, n, h, w, c, o, pad
+    ("c64_o300", 2, 20, 20, 64, 300, 1),
+    ("c128_o256_p0", 1, 33, 35, 128, 256, 0),
+    ("c192_o520_ragged", 3, 17, 29, 192, 520, 1),
+    ("c64_tiny", 2, 5, 3, 64, 70, 1),
+    ("c64_wide", 1, 6, 70, 64, 256, 1),
+    ("c256_narrow", 1, 70, 5, 256, 96, 1),
+]
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("spec", PATCH_CASES, ids=[c[0] for c in PATCH_CASES])
+def test_patch_tile_parity(dtype, spec):
+    name, n, h, w, c, o, p = spec
+    case = cw.ConvCase(f"patch_{name}_{dtype}", n, h, w, c, o, 3, 3, (1, 1), (p, p), (1, 1), dtype,
+                       "normal", "normal", None, 29, len(name) * 3 + c)
+    x, wt = case.input(), case.weight()
+    yr, den = oracle.conv(to_oracle(x), to_oracle(wt), **case.conv_kwargs())
+    plan = cn.plan2d(case.x_shape(), case.w_shape(), **case.conv_kwargs(), dtype=x.dtype, algo="implicit_gemm",
+                     gemm_config=16)
+    assert plan.kernel_config == 16
+    y = cn.conv2d(_dev(x), _dev(wt), **case.conv_kwargs(), plan=plan, out=poisoned(yr.shape, x.dtype))
+    check_parity(y.cpu(), yr, den, y.dtype, f"{case.name}/cfg16")
+    y2 = cn.conv2d(_dev(x), _dev(wt), **case.conv_kwargs(), plan=plan)
+    assert torch.equal(bits(y), bits(y2)), f"{case.name}: run-to-run bits differ"
+
+
+PATCH3D_CASES = [  # name, n, d, h, w, c, o, kd, stride, pad, dil, dtype
+    ("video_like", 1, 7, 20, 22, 64, 288, 3, (1, 1, 1), (0, 1, 1), (1, 1, 1), "bf16"),
+    ("pad_d_batch2", 2, 6, 9, 10, 64, 80, 3, (1, 1, 1), (1, 1, 1), (1, 1, 1), "f16"),
+    ("stride_d2_dil_d2", 1, 11, 12, 19, 128, 64, 3, (2, 1, 1), (1, 0, 1), (2, 1, 1), "bf16"),
+    ("kd1", 2, 3, 17, 9, 64, 256, 1, (1, 1, 1), (0, 1, 1), (1, 1, 1), "f16"),
+]
+
+
+@pytest.mark.parametrize("spec", PATCH3D_CASES, ids=[c[0] for c in PATCH3D_CASES])
+def test_patch_tile_3d_parity(spec):
+    name, n, d, h, w, c, o, kd, s_, p_, dl, dt = spec
+    case = cw.ConvCase(f"patch3d_{name}", n, h, w, c, o, 3, 3, s_, p_, dl, dt, "normal", "normal", None, 31,
+                       len(name) + c, nd=3, d=d, kd=kd)
+    x, wt = case.input(), case.weight()
+    yr, den = oracle.conv(to_oracle(x), to_oracle(wt), **case.conv_kwargs())
+    plan = cn.plan3d(case.x_shape(), case.w_shape(), **case.conv_kwargs(), dtype=x.dtype, algo="implicit_gemm",
+                     gemm_config=16)
+    assert plan.kernel_config == 16
+    y = cn.conv3d(_dev(x), _dev(wt), **case.conv_kwargs(), plan=plan, out=poisoned(yr.shape, x.dtype))
+    check_parity(y.cpu(), yr, den, y.dtype, f"{case.name}/cfg16")
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_patch_tile_accumulating_epilogue(dtype):
+    """The per-tap 2D convs of the 3D decomposition through config 16 (first /
+    middle / last tap epilogues), and KD = 1 giving conv2d's bits."""
+    case = cw.ConvCase(f"patchkd_{dtype}", 1, 18, 19, 64, 272, 3, 3, (1, 1, 1), (0, 1, 1), (1, 1, 1), dtype,
+                       "normal", "normal", None, 33, 5, nd=3, d=6, kd=3)
+    x, wt = case.input(), case.weight()
+    plan = cn.plan3d(case.x_shape(), case.w_shape(), **case.conv_kwargs(), dtype=x.dtype, algo="small_kd",
+                     inner_algo="implicit_gemm", gemm_config=16)
+    assert plan.algo_name == "small_kd" and plan.kernel_config == 16
+    y = cn.conv3d(_dev(x), _dev(wt), **case.conv_kwargs(), plan=plan)
+    yr, den = oracle.conv(to_oracle(x), to_oracle(wt), **case.conv_kwargs())
+    check_parity(y.cpu(), yr, den, y.dtype, case.name)
+    x1, w1 = _dev(x[:, :4]), _dev(wt[:, :1].contiguous())
+    y3 = cn.conv3d(x1, w1, 1, (0, 1, 1), 1, algo="implicit_gemm", gemm_config=16)
+    y2 = cn.conv2d(x1[0], w1[:, 0].contiguous(), 1, 1, 1, algo="implicit_gemm", gemm_config=16)
+    assert torch.equal(bits(y3[0]), bits(y2))
+
+
 # ---------------------------------------------------------------- split K
 # Small-grid GEMMs split K; the partial sums are added in a fixed order by a
 # second kernel.  Forced splits (including a short last split) on every dtype

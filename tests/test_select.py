@@ -370,18 +370,45 @@ def test_3d_forced_inner_winograd():
 F16 = torch.float16
 
 
-def test_large_half_convs_take_the_256_tile():
-    """Large fp16/bf16 implicit GEMMs (C % 32 == 0) get the 256x256 direct-to-LDS tile;
-    small ones (a ResNet-50 batch-1 layer) and C % 32 != 0 do not."""
+def test_large_half_convs_take_the_256_tiles():
+    """Large fp16/bf16 implicit GEMMs of 3x3 stride-1 convs with C % 64 == 0 get
+    the patch-staged 256x256 tile (16); other large ones with C % 32 == 0 the
+    256x256 direct-to-LDS tile (14); small ones (a ResNet-50 batch-1 layer) and
+    C % 32 != 0 neither."""
     big = cn.plan2d((64, 32, 32, 256), (4096, 3, 3, 256), 1, 1, 1, F16, algo="implicit_gemm")
-    assert big.kernel_config == 14
+    assert big.kernel_config == 16
     big3 = cn.plan3d((1, 41, 120, 208, 512), (512, 3, 3, 3, 512), 1, (0, 1, 1), 1, torch.bfloat16,
                      algo="implicit_gemm")
-    assert big3.kernel_config == 14
+    assert big3.kernel_config == 16
+    for xs, ws, s in (((64, 32, 32, 96), (4096, 3, 3, 96), 1), ((64, 64, 64, 256), (4096, 3, 3, 256), 2),
+                      ((64, 32, 32, 256), (4096, 5, 5, 256), 1)):
+        assert cn.plan2d(xs, ws, s, 1, 1, F16, algo="implicit_gemm").kernel_config == 14
     small = cn.plan2d((1, 56, 56, 64), (64, 3, 3, 64), 1, 1, 1, F16)
-    assert small.kernel_config != 14
+    assert small.kernel_config not in (14, 16)
     odd = cn.plan2d((64, 32, 32, 120), (4096, 3, 3, 120), 1, 1, 1, F16, algo="implicit_gemm")
-    assert odd.kernel_config != 14
+    assert odd.kernel_config not in (14, 16)
+
+
+def test_patch_tile_forcing():
+    """Config 16 needs 3x3 taps at stride 1 and dilation 1 in the image plane and
+    C % 64 == 0 (any depth geometry); it takes no K split."""
+    ok = cn.plan2d((2, 20, 20, 64), (300, 3, 3, 64), 1, 1, 1, F16, algo="implicit_gemm", gemm_config=16)
+    assert ok.kernel_config == 16 and ok.split_k == 1 and ok.workspace_bytes == 0
+    ok3 = cn.plan3d((2, 8, 17, 15, 64), (256, 3, 3, 3, 64), (2, 1, 1), (1, 1, 1), (2, 1, 1), torch.bfloat16,
+                    algo="implicit_gemm", gemm_config=16)
+    assert ok3.kernel_config == 16
+    for xs, ws, s, d, dt in (((2, 20, 20, 96), (64, 3, 3, 96), 1, 1, F16), ((2, 20, 20, 64), (64, 3, 3, 64), 2, 1, F16),
+                             ((2, 20, 20, 64), (64, 3, 3, 64), 1, 2, F16), ((2, 20, 20, 64), (64, 5, 5, 64), 1, 1, F16),
+                             ((2, 20, 20, 64), (64, 3, 3, 64), 1, 1, torch.float32)):
+        with pytest.raises(cn.CnhwcError) as e:
+            cn.plan2d(xs, ws, s, 1, d, dt, algo="implicit_gemm", gemm_config=16)
+        assert e.value.name == "NOT_APPLICABLE"
+    with pytest.raises(cn.CnhwcError) as e:
+        cn.plan2d((2, 20, 20, 64), (300, 3, 3, 64), 1, 1, 1, F16, algo="implicit_gemm", gemm_config=16, split_k=2)
+    assert e.value.name == "NOT_APPLICABLE"
+    with pytest.raises(cn.CnhwcError) as e:  # dense A (unfold rows) never takes it
+        cn.plan2d((2, 20, 20, 64), (300, 3, 3, 64), 1, 1, 1, F16, algo="unfold_gemm", gemm_config=16)
+    assert e.value.name == "NOT_APPLICABLE"
 
 
 def test_forced_gemm_config():
