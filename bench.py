@@ -72,7 +72,8 @@ def parse():
 # The sources the headline workload's kernels (the fp32 Winograd transforms and
 # the resident Winograd GEMM) are compiled from, headers included (and the
 # public header include/cnhwc.h, which they include too).
-HEADLINE_SOURCES = ("winograd.hip", "wino_gemm.hip", "wino_f63_api.hpp", "device_common.hpp", "winograd_f63.h")
+HEADLINE_SOURCES = ("winograd.hip", "wino_gemm.hip", "wino_f63_api.hpp", "wino_mask.hpp", "device_common.hpp",
+                    "winograd_f63.h")
 
 
 def _code_only(text):

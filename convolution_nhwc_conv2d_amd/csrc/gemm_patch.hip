@@ -31,10 +31,11 @@
 // channel); the two differ in rounding only.)
 //
 // LDS layouts: patch pixel p at 128 p, its 16-byte piece c (8 channels) at
-// physical piece c ^ (p & 7); weight row r of a stage at 128 r, piece c at
-// c ^ (r & 7).  Eight consecutive rows (or pixels) of one logical piece then
-// hit eight distinct bank groups.  A lane's LDS destination is fixed by its
-// lane index, so the swizzle is applied on the global side.
+// physical piece c ^ ((p >> 1) & 7); weight row r of a stage at 128 r, piece
+// c at c ^ ((r >> 1) & 7).  Sixteen consecutive rows (or pixels) of one
+// logical piece then hit sixteen distinct bank groups.  A lane's LDS
+// destination is fixed by its lane index, so the swizzle is applied on the
+// global side.
 //
 // MFMA: v_mfma_f32_32x32x16_{f16,bf16}; in 16-channel step s of a chunk,
 // lanes 0..31 supply channels 16 s + 0..7 and lanes 32..63 16 s + 8..15 of
@@ -112,6 +113,13 @@ __device__ __forceinline__ int64_t xcd_tile(int64_t bid, int64_t n) {
 }
 constexpr int64_t kGroupM = 8;
 
+// Physical 16-byte piece of logical piece c in LDS row (pixel) r is
+// c ^ swz(r).  A 128-byte row covers half of the 64 four-byte banks, so rows
+// r and r + 1 cover the two halves; with swz(r) = (r >> 1) & 7 any 16
+// consecutive rows of one logical piece (the lanes a 16-byte read serves
+// together) land on 16 distinct 16-byte bank groups.
+__device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
+
 struct Frag {
   uint4 a[4];
   uint4 b[4];
@@ -161,7 +169,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_patch_kernel(const GemmParam
 #pragma unroll
   for (int j = 0; j < kPatchLoads; ++j) {
     const int pix = 8 * (wave * kPatchLoads + j) + (lane >> 3);
-    const int lpc = (lane & 7) ^ (pix & 7);
+    const int lpc = (lane & 7) ^ swz(pix);
     const int py = pix / PW, px = pix - (pix / PW) * PW;
     const int64_t iy = oh0 - p.ph + py, ix = ow0 - p.pw + px;
     const bool ok = pix < PPIX && iy >= 0 && iy < H && ix >= 0 && ix < W;
@@ -172,8 +180,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_patch_kernel(const GemmParam
   const uint16_t* brow[kBLoads];  // null: a row past O
 #pragma unroll
   for (int j = 0; j < kBLoads; ++j) {
-    const int64_t row = n0 + (wave * kBLoads + j) * 8 + (lane >> 3);
-    const int lpc = (lane & 7) ^ (lane >> 3);
+    const int rl = (wave * kBLoads + j) * 8 + (lane >> 3);  // row within the tile
+    const int64_t row = n0 + rl;
+    const int lpc = (lane & 7) ^ swz(rl);
     brow[j] = row < N ? Bw + row * p.ldb + lpc * 8 : nullptr;
   }
 
@@ -239,7 +248,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_patch_kernel(const GemmParam
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int r = wn * 128 + j * 32 + frow;
-      rb_off[s][j] = uint32_t(r * kRowB + (((2 * s + khalf) ^ (r & 7)) << 4));
+      rb_off[s][j] = uint32_t(r * kRowB + (((2 * s + khalf) ^ swz(r)) << 4));
       asm volatile("" : "+v"(rb_off[s][j]));
     }
   int pbl[4];  // pb, re-derived opaquely every iteration: the compiler would otherwise
@@ -250,7 +259,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_patch_kernel(const GemmParam
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int px = pbl[i] + shift;
-      const uint32_t off = uint32_t(px * kRowB + (((2 * s + khalf) ^ (px & 7)) << 4));
+      const uint32_t off = uint32_t(px * kRowB + (((2 * s + khalf) ^ swz(px)) << 4));
       fr.a[i] = *reinterpret_cast<const uint4*>(pbase + off);
     }
     const uint8_t* wbase = g_wring + wstage * kBStage;
