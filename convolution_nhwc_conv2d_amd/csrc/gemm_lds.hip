@@ -49,14 +49,15 @@ namespace {
 constexpr int kBM = 256;  // tile rows
 constexpr int kThreads = 256;
 
-// Physical 16-byte piece of logical piece c in LDS row r, so that the 8 lanes
-// served per LDS cycle (8 consecutive rows, same logical piece) hit distinct
-// bank groups: 64-byte rows (4 pieces, two rows per 128-byte bank line) XOR
-// bits 1..2 of the row; 128-byte rows (8 pieces) XOR bits 0..2.
+// Physical 16-byte piece of logical piece c in LDS row r, so that 16
+// consecutive rows of one logical piece (the lanes a 16-byte LDS read serves
+// together) hit 16 distinct 16-byte bank groups of the 64 four-byte banks:
+// 64-byte rows (4 pieces, four rows per 256-byte bank line) XOR bits 2..3 of
+// the row; 128-byte rows (8 pieces, two rows per bank line) XOR bits 1..3.
 template <int PIECES>
 __device__ __forceinline__ int piece(int r, int c) {
-  if constexpr (PIECES == 4) return c ^ ((r >> 1) & 3);
-  else return c ^ (r & 7);
+  if constexpr (PIECES == 4) return c ^ ((r >> 2) & 3);
+  else return c ^ ((r >> 1) & 7);
 }
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -199,21 +200,26 @@ __global__ __launch_bounds__(kThreads, T::OCC) void gemm_lds_kernel(const GemmPa
   const uint16_t* __restrict__ A = reinterpret_cast<const uint16_t*>(p.a) + bz * p.stride_a;
   const uint16_t* __restrict__ B = reinterpret_cast<const uint16_t*>(p.b) + bz * p.stride_b;
 
-  // ---- this lane's load slots: row (lane >> 2) of each 16-row block, piece
-  // slot lane & 3, holding logical piece lpc (the row swizzle inverted; block
-  // bases are multiples of 16 rows, so it is the same for every block).
+  // ---- this lane's load slots: row lane / kPieces of each block of
+  // kRowsPerLoad rows (16 rows of 64 bytes, or 8 of 128), piece slot
+  // lane % kPieces, holding the logical piece the row swizzle puts there (the
+  // swizzle is its own inverse).  The swizzle depends on the row modulo 16:
+  // with 16-row blocks that is the same for every block (kin), with 8-row
+  // blocks it alternates from block to block (kin_of).
   const int lrow = lane / kPieces;
-  const int lpc = piece<kPieces>(lrow, lane % kPieces);  // the swizzle is its own inverse
-  const int kin = lpc * 8;  // element offset of the piece within the chunk
+  auto kin_of = [&](int row_in_tile) { return piece<kPieces>(row_in_tile, lane % kPieces) * 8; };
+  const int kin = kin_of(lrow);  // element offset of the piece within the chunk (16-row blocks)
 
   int64_t a_off[kLoadsA];
   int32_t a_ih0[kLoadsA], a_iw0[kLoadsA], a_id0[kLoadsA];
 #pragma unroll
   for (int j = 0; j < kLoadsA; ++j) {
-    const int64_t m = m0 + (wave * kLoadsA + j) * kRowsPerLoad + lrow;
+    const int rt = (wave * kLoadsA + j) * kRowsPerLoad + lrow;  // row within the tile
+    const int64_t m = m0 + rt;
+    const int kin_j = kin_of(rt);
     a_id0[j] = 0;
     if (!IMPLICIT) {
-      a_off[j] = m < M ? m * p.lda + kin : -1;
+      a_off[j] = m < M ? m * p.lda + kin_j : -1;
       a_ih0[j] = a_iw0[j] = 0;
     } else if (m < M) {
       const int64_t hw = p.oh * p.ow;
@@ -235,7 +241,7 @@ __global__ __launch_bounds__(kThreads, T::OCC) void gemm_lds_kernel(const GemmPa
       a_iw0[j] = int32_t(ow * p.sw - p.pw);
       const int64_t depth = D3 ? p.d : 1;
       a_off[j] = n * depth * p.h * p.w * p.c +
-                 ((int64_t(a_id0[j]) * p.h + a_ih0[j]) * p.w + a_iw0[j]) * p.c + kin;
+                 ((int64_t(a_id0[j]) * p.h + a_ih0[j]) * p.w + a_iw0[j]) * p.c + kin_j;
     } else {
       a_off[j] = 0;
       a_ih0[j] = -0x40000000;
@@ -246,8 +252,9 @@ __global__ __launch_bounds__(kThreads, T::OCC) void gemm_lds_kernel(const GemmPa
   int64_t b_off[kLoadsB];
 #pragma unroll
   for (int j = 0; j < kLoadsB; ++j) {
-    const int64_t n = n0 + (wave * kLoadsB + j) * kRowsPerLoad + lrow;
-    b_off[j] = n < N ? n * p.ldb + kin : -1;
+    const int rt = (wave * kLoadsB + j) * kRowsPerLoad + lrow;
+    const int64_t n = n0 + rt;
+    b_off[j] = n < N ? n * p.ldb + kin_of(rt) : -1;
   }
 
   // ---- K position of the next chunk to issue (implicit: C % 32 == 0, so a
@@ -302,6 +309,7 @@ __global__ __launch_bounds__(kThreads, T::OCC) void gemm_lds_kernel(const GemmPa
         t_kh = t_kh == p.kh ? 0 : t_kh;
       }
     } else {
+      static_assert(kRowsPerLoad == 16, "dense A uses 16-row load blocks: kin is every slot's offset");
       const bool k_in = k_next + kin < K;
 #pragma unroll
       for (int j = 0; j < kLoadsA; ++j) {
