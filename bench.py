@@ -62,7 +62,7 @@ def parse():
                          "with --calib-copy, write profiles/traffic.json, print it and exit")
     ap.add_argument("--suite", default=None,
                     help="instead of the headline line, time other workloads: "
-                         "comma list of small,wide,sweep,wino_half,resnet,video,video_auto,video_gemm,conv1d,"
+                         "comma list of small,wide,sweep,wino_half,resnet,video,video_auto,video_gemm,big_gemm,conv1d,"
                          "vendor_gemm "
                          "or 'all' "
                          "(one JSON line each)")
@@ -410,6 +410,23 @@ def run_suite(names):
         for shape in cw.VIDEO3D_SHAPES:
             r = measure(cw.video3d(*shape))
             r["suite"] = "video3d_auto"
+            emit(r)
+    if "big_gemm" in names:
+        # the largest half-precision GEMM stages alone, for counter profiles:
+        # the C_out 4096 implicit GEMM (65536 x 4096 x 2304) in f16 and bf16,
+        # the K-axis one (16384 x 1024 x 9216), the native 3D video GEMM
+        # (973440 x 512 x 13824) and the video conv on AUTO (half-precision
+        # Winograd, taps summed in its GEMMs)
+        for dt in ("f16", "bf16"):
+            r = measure(cw.cout_axis(dt, 4096, 64), "implicit_gemm")
+            r["suite"] = "big_gemm"
+            emit(r)
+        r = measure(cw.cout_axis("f16", 1024, 16, 1024), "implicit_gemm")
+        r["suite"] = "big_gemm"
+        emit(r)
+        for algo in ("implicit_gemm", "auto"):
+            r = measure(cw.video3d(41, 120, 208, 512, 512), algo)
+            r["suite"] = "big_gemm"
             emit(r)
     if "wino_half" in names:
         # half-precision Winograd F(4x4,3x3) against the implicit GEMM around

@@ -42,6 +42,7 @@
 // their row.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <type_traits>
 
 #include "internal.hpp"
@@ -103,15 +104,10 @@ __device__ __forceinline__ void block_barrier() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-// Workgroups go round-robin to the 8 XCDs; XCD x takes one contiguous range
-// of tile indices (a bijection on [0, n)).
-__device__ __forceinline__ int64_t xcd_tile(int64_t bid, int64_t n) {
-  constexpr int64_t kXcd = 8;
-  const int64_t x = bid % kXcd, k = bid / kXcd;
-  const int64_t q = n / kXcd, r = n % kXcd;
-  return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + k;
-}
+// Row tiles are grouped kGroupM at a time, so that the workgroups of one XCD
+// running together share input rows.
 constexpr int64_t kGroupM = 8;
+constexpr int kMaxDevices = 64;
 
 // Physical 16-byte piece of logical piece c in LDS row (pixel) r is
 // c ^ swz(r).  A 128-byte row covers half of the 64 four-byte banks, so rows
@@ -128,7 +124,24 @@ struct Frag {
 template <int V>
 using ic = std::integral_constant<int, V>;
 
+// Where a row tile sits: frame f (image, or n * OD + od in 3D), its first
+// output row and column, and the first output channel of its column tile.
+struct TileGeo {
+  int32_t f, img, od, oh0, ow0, n0;
+};
+
 // BW: block width (output columns); the block is (256 / BW) x BW pixels.
+//
+// Persistent: the grid holds at most one workgroup per CU, and each workgroup
+// walks a fixed list of tiles.  Tile t of n is assigned as follows: the 8 XCDs
+// take contiguous ranges of tile indices; the kx workgroups of XCD x (those
+// with blockIdx.x % 8 == x) take every kx-th tile of its range, so the tiles
+// an XCD runs at one time are consecutive and share input rows and weights in
+// its L2.  The load sequence runs on across tiles: during a tile's last
+// (depth tap, chunk) iteration, the patch slices and the first two weight
+// stages that are loaded are the next tile's, so a tile starts with its
+// operands in LDS.  The loads of a workgroup's last iteration, which have no
+// next tile, read a zero vector into buffers that are never read.
 template <bool BF16, bool D3, int BW>
 __global__ __launch_bounds__(kThreads, 1) void gemm_patch_kernel(const GemmParams p) {
   constexpr int BH = 256 / BW;
@@ -138,90 +151,110 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_patch_kernel(const GemmParam
   const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
   const int wm = wave >> 1, wn = wave & 1;
   const int64_t N = p.N, C = p.c, H = p.h, W = p.w, OH = p.oh, OW = p.ow;
-  const int64_t OD = D3 ? p.od : 1, KD = D3 ? p.kd : 1, D = D3 ? p.d : 1;
-  const int64_t frames = p.M / (OH * OW);  // output images (2D) or frames n * OD + od (3D)
+  const int64_t KD = D3 ? p.kd : 1, D = D3 ? p.d : 1;
+  const int32_t OD = D3 ? int32_t(p.od) : 1;
 
-  // ---- tile: (frame, block row, block column) x column tile, in groups of
-  // kGroupM row tiles per XCD range so that concurrent workgroups share rows.
-  const int64_t tby = (OH + BH - 1) / BH, tbx = (OW + BW - 1) / BW;
-  const int64_t mt = frames * tby * tbx, nt = (N + kBN - 1) / kBN;
-  const int64_t t = xcd_tile(blockIdx.x, gridDim.x);
-  const int64_t group = t / (kGroupM * nt);
-  const int64_t first_m = group * kGroupM;
-  const int64_t gsz = mt - first_m < kGroupM ? mt - first_m : kGroupM;
-  const int64_t tg = t - group * (kGroupM * nt);
-  const int64_t mtile = first_m + tg % gsz;
-  const int64_t n0 = (tg / gsz) * kBN;
-  const int64_t f = mtile / (tby * tbx);
-  const int64_t rb = mtile - f * (tby * tbx);
-  const int64_t by = rb / tbx, bx = rb - by * tbx;
-  const int64_t oh0 = by * BH, ow0 = bx * BW;
-  const int64_t img = f / OD, od = f - img * OD;  // input element and output frame
+  // ---- this workgroup's tiles (32-bit indices: the tile count is below 2^31)
+  const int32_t tby = int32_t((OH + BH - 1) / BH), tbx = int32_t((OW + BW - 1) / BW);
+  const int32_t frames = int32_t(p.M / (OH * OW));
+  const int32_t mt = frames * tby * tbx, nt = int32_t((N + kBN - 1) / kBN);
+  const int32_t ntiles = mt * nt;
+  const int32_t G = int32_t(gridDim.x), xcd = int32_t(blockIdx.x) % 8, kw8 = int32_t(blockIdx.x) / 8;
+  const int32_t kx = G / 8 + (xcd < G % 8 ? 1 : 0);
+  const int32_t q8 = ntiles / 8, r8 = ntiles % 8;
+  const int32_t xs = xcd < r8 ? xcd * (q8 + 1) : r8 * (q8 + 1) + (xcd - r8) * q8;
+  const int32_t xl = q8 + (xcd < r8 ? 1 : 0);
+  if (kw8 >= xl) return;
+  const int32_t my_tiles = (xl - kw8 + kx - 1) / kx;
+  auto tile_geo = [&](int32_t j) {
+    const int32_t t = xs + kw8 + j * kx;
+    const int32_t group = t / (int32_t(kGroupM) * nt);
+    const int32_t first_m = group * int32_t(kGroupM);
+    const int32_t gsz = mt - first_m < int32_t(kGroupM) ? mt - first_m : int32_t(kGroupM);
+    const int32_t tg = t - group * (int32_t(kGroupM) * nt);
+    const int32_t mtile = first_m + tg % gsz;
+    TileGeo g;
+    g.n0 = (tg / gsz) * kBN;
+    g.f = mtile / (tby * tbx);
+    const int32_t rb = mtile - g.f * (tby * tbx);
+    const int32_t by = rb / tbx;
+    g.oh0 = by * BH;
+    g.ow0 = (rb - by * tbx) * BW;
+    g.img = g.f / OD;
+    g.od = g.f - g.img * OD;
+    return g;
+  };
   const uint16_t* __restrict__ X = reinterpret_cast<const uint16_t*>(p.a);
   const uint16_t* __restrict__ Bw = reinterpret_cast<const uint16_t*>(p.b);
   const gvec_ptr zero = gvec(&g_patch_zero16);
 
   // ---- patch load slots: slot j of this wavefront is 1 KB load q = 11 wave
   // + j, pixels 8 q .. 8 q + 7; lane l holds pixel 8 q + l / 8, physical
-  // piece l % 8, i.e. logical piece (l % 8) ^ (pixel & 7).  Offsets are within
-  // one input frame (-1: outside the image or past the patch).
+  // piece l % 8, i.e. logical piece (l % 8) ^ swz(pixel).  Offsets are within
+  // one input frame (-1: outside the image or past the patch), for the tile
+  // whose patches are being loaded (pg).
   int32_t poff[kPatchLoads];  // a frame has fewer than 2^31 elements (gemm_patch_ok)
+  TileGeo pg;
+  auto set_patch_tile = [&](const TileGeo& g) {
+    pg = g;
 #pragma unroll
-  for (int j = 0; j < kPatchLoads; ++j) {
-    const int pix = 8 * (wave * kPatchLoads + j) + (lane >> 3);
-    const int lpc = (lane & 7) ^ swz(pix);
-    const int py = pix / PW, px = pix - (pix / PW) * PW;
-    const int64_t iy = oh0 - p.ph + py, ix = ow0 - p.pw + px;
-    const bool ok = pix < PPIX && iy >= 0 && iy < H && ix >= 0 && ix < W;
-    poff[j] = ok ? int32_t((iy * W + ix) * C + lpc * 8) : -1;
-  }
+    for (int j = 0; j < kPatchLoads; ++j) {
+      const int pix = 8 * (wave * kPatchLoads + j) + (lane >> 3);
+      const int lpc = (lane & 7) ^ swz(pix);
+      const int py = pix / PW, px = pix - (pix / PW) * PW;
+      const int32_t iy = g.oh0 - p.ph + py, ix = g.ow0 - p.pw + px;
+      const bool ok = pix < PPIX && iy >= 0 && iy < H && ix >= 0 && ix < W;
+      poff[j] = ok ? (iy * int32_t(W) + ix) * int32_t(C) + lpc * 8 : -1;
+    }
+  };
   // ---- weight load slots: slot j holds row (8 wave + j) * 8 + l / 8 of the
-  // tile's 256, logical piece (l % 8) ^ (row & 7) (row & 7 == l / 8).
+  // tile's 256, logical piece (l % 8) ^ swz(row), for the column tile whose
+  // weights are being loaded.
   const uint16_t* brow[kBLoads];  // null: a row past O
+  auto set_weight_tile = [&](int32_t n0) {
 #pragma unroll
-  for (int j = 0; j < kBLoads; ++j) {
-    const int rl = (wave * kBLoads + j) * 8 + (lane >> 3);  // row within the tile
-    const int64_t row = n0 + rl;
-    const int lpc = (lane & 7) ^ swz(rl);
-    brow[j] = row < N ? Bw + row * p.ldb + lpc * 8 : nullptr;
-  }
+    for (int j = 0; j < kBLoads; ++j) {
+      const int rl = (wave * kBLoads + j) * 8 + (lane >> 3);  // row within the tile
+      const int64_t row = int64_t(n0) + rl;
+      const int lpc = (lane & 7) ^ swz(rl);
+      brow[j] = row < N ? Bw + row * p.ldb + lpc * 8 : nullptr;
+    }
+  };
 
   const int64_t nchunk = C / 64;
-  const int64_t nit = KD * nchunk;          // (depth tap, chunk) iterations
+  const int64_t nit = KD * nchunk;          // (depth tap, chunk) iterations per tile
   const int64_t nsteps = nit * kTaps;
   const uint32_t patch_lds = lds_base(g_patch) + wave * (kPatchLoads * 1024);
   const uint32_t w_lds = lds_base(g_wring) + wave * (kBLoads * 1024);
 
-  // Weight rows of global step g into stage g & 1 (past the end the rows
-  // wrap around to real data, loaded into a stage that is never read again;
-  // the stage still follows the unwrapped g, which keeps it off the stage in
-  // use).
-  auto issue_w = [&](int64_t g) {
-    const uint32_t dst = w_lds + uint32_t(g & 1) * kBStage;
-    g = g < nsteps ? g : g - nsteps;
-    const int64_t it = g / kTaps, tap = g - it * kTaps;
+  // Weight rows of the tile's step ls (ls >= nsteps: the next tile's step
+  // ls - nsteps; `real` false: no next tile, a zero vector) into the stage of
+  // global step gs.
+  auto issue_w = [&](int64_t ls, int64_t gs, bool real) {
+    const uint32_t dst = w_lds + uint32_t(gs & 1) * kBStage;
+    ls = ls < nsteps ? ls : ls - nsteps;
+    const int64_t it = ls / kTaps, tap = ls - it * kTaps;
     const int64_t kd = it / nchunk, cc = it - kd * nchunk;
     const int64_t koff = (kd * kTaps + tap) * C + cc * 64;
 #pragma unroll
     for (int j = 0; j < kBLoads; ++j) {
-      const gvec_ptr src = brow[j] ? gvec(brow[j] + koff) : zero;
+      const gvec_ptr src = (real && brow[j]) ? gvec(brow[j] + koff) : zero;
       __builtin_amdgcn_global_load_lds(src, lds_addr(dst + j * 1024), 16, 0, 0);
     }
   };
-  // Patch slots [j0, j0 + cnt) of iteration it into buffer it & 1 (past the
-  // end the data wraps around; the buffer follows the unwrapped it).
-  auto issue_patch = [&](int64_t it, int j0, int cnt) {
-    const uint32_t dst = patch_lds + uint32_t(it & 1) * kPatchBytes;
-    it = it < nit ? it : it - nit;
+  // Patch slots [j0, j0 + cnt) of iteration it of tile pg into the buffer of
+  // global iteration gi (`real` false: a zero vector).
+  auto issue_patch = [&](int64_t it, int64_t gi, bool real, int j0, int cnt) {
+    const uint32_t dst = patch_lds + uint32_t(gi & 1) * kPatchBytes;
     const int64_t kd = it / nchunk, cc = it - kd * nchunk;
     int64_t base = 0;
-    bool fok = true;
+    bool fok = real;
     if constexpr (D3) {
-      const int64_t id = od * p.sd - p.pd + kd * p.dd;
-      fok = id >= 0 && id < D;
-      base = (img * D + (fok ? id : 0)) * H * W * C;
+      const int64_t id = int64_t(pg.od) * p.sd - p.pd + kd * p.dd;
+      fok = fok && id >= 0 && id < D;
+      base = (int64_t(pg.img) * D + (fok ? id : 0)) * H * W * C;
     } else {
-      base = f * H * W * C;
+      base = int64_t(pg.f) * H * W * C;
     }
     const uint16_t* xf = X + base + cc * 64;
 #pragma unroll
@@ -268,12 +301,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_patch_kernel(const GemmParam
   };
 
   v16f acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
   auto mma = [&](const Frag& fr) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -288,11 +315,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_patch_kernel(const GemmParam
     }
   };
 
-  // ---- prologue: iteration 0's patch, the weights of steps 0 and 1; wait for
-  // the first two everywhere.
-  issue_patch(0, 0, kPatchLoads);
-  issue_w(0);
-  issue_w(1);
+  // ---- prologue: the first tile's first patch and the weights of its steps
+  // 0 and 1; wait for the first two everywhere.
+  TileGeo cur = tile_geo(0);
+  set_patch_tile(cur);
+  set_weight_tile(cur.n0);
+  issue_patch(0, 0, true, 0, kPatchLoads);
+  issue_w(0, 0, true);
+  issue_w(1, 1, true);
   wait_vmcnt<kBLoads>();
   block_barrier();
   __builtin_amdgcn_sched_barrier(0);
@@ -301,15 +331,17 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_patch_kernel(const GemmParam
   for (int i = 0; i < 4; ++i) pbl[i] = pb[i];
   read(0, 0, 0, 0, f0);
 
-  // One tap of iteration it (global step g = 9 it + T): its four 16-channel
-  // MFMA steps; before the last, wait until step g + 1's weights (and, at the
-  // end of an iteration, the next patch) have landed everywhere, then load
-  // step g + 2's weights into the stage just read and a slice of the next
-  // iteration's patch, and read step g + 1's first fragments.
-  auto tap_step = [&](auto tap_c, int64_t it) {
+  // One tap of local iteration it (global iteration gi, global step g = 9 gi
+  // + T): its four 16-channel MFMA steps; before the last, wait until step g
+  // + 1's weights (and, at the end of an iteration, the next patch) have
+  // landed everywhere, then load step g + 2's weights into the stage just
+  // read and a slice of the next iteration's patch, and read step g + 1's
+  // first fragments.  In the tile's last iteration the loads are the next
+  // tile's (nx: it exists), and from tap 7 on its weights.
+  auto tap_step = [&](auto tap_c, int64_t it, int64_t gi, bool last, bool nx, const TileGeo& ng) {
     constexpr int T = decltype(tap_c)::value;
-    const int64_t g = it * kTaps + T;
-    const int buf = int(it & 1), ws = int(g & 1);
+    const int64_t g = gi * kTaps + T;
+    const int buf = int(gi & 1), ws = int(g & 1);
     read(buf, ws, T, 1, f1);
     mma(f0);
     interleave();
@@ -326,8 +358,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_patch_kernel(const GemmParam
     wait_vmcnt_lds<(T == 0 ? 0 : kSlice[T == 0 ? 0 : T - 1])>();
     block_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    issue_w(g + 2);
-    if constexpr (kSlice[T] > 0) issue_patch(it + 1, kSliceStart[T], kSlice[T]);
+    if constexpr (T == 7) {
+      if (last && nx) set_weight_tile(ng.n0);
+    }
+    const int64_t ls = it * kTaps + T + 2;
+    issue_w(ls, g + 2, ls < nsteps || nx);
+    if constexpr (kSlice[T] > 0) issue_patch(last ? 0 : it + 1, gi + 1, !last || nx, kSliceStart[T], kSlice[T]);
     constexpr int TN = (T + 1) % kTaps;
     read(T + 1 == kTaps ? (buf ^ 1) : buf, ws ^ 1, TN, 0, f0);
     mma(f1);
@@ -344,102 +380,136 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_patch_kernel(const GemmParam
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the next step's first reads are done
   };
-  for (int64_t it = 0; it < nit; ++it) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      pbl[i] = pb[i];
-      asm volatile("" : "+v"(pbl[i]));
-    }
-    tap_step(ic<0>{}, it);
-    tap_step(ic<1>{}, it);
-    tap_step(ic<2>{}, it);
-    tap_step(ic<3>{}, it);
-    tap_step(ic<4>{}, it);
-    tap_step(ic<5>{}, it);
-    tap_step(ic<6>{}, it);
-    tap_step(ic<7>{}, it);
-    tap_step(ic<8>{}, it);
-  }
-  wait_vmcnt<0>();  // the trailing loads must land before LDS is reused
 
-  // ---- epilogue through LDS, one 32-row slice of the wavefront's quadrant at
-  // a time (layout as in gemm_lds.hip): D[row][col] of a 32x32 block sits in
-  // lane l, register r at row = 8 (r / 4) + 4 (l / 32) + r % 4, col = l % 32.
-  block_barrier();  // every wavefront has finished its LDS reads
-  constexpr int WN = 128, EP = WN + 4;
-  float* ep = reinterpret_cast<float*>(g_patch + wave * (32 * EP * 4));
-  static_assert(4 * 32 * EP * 4 <= 2 * kPatchBytes, "the epilogue slices fit the patch buffers");
   uint16_t* __restrict__ out = reinterpret_cast<uint16_t*>(p.out);
   float* __restrict__ accbuf = p.acc;
   const int epi = p.epi;
   const bool vec = (p.ldc % 8) == 0 && (reinterpret_cast<uintptr_t>(out) & 15) == 0 &&
                    (accbuf == nullptr || (reinterpret_cast<uintptr_t>(accbuf) & 15) == 0);
-  constexpr int LPR = WN / 8, RPG = 64 / LPR;
-  const int rl = lane / LPR, cl = (lane % LPR) * 8;
+  int64_t gi = 0;  // global iteration: patch buffer gi & 1
+  for (int32_t jt = 0;; ++jt) {
+    const bool nx = jt + 1 < my_tiles;
+    const TileGeo ng = nx ? tile_geo(jt + 1) : cur;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+      for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        ep[(8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * EP + 32 * j + (lane & 31)] = acc[i][j][r];
-    for (int g = 0; g < 32 / RPG; ++g) {
-      const int rr = g * RPG + rl;
-      const int trow = wm * 128 + i * 32 + rr;  // row of the tile: pixel (trow / BW, trow % BW)
-      const int64_t oh = oh0 + trow / BW, ow = ow0 + trow % BW;
-      const int64_t col = n0 + wn * WN + cl;
-      const float4 lo = *reinterpret_cast<const float4*>(ep + rr * EP + cl);
-      const float4 hi = *reinterpret_cast<const float4*>(ep + rr * EP + cl + 4);
-      float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-      if (oh >= OH || ow >= OW || col >= N) continue;
-      const int64_t idx = ((f * OH + oh) * OW + ow) * p.ldc + col;
-      if (vec && col + 8 <= N) {
-        if (epi == kEpiAccFirst || epi == kEpiAccMid) {
-          float4* dst = reinterpret_cast<float4*>(accbuf + idx);
-          if (epi == kEpiAccMid) {
-            const float4 a0 = dst[0], a1 = dst[1];
-            v[0] += a0.x; v[1] += a0.y; v[2] += a0.z; v[3] += a0.w;
-            v[4] += a1.x; v[5] += a1.y; v[6] += a1.z; v[7] += a1.w;
-          }
-          dst[0] = make_float4(v[0], v[1], v[2], v[3]);
-          dst[1] = make_float4(v[4], v[5], v[6], v[7]);
-        } else {
-          if (epi == kEpiAccLast) {
-            const float4* src = reinterpret_cast<const float4*>(accbuf + idx);
-            const float4 a0 = src[0], a1 = src[1];
-            v[0] = a0.x + v[0]; v[1] = a0.y + v[1]; v[2] = a0.z + v[2]; v[3] = a0.w + v[3];
-            v[4] = a1.x + v[4]; v[5] = a1.y + v[5]; v[6] = a1.z + v[6]; v[7] = a1.w + v[7];
-          }
-          uint4 o;
-          o.x = uint32_t(from_f32<uint16_t, BF16>(v[0])) | (uint32_t(from_f32<uint16_t, BF16>(v[1])) << 16);
-          o.y = uint32_t(from_f32<uint16_t, BF16>(v[2])) | (uint32_t(from_f32<uint16_t, BF16>(v[3])) << 16);
-          o.z = uint32_t(from_f32<uint16_t, BF16>(v[4])) | (uint32_t(from_f32<uint16_t, BF16>(v[5])) << 16);
-          o.w = uint32_t(from_f32<uint16_t, BF16>(v[6])) | (uint32_t(from_f32<uint16_t, BF16>(v[7])) << 16);
-          *reinterpret_cast<uint4*>(out + idx) = o;
-        }
-      } else {
-        for (int q = 0; q < 8 && col + q < N; ++q) {
-          const float x = v[q];
-          if (epi == kEpiStore) {
-            out[idx + q] = from_f32<uint16_t, BF16>(x);
-          } else if (epi == kEpiAccFirst) {
-            accbuf[idx + q] = x;
-          } else if (epi == kEpiAccMid) {
-            accbuf[idx + q] = accbuf[idx + q] + x;
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+    for (int64_t it = 0; it < nit; ++it, ++gi) {
+      const bool last = it + 1 == nit;
+      if (last && nx) set_patch_tile(ng);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pbl[i] = pb[i];
+        asm volatile("" : "+v"(pbl[i]));
+      }
+      tap_step(ic<0>{}, it, gi, last, nx, ng);
+      tap_step(ic<1>{}, it, gi, last, nx, ng);
+      tap_step(ic<2>{}, it, gi, last, nx, ng);
+      tap_step(ic<3>{}, it, gi, last, nx, ng);
+      tap_step(ic<4>{}, it, gi, last, nx, ng);
+      tap_step(ic<5>{}, it, gi, last, nx, ng);
+      tap_step(ic<6>{}, it, gi, last, nx, ng);
+      tap_step(ic<7>{}, it, gi, last, nx, ng);
+      tap_step(ic<8>{}, it, gi, last, nx, ng);
+    }
+
+    // ---- epilogue through LDS, 16 rows of the wavefront's quadrant at a
+    // time, staged in the patch buffer of the tile's last iteration (every
+    // wavefront passed the barrier after its last read of it; the next tile's
+    // patch is in the other buffer).  D[row][col] of a 32x32 block sits in
+    // lane l, register r at row = 8 (r / 4) + 4 (l / 32) + r % 4, col = l %
+    // 32, so registers 8 h .. 8 h + 7 hold rows 16 h .. 16 h + 15.
+    constexpr int WN = 128, EP = WN + 8;  // 4 rows apart = 32 banks apart: conflict-free writes
+    float* ep = reinterpret_cast<float*>(g_patch + int((gi - 1) & 1) * kPatchBytes + wave * (16 * EP * 4));
+    static_assert(4 * 16 * EP * 4 <= kPatchBytes, "the epilogue slices fit one patch buffer");
+    constexpr int LPR = WN / 8, RPG = 64 / LPR;
+    const int rl = lane / LPR, cl = (lane % LPR) * 8;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int r = 8 * hh; r < 8 * hh + 8; ++r)
+            ep[(8 * ((r >> 2) & 1) + 4 * (lane >> 5) + (r & 3)) * EP + 32 * j + (lane & 31)] = acc[i][j][r];
+        for (int gq = 0; gq < 16 / RPG; ++gq) {
+          const int rr = gq * RPG + rl;
+          const int trow = wm * 128 + i * 32 + 16 * hh + rr;  // row of the tile: pixel (trow / BW, trow % BW)
+          const int64_t oh = cur.oh0 + trow / BW, ow = cur.ow0 + trow % BW;
+          const int64_t col = int64_t(cur.n0) + wn * WN + cl;
+          const float4 lo = *reinterpret_cast<const float4*>(ep + rr * EP + cl);
+          const float4 hi = *reinterpret_cast<const float4*>(ep + rr * EP + cl + 4);
+          float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+          if (oh >= OH || ow >= OW || col >= N) continue;
+          const int64_t idx = ((int64_t(cur.f) * OH + oh) * OW + ow) * p.ldc + col;
+          if (vec && col + 8 <= N) {
+            if (epi == kEpiAccFirst || epi == kEpiAccMid) {
+              float4* dst = reinterpret_cast<float4*>(accbuf + idx);
+              if (epi == kEpiAccMid) {
+                const float4 a0 = dst[0], a1 = dst[1];
+                v[0] += a0.x; v[1] += a0.y; v[2] += a0.z; v[3] += a0.w;
+                v[4] += a1.x; v[5] += a1.y; v[6] += a1.z; v[7] += a1.w;
+              }
+              dst[0] = make_float4(v[0], v[1], v[2], v[3]);
+              dst[1] = make_float4(v[4], v[5], v[6], v[7]);
+            } else {
+              if (epi == kEpiAccLast) {
+                const float4* src = reinterpret_cast<const float4*>(accbuf + idx);
+                const float4 a0 = src[0], a1 = src[1];
+                v[0] = a0.x + v[0]; v[1] = a0.y + v[1]; v[2] = a0.z + v[2]; v[3] = a0.w + v[3];
+                v[4] = a1.x + v[4]; v[5] = a1.y + v[5]; v[6] = a1.z + v[6]; v[7] = a1.w + v[7];
+              }
+              uint4 o;
+              o.x = uint32_t(from_f32<uint16_t, BF16>(v[0])) | (uint32_t(from_f32<uint16_t, BF16>(v[1])) << 16);
+              o.y = uint32_t(from_f32<uint16_t, BF16>(v[2])) | (uint32_t(from_f32<uint16_t, BF16>(v[3])) << 16);
+              o.z = uint32_t(from_f32<uint16_t, BF16>(v[4])) | (uint32_t(from_f32<uint16_t, BF16>(v[5])) << 16);
+              o.w = uint32_t(from_f32<uint16_t, BF16>(v[6])) | (uint32_t(from_f32<uint16_t, BF16>(v[7])) << 16);
+              *reinterpret_cast<uint4*>(out + idx) = o;
+            }
           } else {
-            out[idx + q] = from_f32<uint16_t, BF16>(accbuf[idx + q] + x);
+            for (int q = 0; q < 8 && col + q < N; ++q) {
+              const float x = v[q];
+              if (epi == kEpiStore) {
+                out[idx + q] = from_f32<uint16_t, BF16>(x);
+              } else if (epi == kEpiAccFirst) {
+                accbuf[idx + q] = x;
+              } else if (epi == kEpiAccMid) {
+                accbuf[idx + q] = accbuf[idx + q] + x;
+              } else {
+                out[idx + q] = from_f32<uint16_t, BF16>(accbuf[idx + q] + x);
+              }
+            }
           }
         }
       }
     }
+    if (!nx) break;
+    cur = ng;
   }
+  wait_vmcnt<0>();  // the trailing zero loads land before the workgroup ends
+}
+
+// Compute units of the current device (one persistent workgroup each).
+int cu_count() {
+  static std::atomic<int> cache[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n > 0) return n;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+  cache[dev].store(n, std::memory_order_relaxed);
+  return n;
 }
 
 template <bool BF16, bool D3>
 hipError_t launch_bw(const GemmParams& p, hipStream_t s) {
   const int bw = int(patch_block_w(p.oh, p.ow));
   const int64_t tiles = patch_row_tiles(p.M / (p.oh * p.ow), p.oh, p.ow) * ((p.N + kBN - 1) / kBN);
-  const dim3 grid{unsigned(tiles), 1u, 1u};
+  const int64_t wgs = tiles < cu_count() ? tiles : cu_count();
+  const dim3 grid{unsigned(wgs), 1u, 1u};
   if (bw == 8) hipLaunchKernelGGL((gemm_patch_kernel<BF16, D3, 8>), grid, dim3(kThreads), 0, s, p);
   else if (bw == 32) hipLaunchKernelGGL((gemm_patch_kernel<BF16, D3, 32>), grid, dim3(kThreads), 0, s, p);
   else hipLaunchKernelGGL((gemm_patch_kernel<BF16, D3, 16>), grid, dim3(kThreads), 0, s, p);

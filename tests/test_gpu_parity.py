@@ -366,6 +366,72 @@ def test_patch_tile_accumulating_epilogue(dtype):
     assert torch.equal(bits(y3[0]), bits(y2))
 
 
+# More tiles than compute units: each persistent workgroup of config 16 runs
+# several tiles, loading the next tile's patch and first weight stages during
+# its current tile's last (depth tap, chunk) iteration.  One iteration per
+# tile (C = 64, KD = 1), odd iteration counts, two column tiles, ragged
+# blocks, 3D depth taps and the accumulating epilogues; a seeded sample of
+# output pixels (with every pixel of the first and last blocks) against the
+# oracle, every output written (the buffer starts as NaN) and the same bits
+# on every run.
+PERSIST_CASES = [  # name, n, d, h, w, c, o, kd, pad, dtype, algo
+    ("c64_nit1", 70, 1, 32, 32, 64, 96, 0, (1, 1), "f16", "implicit_gemm"),
+    ("c192_o300_ragged", 24, 1, 33, 35, 192, 300, 0, (1, 1), "bf16", "implicit_gemm"),
+    ("video_kd3", 1, 20, 64, 64, 128, 64, 3, (0, 1, 1), "bf16", "implicit_gemm"),
+    ("small_kd_acc", 1, 19, 64, 64, 64, 72, 3, (0, 1, 1), "f16", "small_kd"),
+]
+
+
+@pytest.mark.parametrize("spec", PERSIST_CASES, ids=[c[0] for c in PERSIST_CASES])
+def test_patch_tile_persistent(spec):
+    name, n, d, h, w, c, o, kd, pad, dt, algo = spec
+    nd = 3 if kd else 2
+    stride, dil = (1,) * nd, (1,) * nd
+    case = cw.ConvCase(f"persist_{name}", n, h, w, c, o, 3, 3, stride, pad, dil, dt, "normal", "normal", None, 37,
+                       len(name) + c, nd=nd, d=d if kd else 1, kd=kd or 1)
+    x, wt = case.input(), case.weight()
+    kw = dict(algo=algo, gemm_config=16)
+    if algo == "small_kd":
+        kw["inner_algo"] = "implicit_gemm"
+    plan = (cn.plan3d if nd == 3 else cn.plan2d)(case.x_shape(), case.w_shape(), **case.conv_kwargs(),
+                                                 dtype=x.dtype, **kw)
+    assert plan.kernel_config == 16
+    per = plan.out_h * plan.out_w
+    frames = n * (plan.out_d if nd == 3 else 1)
+    assert _patch_tiles(frames, plan.out_h, plan.out_w) * -(-o // 256) > 256, "more tiles than CUs"
+    fn = cn.conv3d if nd == 3 else cn.conv2d
+    y = fn(_dev(x), _dev(wt), **case.conv_kwargs(), plan=plan, out=poisoned(plan_out_shape(plan, case), x.dtype))
+    torch.cuda.synchronize()
+    assert not torch.isnan(y).any(), "every output is written"
+    total = frames * per
+    rows = set(cw.sample_rows(total, 1500, 37).tolist())
+    rows.update(range(0, 2 * plan.out_w))
+    rows.update(range(total - 2 * plan.out_w, total))
+    rows = np.array(sorted(rows), dtype=np.int64)
+    yr, den = oracle.conv(to_oracle(x), to_oracle(wt), **case.conv_kwargs(), rows=rows)
+    check_parity(gather_rows(y, rows), yr, den, x.dtype, case.name)
+    y2 = fn(_dev(x), _dev(wt), **case.conv_kwargs(), plan=plan)
+    assert torch.equal(bits(y), bits(y2)), f"{case.name}: run-to-run bits differ"
+
+
+def _patch_tiles(frames, oh, ow):
+    """Row tiles of config 16: blocks of the least padded width among 16, 32, 8."""
+    best = None
+    for bw in (16, 32, 8):
+        bh = 256 // bw
+        area = -(-oh // bh) * bh * -(-ow // bw) * bw
+        if best is None or area < best[0]:
+            best = (area, bw, bh)
+    _, bw, bh = best
+    return frames * -(-oh // bh) * -(-ow // bw)
+
+
+def plan_out_shape(plan, case):
+    if case.nd == 3:
+        return (case.n, plan.out_d, plan.out_h, plan.out_w, case.o)
+    return (case.n, plan.out_h, plan.out_w, case.o)
+
+
 # ---------------------------------------------------------------- split K
 # Small-grid GEMMs split K; the partial sums are added in a fixed order by a
 # second kernel.  Forced splits (including a short last split) on every dtype
