@@ -275,12 +275,17 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_patch_kernel(const GemmParam
     const int r = wm * 128 + i * 32 + frow;
     pb[i] = (r / BW) * PW + (r % BW);
   }
+  // B: block j's lane l supplies weight row wn*128 + 32 j + perm(l & 31), perm
+  // swapping bits 2 and 3 (a permutation within each 16 rows, so the reads
+  // stay conflict-free); with the operands swapped in the MFMA (below) each
+  // lane's accumulators then hold 8 consecutive output channels of one pixel.
+  const int brow_l = (frow & 0x13) | ((frow & 4) << 1) | ((frow & 8) >> 1);
   uint32_t rb_off[4][4];
 #pragma unroll
   for (int s = 0; s < 4; ++s)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int r = wn * 128 + j * 32 + frow;
+      const int r = wn * 128 + j * 32 + brow_l;
       rb_off[s][j] = uint32_t(r * kRowB + (((2 * s + khalf) ^ swz(r)) << 4));
       asm volatile("" : "+v"(rb_off[s][j]));
     }
@@ -305,7 +310,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_patch_kernel(const GemmParam
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = mfma_32x32x16<BF16>(fr.a[i], fr.b[j], acc[i][j]);
+      for (int j = 0; j < 4; ++j) acc[i][j] = mfma_32x32x16<BF16>(fr.b[j], fr.a[i], acc[i][j]);
   };
   auto interleave = [&]() {  // 16 MFMAs with the 8 fragment reads of the next step between them
 #pragma unroll
@@ -415,77 +420,94 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_patch_kernel(const GemmParam
       tap_step(ic<8>{}, it, gi, last, nx, ng);
     }
 
-    // ---- epilogue through LDS, 16 rows of the wavefront's quadrant at a
-    // time, staged in the patch buffer of the tile's last iteration (every
-    // wavefront passed the barrier after its last read of it; the next tile's
-    // patch is in the other buffer).  D[row][col] of a 32x32 block sits in
-    // lane l, register r at row = 8 (r / 4) + 4 (l / 32) + r % 4, col = l %
-    // 32, so registers 8 h .. 8 h + 7 hold rows 16 h .. 16 h + 15.
-    constexpr int WN = 128, EP = WN + 8;  // 4 rows apart = 32 banks apart: conflict-free writes
-    float* ep = reinterpret_cast<float*>(g_patch + int((gi - 1) & 1) * kPatchBytes + wave * (16 * EP * 4));
-    static_assert(4 * 16 * EP * 4 <= kPatchBytes, "the epilogue slices fit one patch buffer");
-    constexpr int LPR = WN / 8, RPG = 64 / LPR;
-    const int rl = lane / LPR, cl = (lane % LPR) * 8;
+    // ---- epilogue through LDS, in the patch buffer of the tile's last
+    // iteration (every wavefront passed the barrier after its last read of
+    // it; the next tile's patch is in the other buffer).  acc[i][j] is the
+    // transposed 32x32 block (output channels x pixels): lane l, register r
+    // holds output channel 32 j + 16 (r / 8) + 8 (l / 32) + r % 8 of pixel
+    // 32 i + l % 32 of the wavefront's quadrant (the B row permutation above),
+    // so four consecutive registers are four consecutive channels of one
+    // pixel and go to LDS in one 16-byte write.  Rounds of 32 pixels x 64
+    // channels; each pixel row is then read back 8 channels per lane and
+    // stored in whole lines.
+    int el = lane;  // opaque copy: the address arithmetic stays inside the tile loop
+    asm volatile("" : "+v"(el));
+    const int h8 = 8 * (el >> 5), erow = el & 31;
+    constexpr int kEpRowB = 64 * 4 + 16;  // 64 fp32 + 16 B: 16 consecutive rows hit 16 bank groups
+    static_assert(4 * 32 * kEpRowB <= kPatchBytes, "the epilogue rows fit one patch buffer");
+    float* e32 = reinterpret_cast<float*>(g_patch + int((gi - 1) & 1) * kPatchBytes + wave * (32 * kEpRowB));
+    const int rl = el >> 3, cl = (el & 7) * 8;
+    auto round = [&](auto i_c, auto jp_c) {  // compile-time indices into acc
+      constexpr int i = decltype(i_c)::value, jp = decltype(jp_c)::value;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+      for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
+        for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-#pragma unroll
-          for (int r = 8 * hh; r < 8 * hh + 8; ++r)
-            ep[(8 * ((r >> 2) & 1) + 4 * (lane >> 5) + (r & 3)) * EP + 32 * j + (lane & 31)] = acc[i][j][r];
-        for (int gq = 0; gq < 16 / RPG; ++gq) {
-          const int rr = gq * RPG + rl;
-          const int trow = wm * 128 + i * 32 + 16 * hh + rr;  // row of the tile: pixel (trow / BW, trow % BW)
-          const int64_t oh = cur.oh0 + trow / BW, ow = cur.ow0 + trow % BW;
-          const int64_t col = int64_t(cur.n0) + wn * WN + cl;
-          const float4 lo = *reinterpret_cast<const float4*>(ep + rr * EP + cl);
-          const float4 hi = *reinterpret_cast<const float4*>(ep + rr * EP + cl + 4);
-          float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-          if (oh >= OH || ow >= OW || col >= N) continue;
-          const int64_t idx = ((int64_t(cur.f) * OH + oh) * OW + ow) * p.ldc + col;
-          if (vec && col + 8 <= N) {
-            if (epi == kEpiAccFirst || epi == kEpiAccMid) {
-              float4* dst = reinterpret_cast<float4*>(accbuf + idx);
-              if (epi == kEpiAccMid) {
-                const float4 a0 = dst[0], a1 = dst[1];
-                v[0] += a0.x; v[1] += a0.y; v[2] += a0.z; v[3] += a0.w;
-                v[4] += a1.x; v[5] += a1.y; v[6] += a1.z; v[7] += a1.w;
-              }
-              dst[0] = make_float4(v[0], v[1], v[2], v[3]);
-              dst[1] = make_float4(v[4], v[5], v[6], v[7]);
-            } else {
-              if (epi == kEpiAccLast) {
-                const float4* src = reinterpret_cast<const float4*>(accbuf + idx);
-                const float4 a0 = src[0], a1 = src[1];
-                v[0] = a0.x + v[0]; v[1] = a0.y + v[1]; v[2] = a0.z + v[2]; v[3] = a0.w + v[3];
-                v[4] = a1.x + v[4]; v[5] = a1.y + v[5]; v[6] = a1.z + v[6]; v[7] = a1.w + v[7];
-              }
-              uint4 o;
-              o.x = uint32_t(from_f32<uint16_t, BF16>(v[0])) | (uint32_t(from_f32<uint16_t, BF16>(v[1])) << 16);
-              o.y = uint32_t(from_f32<uint16_t, BF16>(v[2])) | (uint32_t(from_f32<uint16_t, BF16>(v[3])) << 16);
-              o.z = uint32_t(from_f32<uint16_t, BF16>(v[4])) | (uint32_t(from_f32<uint16_t, BF16>(v[5])) << 16);
-              o.w = uint32_t(from_f32<uint16_t, BF16>(v[6])) | (uint32_t(from_f32<uint16_t, BF16>(v[7])) << 16);
-              *reinterpret_cast<uint4*>(out + idx) = o;
+          for (int qq = 0; qq < 2; ++qq) {
+            const v16f& a = acc[i][2 * jp + jj];
+            const int r0 = 8 * hh + 4 * qq;
+            *reinterpret_cast<float4*>(e32 + erow * (kEpRowB / 4) + 32 * jj + 16 * hh + h8 + 4 * qq) =
+                make_float4(a[r0], a[r0 + 1], a[r0 + 2], a[r0 + 3]);
+          }
+      for (int gq = 0; gq < 4; ++gq) {
+        const int rr = gq * 8 + rl;
+        const float4 lo = *reinterpret_cast<const float4*>(e32 + rr * (kEpRowB / 4) + cl);
+        const float4 hi = *reinterpret_cast<const float4*>(e32 + rr * (kEpRowB / 4) + cl + 4);
+        float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+        const int trow = wm * 128 + i * 32 + rr;  // row of the tile: pixel (trow / BW, trow % BW)
+        const int64_t oh = cur.oh0 + trow / BW, ow = cur.ow0 + trow % BW;
+        const int64_t col = int64_t(cur.n0) + wn * 128 + 64 * jp + cl;
+        if (oh >= OH || ow >= OW || col >= N) continue;
+        const int64_t idx = ((int64_t(cur.f) * OH + oh) * OW + ow) * p.ldc + col;
+        if (vec && col + 8 <= N) {
+          if (epi == kEpiAccFirst || epi == kEpiAccMid) {
+            float4* dst = reinterpret_cast<float4*>(accbuf + idx);
+            if (epi == kEpiAccMid) {
+              const float4 a0 = dst[0], a1 = dst[1];
+              v[0] += a0.x; v[1] += a0.y; v[2] += a0.z; v[3] += a0.w;
+              v[4] += a1.x; v[5] += a1.y; v[6] += a1.z; v[7] += a1.w;
             }
+            dst[0] = make_float4(v[0], v[1], v[2], v[3]);
+            dst[1] = make_float4(v[4], v[5], v[6], v[7]);
           } else {
-            for (int q = 0; q < 8 && col + q < N; ++q) {
-              const float x = v[q];
-              if (epi == kEpiStore) {
-                out[idx + q] = from_f32<uint16_t, BF16>(x);
-              } else if (epi == kEpiAccFirst) {
-                accbuf[idx + q] = x;
-              } else if (epi == kEpiAccMid) {
-                accbuf[idx + q] = accbuf[idx + q] + x;
-              } else {
-                out[idx + q] = from_f32<uint16_t, BF16>(accbuf[idx + q] + x);
-              }
+            if (epi == kEpiAccLast) {
+              const float4* src = reinterpret_cast<const float4*>(accbuf + idx);
+              const float4 a0 = src[0], a1 = src[1];
+              v[0] = a0.x + v[0]; v[1] = a0.y + v[1]; v[2] = a0.z + v[2]; v[3] = a0.w + v[3];
+              v[4] = a1.x + v[4]; v[5] = a1.y + v[5]; v[6] = a1.z + v[6]; v[7] = a1.w + v[7];
+            }
+            uint4 o;
+            o.x = uint32_t(from_f32<uint16_t, BF16>(v[0])) | (uint32_t(from_f32<uint16_t, BF16>(v[1])) << 16);
+            o.y = uint32_t(from_f32<uint16_t, BF16>(v[2])) | (uint32_t(from_f32<uint16_t, BF16>(v[3])) << 16);
+            o.z = uint32_t(from_f32<uint16_t, BF16>(v[4])) | (uint32_t(from_f32<uint16_t, BF16>(v[5])) << 16);
+            o.w = uint32_t(from_f32<uint16_t, BF16>(v[6])) | (uint32_t(from_f32<uint16_t, BF16>(v[7])) << 16);
+            *reinterpret_cast<uint4*>(out + idx) = o;
+          }
+        } else {
+          for (int q = 0; q < 8 && col + q < N; ++q) {
+            const float x = v[q];
+            if (epi == kEpiStore) {
+              out[idx + q] = from_f32<uint16_t, BF16>(x);
+            } else if (epi == kEpiAccFirst) {
+              accbuf[idx + q] = x;
+            } else if (epi == kEpiAccMid) {
+              accbuf[idx + q] = accbuf[idx + q] + x;
+            } else {
+              out[idx + q] = from_f32<uint16_t, BF16>(accbuf[idx + q] + x);
             }
           }
         }
       }
-    }
+    };
+    round(ic<0>{}, ic<0>{});
+    round(ic<0>{}, ic<1>{});
+    round(ic<1>{}, ic<0>{});
+    round(ic<1>{}, ic<1>{});
+    round(ic<2>{}, ic<0>{});
+    round(ic<2>{}, ic<1>{});
+    round(ic<3>{}, ic<0>{});
+    round(ic<3>{}, ic<1>{});
     if (!nx) break;
     cur = ng;
   }
