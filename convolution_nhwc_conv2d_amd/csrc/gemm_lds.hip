@@ -257,8 +257,9 @@ __global__ __launch_bounds__(kThreads, T::OCC) void gemm_lds_kernel(const GemmPa
     b_off[j] = n < N ? n * p.ldb + kin_of(rt) : -1;
   }
 
-  // ---- K position of the next chunk to issue (implicit: C % 32 == 0, so a
-  // chunk never straddles two taps and its tap is wave-uniform).  Chunks past
+  // ---- K position of the next chunk to issue (implicit: C is a multiple of
+  // the chunk, 32 or 64 elements, so a chunk never straddles two taps and its
+  // tap is wave-uniform).  Chunks past
   // the end are issued too (dense: as zero loads), so every wait count is
   // fixed.
   int64_t k_next = 0;
@@ -331,7 +332,8 @@ __global__ __launch_bounds__(kThreads, T::OCC) void gemm_lds_kernel(const GemmPa
 
   // ---- fragment reads: lane's A rows wm*128 + 32 i + (lane & 31), B rows
   // wn*128 + 32 j + (lane & 31), logical piece 2 q + (lane >> 5), physical
-  // piece that ^ ((row >> 1) & 3) (the same for all four 32-row groups).
+  // piece piece<kPieces>(row, that) (it depends on the row modulo 16 only, so
+  // it is the same for all four 32-row groups).
   // Each read is addressed as ring + (offset + stage base) with the offsets
   // precomputed and kept opaque, so the compiler sees every fragment read as a
   // read of its ring object (and tags it so).
