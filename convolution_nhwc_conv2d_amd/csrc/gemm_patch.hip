@@ -37,9 +37,14 @@
 // destination is fixed by its lane index, so the swizzle is applied on the
 // global side.
 //
-// MFMA: v_mfma_f32_32x32x16_{f16,bf16}; in 16-channel step s of a chunk,
-// lanes 0..31 supply channels 16 s + 0..7 and lanes 32..63 16 s + 8..15 of
-// their row.
+// MFMA: v_mfma_f32_32x32x16_{f16,bf16} with the weight fragment as the first
+// operand, so each accumulator block is the transposed (channels x pixels)
+// 32x32 block; in 16-channel step s of a chunk, lanes 0..31 supply channels
+// 16 s + 0..7 and lanes 32..63 16 s + 8..15 of their row.
+//
+// Workgroups are persistent (at most one per CU, each walking a list of
+// tiles, see the kernel), and each tile's results leave through LDS in
+// whole-line stores.
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -482,7 +487,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_patch_kernel(const GemmParam
             o.y = uint32_t(from_f32<uint16_t, BF16>(v[2])) | (uint32_t(from_f32<uint16_t, BF16>(v[3])) << 16);
             o.z = uint32_t(from_f32<uint16_t, BF16>(v[4])) | (uint32_t(from_f32<uint16_t, BF16>(v[5])) << 16);
             o.w = uint32_t(from_f32<uint16_t, BF16>(v[6])) | (uint32_t(from_f32<uint16_t, BF16>(v[7])) << 16);
-            *reinterpret_cast<uint4*>(out + idx) = o;
+            const u32x4 ov = {o.x, o.y, o.z, o.w};  // written once: stored past L2
+            __builtin_nontemporal_store(ov, reinterpret_cast<u32x4*>(out + idx));
           }
         } else {
           for (int q = 0; q < 8 && col + q < N; ++q) {
