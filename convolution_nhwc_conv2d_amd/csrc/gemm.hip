@@ -28,6 +28,8 @@
 // on the launch a row is in, or on the grid.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "internal.hpp"
 #include "device_common.hpp"
 
@@ -441,26 +443,75 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_kernel(const GemmParams p) {
 }
 
 // y (or the fp32 accumulator) from the K-split partial slices: the slices are
-// added in order 0, 1, ..., ksplit-1, then the epilogue of p is applied.
-template <typename E, bool BF16>
+// added in order 0, 1, ..., ksplit-1, then the epilogue of p is applied.  Each
+// thread takes V consecutive columns of one row (V = 4: 16-byte slice loads;
+// V divides N); NARROW: the thread index fits 32 bits, so the row and column
+// come from 32-bit arithmetic.
+template <typename E, bool BF16, int V, bool NARROW>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const GemmParams p) {
-  const int64_t t = int64_t(blockIdx.x) * 256 + threadIdx.x;
-  if (t >= p.M * p.N) return;
-  const int64_t row = t / p.N, col = t - row * p.N;
-  const int64_t idx = row * p.ldc + col;
+  using I = typename std::conditional<NARROW, uint32_t, uint64_t>::type;
+  const I nv = I(p.N / V);
+  const I t = I(blockIdx.x) * 256 + threadIdx.x;
+  if (t >= I(p.M) * nv) return;
+  const I row = t / nv;
+  const int64_t col = int64_t(t - row * nv) * V;
+  const int64_t idx = int64_t(row) * p.ldc + col;
   const int64_t slice = p.M * p.ldc;
-  float v = p.part[idx];
-  for (int s = 1; s < p.ksplit; ++s) v += p.part[s * slice + idx];
-  E* __restrict__ out = reinterpret_cast<E*>(p.out);
-  if (p.epi == kEpiStore) {
-    out[idx] = from_f32<E, BF16>(v);
-  } else if (p.epi == kEpiAccFirst) {
-    p.acc[idx] = v;
-  } else if (p.epi == kEpiAccMid) {
-    p.acc[idx] = p.acc[idx] + v;
+  float v[V];
+  if constexpr (V == 4) {
+    const float4 a = *reinterpret_cast<const float4*>(p.part + idx);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    for (int s = 1; s < p.ksplit; ++s) {
+      const float4 b = *reinterpret_cast<const float4*>(p.part + s * slice + idx);
+      v[0] += b.x; v[1] += b.y; v[2] += b.z; v[3] += b.w;
+    }
   } else {
-    out[idx] = from_f32<E, BF16>(p.acc[idx] + v);
+    v[0] = p.part[idx];
+    for (int s = 1; s < p.ksplit; ++s) v[0] += p.part[s * slice + idx];
   }
+  E* __restrict__ out = reinterpret_cast<E*>(p.out);
+  if (p.epi == kEpiAccFirst || p.epi == kEpiAccMid) {
+    if (p.epi == kEpiAccMid) {
+#pragma unroll
+      for (int q = 0; q < V; ++q) v[q] = p.acc[idx + q] + v[q];
+    }
+#pragma unroll
+    for (int q = 0; q < V; ++q) p.acc[idx + q] = v[q];
+    return;
+  }
+  if (p.epi == kEpiAccLast) {
+#pragma unroll
+    for (int q = 0; q < V; ++q) v[q] = p.acc[idx + q] + v[q];
+  }
+  if constexpr (V == 4 && sizeof(E) == 2) {
+    uint2 o;
+    o.x = uint32_t(from_f32<E, BF16>(v[0])) | (uint32_t(from_f32<E, BF16>(v[1])) << 16);
+    o.y = uint32_t(from_f32<E, BF16>(v[2])) | (uint32_t(from_f32<E, BF16>(v[3])) << 16);
+    *reinterpret_cast<uint2*>(out + idx) = o;
+  } else if constexpr (V == 4) {
+    *reinterpret_cast<float4*>(out + idx) = make_float4(v[0], v[1], v[2], v[3]);
+  } else {
+    out[idx] = from_f32<E, BF16>(v[0]);
+  }
+}
+
+template <typename E, bool BF16>
+hipError_t launch_reduce(const GemmParams& p, hipStream_t s) {
+  const auto aligned = [](const void* q, uintptr_t a) { return (reinterpret_cast<uintptr_t>(q) % a) == 0; };
+  const bool v4 = p.N % 4 == 0 && p.ldc % 4 == 0 && aligned(p.part, 16) &&
+                  (p.epi == kEpiAccFirst || p.epi == kEpiAccMid || aligned(p.out, 4 * sizeof(E))) &&
+                  (p.acc == nullptr || aligned(p.acc, 16));
+  const int64_t threads = p.M * (v4 ? p.N / 4 : p.N);
+  const dim3 grid{unsigned((threads + 255) / 256), 1u, 1u};
+  const bool narrow = threads + 256 < (int64_t(1) << 32);
+  if (v4) {
+    if (narrow) hipLaunchKernelGGL((splitk_reduce_kernel<E, BF16, 4, true>), grid, dim3(256), 0, s, p);
+    else hipLaunchKernelGGL((splitk_reduce_kernel<E, BF16, 4, false>), grid, dim3(256), 0, s, p);
+  } else {
+    if (narrow) hipLaunchKernelGGL((splitk_reduce_kernel<E, BF16, 1, true>), grid, dim3(256), 0, s, p);
+    else hipLaunchKernelGGL((splitk_reduce_kernel<E, BF16, 1, false>), grid, dim3(256), 0, s, p);
+  }
+  return hipGetLastError();
 }
 
 template <class Cfg, bool BF16>
@@ -498,14 +549,9 @@ int splitk_reduce_launch(const GemmParams& p, void* stream) {
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (p.M <= 0 || p.N <= 0) return hipSuccess;
   if (p.ksplit < 2 || !p.part) return hipErrorInvalidValue;
-  const dim3 grid(unsigned((p.M * p.N + 255) / 256));
-  if (p.dtype == CNHWC_F32)
-    hipLaunchKernelGGL((splitk_reduce_kernel<float, false>), grid, dim3(256), 0, s, p);
-  else if (p.dtype == CNHWC_F16)
-    hipLaunchKernelGGL((splitk_reduce_kernel<uint16_t, false>), grid, dim3(256), 0, s, p);
-  else
-    hipLaunchKernelGGL((splitk_reduce_kernel<uint16_t, true>), grid, dim3(256), 0, s, p);
-  return hipGetLastError();
+  if (p.dtype == CNHWC_F32) return launch_reduce<float, false>(p, s);
+  if (p.dtype == CNHWC_F16) return launch_reduce<uint16_t, false>(p, s);
+  return launch_reduce<uint16_t, true>(p, s);
 }
 
 int gemm_launch(const GemmParams& p, void* stream) {
