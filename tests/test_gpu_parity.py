@@ -561,9 +561,12 @@ def test_conv1d_parity(spec):
 # Each replay must give the eager bits; eager work runs between replays.
 
 def test_graph_capture_replays_bit_identical():
-    cases = [  # (fn, case, kwargs): split-K implicit GEMM, native 3D, Winograd, half Winograd 2D/3D
+    cases = [  # (fn, case, kwargs): split-K implicit GEMM, native 3D, Winograd, half Winograd 2D/3D,
+        # and the persistent patch-staged GEMM with more tiles than CUs
         (cn.conv2d, cw.ConvCase("g_l4", 1, 7, 7, 512, 512, 3, 3, (1, 1), (1, 1), (1, 1), "f16",
                                 "normal", "normal", None, 61, 1), {}),
+        (cn.conv2d, cw.ConvCase("g_patch", 70, 32, 32, 64, 96, 3, 3, (1, 1), (1, 1), (1, 1), "f16",
+                                "normal", "normal", None, 66, 6), {"algo": "implicit_gemm", "gemm_config": 16}),
         (cn.conv3d, cw.ConvCase("g_3d", 2, 8, 9, 64, 48, 3, 3, (1, 1, 1), (1, 1, 1), (1, 1, 1), "bf16",
                                 "normal", "normal", None, 62, 2, nd=3, d=5, kd=3), {}),
         (cn.conv2d, cw.ConvCase("g_wino", 2, 30, 30, 64, 64, 3, 3, (1, 1), (1, 1), (1, 1), "f32",
