@@ -183,7 +183,7 @@ __global__ __launch_bounds__(256) void wino_output_kernel(const float* __restric
   for (int b = 0; b < 8; ++b) {
     float col[8];
 #pragma unroll
-    for (int a = 0; a < 8; ++a) col[a] = src[(a * 8 + b) * plane];
+    for (int a = 0; a < 8; ++a) col[a] = __builtin_nontemporal_load(src + (a * 8 + b) * plane);  // read once
     float res[6];
     cmatvec(kWinoAT, col, res);
 #pragma unroll
