@@ -370,12 +370,14 @@ def test_patch_tile_accumulating_epilogue(dtype):
 # several tiles, loading the next tile's patch and first weight stages during
 # its current tile's last (depth tap, chunk) iteration.  One iteration per
 # tile (C = 64, KD = 1), odd iteration counts, two column tiles, ragged
-# blocks, 3D depth taps and the accumulating epilogues; a seeded sample of
-# output pixels (with every pixel of the first and last blocks) against the
-# oracle, every output written (the buffer starts as NaN) and the same bits
-# on every run.
+# blocks, whole tiles only, 3D depth taps and the accumulating epilogues; a
+# seeded sample of output pixels (with every pixel of the first and last
+# blocks) against the oracle, every output written (the buffer starts as NaN)
+# and the same bits on every run.
 PERSIST_CASES = [  # name, n, d, h, w, c, o, kd, pad, dtype, algo
     ("c64_nit1", 70, 1, 32, 32, 64, 96, 0, (1, 1), "f16", "implicit_gemm"),
+    ("c64_o512_whole_tiles", 40, 1, 32, 32, 64, 512, 0, (1, 1), "f16", "implicit_gemm"),
+    ("c128_o256_whole_tiles", 72, 1, 32, 32, 128, 256, 0, (1, 1), "bf16", "implicit_gemm"),
     ("c192_o300_ragged", 24, 1, 33, 35, 192, 300, 0, (1, 1), "bf16", "implicit_gemm"),
     ("video_kd3", 1, 20, 64, 64, 128, 64, 3, (0, 1, 1), "bf16", "implicit_gemm"),
     ("small_kd_acc", 1, 19, 64, 64, 64, 72, 3, (0, 1, 1), "f16", "small_kd"),
