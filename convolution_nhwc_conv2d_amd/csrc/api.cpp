@@ -88,7 +88,9 @@ cnhwc_status_t run_wino_h(const cnhwc_conv_desc_t& d, const cnhwc_plan_t& p, con
   q.K = L.ku;
   q.lda = L.cs;
   q.b = U;
-  q.ldb = L.ku;
+  // K-chunk-major U: O rows of 32 elements per chunk, one chunk plane after another
+  q.ldb = 32;
+  q.b_kstep = d.o * 32;
   q.out = Mt;  // not written with kEpiAccFirst
   q.acc = Mt;
   q.ldc = d.o;

@@ -564,9 +564,12 @@ int gemm_launch(const GemmParams& p, void* stream) {
                        p.kchunk <= 0 || p.kchunk % gemm_config_bk(p.config) != 0 ||
                        (p.ksplit - 1) * p.kchunk >= p.K))
     return hipErrorInvalidValue;
-  // segmented dense A: the 256-row tiles only
-  if ((p.a_seg_len != 0 || p.a_seg_jump != 0) && p.config != kCfgH_256x256 &&
-      p.config != kCfgH_256x128L)
+  // segmented or K-chunk-major dense A: the 256-row tiles only
+  if ((p.a_seg_len != 0 || p.a_seg_jump != 0 || p.a_kstep != 0 || p.b_kstep != 0) &&
+      p.config != kCfgH_256x256 && p.config != kCfgH_256x128L)
+    return hipErrorInvalidValue;
+  if ((p.a_kstep != 0 || p.b_kstep != 0) &&
+      (p.a_mode != kADense || (p.a_kstep != 0 && p.lda != 32) || (p.b_kstep != 0 && p.ldb != 32)))
     return hipErrorInvalidValue;
   switch (p.config) {
     case kCfgF32_N32: return launch_cfg<TileCfg<128, 32, 32, 32, false, 2>, false>(p, s);

@@ -267,6 +267,10 @@ __global__ __launch_bounds__(kThreads, T::OCC) void gemm_lds_kernel(const GemmPa
   // segmented dense A: K position within the segment, and the row shift of
   // the segments passed so far (a_seg_len == 0 never wraps)
   int64_t seg_k = 0, seg_off = 0;
+  // dense operands: element offset of the next chunk (row-major: k_next;
+  // K-chunk-major: chunk index x a_kstep / b_kstep)
+  const int64_t a_step = p.a_kstep ? p.a_kstep : kBK, b_step = p.b_kstep ? p.b_kstep : kBK;
+  int64_t a_k = 0, b_k = 0;
   const gvec_ptr zero = gvec(&g_lds_zero16);
 
   const uint32_t ring_a = lds_base(ring_a_obj<T>()) + wave * (kLoadsA * 64 * 16);
@@ -314,18 +318,20 @@ __global__ __launch_bounds__(kThreads, T::OCC) void gemm_lds_kernel(const GemmPa
       const bool k_in = k_next + kin < K;
 #pragma unroll
       for (int j = 0; j < kLoadsA; ++j) {
-        const gvec_ptr src = (a_off[j] >= 0 && k_in) ? gvec(A + a_off[j] + k_next + seg_off) : zero;
+        const gvec_ptr src = (a_off[j] >= 0 && k_in) ? gvec(A + a_off[j] + a_k + seg_off) : zero;
         __builtin_amdgcn_global_load_lds(src, lds_addr(sa + j * (64 * 16)), 16, 0, 0);
       }
 #pragma unroll
       for (int j = 0; j < kLoadsB; ++j) {
-        const gvec_ptr src = (b_off[j] >= 0 && k_in) ? gvec(B + b_off[j] + k_next) : zero;
+        const gvec_ptr src = (b_off[j] >= 0 && k_in) ? gvec(B + b_off[j] + b_k) : zero;
         __builtin_amdgcn_global_load_lds(src, lds_addr(sb + j * (64 * 16)), 16, 0, 0);
       }
       seg_k += kBK;
       const bool sw = seg_k == p.a_seg_len;
       seg_k = sw ? 0 : seg_k;
       seg_off += sw ? p.a_seg_jump : 0;
+      a_k += a_step;
+      b_k += b_step;
     }
     k_next += kBK;
   };
@@ -613,8 +619,9 @@ bool gemm_lds_ok(const GemmParams& p) {
   if (((p.M + kBM - 1) / kBM) * ((p.N + bn - 1) / bn) * p.batch >= (int64_t(1) << 31)) return false;
   if (p.K % 8 != 0 || p.ldb % 8 != 0) return false;
   if (p.a_seg_len < 0 || p.a_seg_len % 32 != 0) return false;  // a chunk never straddles segments
+  if (p.a_kstep % 8 != 0 || p.b_kstep % 8 != 0) return false;  // 16-byte pieces stay aligned
   if (p.a_mode == kADense) return p.lda % 8 == 0 && p.a_seg_jump % 8 == 0;
-  if (p.a_seg_len != 0) return false;
+  if (p.a_seg_len != 0 || p.a_kstep != 0 || p.b_kstep != 0) return false;
   return p.c % 32 == 0;  // a chunk never straddles two taps
 }
 

@@ -113,6 +113,13 @@ struct GemmParams {
   // depth taps: segment kd reads the rows kd * dd frames further on.
   int64_t a_seg_len;     // multiple of the 32-element K chunk
   int64_t a_seg_jump;
+  // K-chunk-major dense operands (256-row tiles, dense A only; 0: row-major).
+  // With lda = 32, the 32-element K chunk q of row m sits at
+  // a[q * a_kstep + m * 32 + k % 32] (plus the segment jumps), and likewise
+  // for B with ldb = 32 and b_kstep: a chunk of 16 consecutive rows is then
+  // 1 KB of whole 128-byte lines instead of half of each of 16 lines.
+  int64_t a_kstep;
+  int64_t b_kstep;
 };
 
 int gemm_launch(const GemmParams& p, void* stream);  // returns hipError_t
@@ -162,7 +169,8 @@ int gemm_lds_launch(const GemmParams& p, void* stream);  // returns hipError_t
 // elements, 1: w of nw).
 int wino_h_absmax_launch(int dtype, const void* x, int64_t nx, const void* w, int64_t nw,
                          uint32_t* partial, void* stream);
-// U[p][o][kd*cs + c] = fp16(G (sw g) G^T)_p, g = w[o][kd][kh][kw][c] (KD = kd planes);
+// U[p][k / 32][o][k % 32] = fp16(G (sw g) G^T)_p for k = kd*cs + c (K-chunk-major),
+// g = w[o][kd][kh][kw][c] (KD = kd planes);
 // the scales come from the partial maxima, and scales = {sx, sw, a, b} with
 // a b = 1/(sx sw) is stored for the transforms that follow.  wm[k*o + oc]:
 // bit kh*3 + kw set iff some channel of tap (kh, kw) of slice (oc, k) is nonzero.

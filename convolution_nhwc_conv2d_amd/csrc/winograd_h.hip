@@ -25,8 +25,8 @@
 //
 // Workspace (elements): partial maxima, then the scales {sx, sw} and 1/(sx sw)
 // as two powers of two,
-//   U [36][O][KD*Cs]    fp16, Cs = C rounded up to 32 (zero channels)
-//   V [36][rows][Cs]    fp16, rows = (image or frame) * tiles, frames padded by pd
+//   U [36][KD*Cs/32][O][32]   fp16, Cs = C rounded up to 32 (zero channels)
+//   V [36][rows][Cs]          fp16, rows = (image or frame) * tiles, frames padded by pd
 //   M [36][rows'][O]    fp32, rows' = output images or frames * tiles
 //   tap masks [KD][O]   nonzero 3x3 taps of each (o, kd) filter slice (uint32)
 //   tile masks [rows][P] nonzero pixels of each 6x6 input tile, in parts
@@ -34,6 +34,13 @@
 // wino_mask.hpp); in 3D an output's window spans the KD frames its taps read.
 // Tile (ty, tx) covers input rows 4 ty - ph .. +5 and columns 4 tx - pw .. +5
 // and produces output rows 4 ty .. 4 ty + 3 (cropped).
+// U is K-chunk-major: each position's plane holds its 32-element K chunks one
+// after another, each as O rows of 32 elements (64 bytes), so the GEMM's load
+// of one chunk for 16 consecutive filter rows reads 1 KB of whole 128-byte
+// lines; row-major rows would give each load half of each of 16 lines and
+// bring every line into the vector L1 twice.  V stays row-major: written
+// K-chunk-major, the input transform's stores (one tile's 64-byte pieces in
+// eight chunk planes per wavefront) cost more than its GEMM loads gain.
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
@@ -203,7 +210,7 @@ __global__ __launch_bounds__(256) void wino_h_filter_kernel(const uint16_t* __re
     for (int i = 0; i < kT; ++i) t1[i][b] = res[i];
   }
   const int64_t plane = O * ku;
-  uint16_t* __restrict__ out = U + o * ku + r;
+  uint16_t* __restrict__ out = U + (r >> 5) * (O * 32) + o * 32 + (r & 31);  // K-chunk-major
 #pragma unroll
   for (int i = 0; i < kT; ++i) {
     const float row[3] = {t1[i][0], t1[i][1], t1[i][2]};
