@@ -457,17 +457,35 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const GemmParams p) 
   const int64_t col = int64_t(t - row * nv) * V;
   const int64_t idx = int64_t(row) * p.ldc + col;
   const int64_t slice = p.M * p.ldc;
+  // The slices' loads go out kGroup at a time and are then added in slice
+  // order, so a thread waits for one load latency per group, not per slice.
+  constexpr int kGroup = 8;
   float v[V];
   if constexpr (V == 4) {
     const float4 a = *reinterpret_cast<const float4*>(p.part + idx);
     v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-    for (int s = 1; s < p.ksplit; ++s) {
-      const float4 b = *reinterpret_cast<const float4*>(p.part + s * slice + idx);
-      v[0] += b.x; v[1] += b.y; v[2] += b.z; v[3] += b.w;
+    for (int s0 = 1; s0 < p.ksplit; s0 += kGroup) {
+      float4 b[kGroup];
+#pragma unroll
+      for (int j = 0; j < kGroup; ++j)
+        if (s0 + j < p.ksplit) b[j] = *reinterpret_cast<const float4*>(p.part + (s0 + j) * slice + idx);
+#pragma unroll
+      for (int j = 0; j < kGroup; ++j)
+        if (s0 + j < p.ksplit) {
+          v[0] += b[j].x; v[1] += b[j].y; v[2] += b[j].z; v[3] += b[j].w;
+        }
     }
   } else {
     v[0] = p.part[idx];
-    for (int s = 1; s < p.ksplit; ++s) v[0] += p.part[s * slice + idx];
+    for (int s0 = 1; s0 < p.ksplit; s0 += kGroup) {
+      float b[kGroup];
+#pragma unroll
+      for (int j = 0; j < kGroup; ++j)
+        if (s0 + j < p.ksplit) b[j] = p.part[(s0 + j) * slice + idx];
+#pragma unroll
+      for (int j = 0; j < kGroup; ++j)
+        if (s0 + j < p.ksplit) v[0] += b[j];
+    }
   }
   E* __restrict__ out = reinterpret_cast<E*>(p.out);
   if (p.epi == kEpiAccFirst || p.epi == kEpiAccMid) {
