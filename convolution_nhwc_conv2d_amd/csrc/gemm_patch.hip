@@ -442,8 +442,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_patch_kernel(const GemmParam
     static_assert(4 * 32 * kEpRowB <= kPatchBytes, "the epilogue rows fit one patch buffer");
     float* e32 = reinterpret_cast<float*>(g_patch + int((gi - 1) & 1) * kPatchBytes + wave * (32 * kEpRowB));
     const int rl = el >> 3, cl = (el & 7) * 8;
-    auto round = [&](auto i_c, auto jp_c) {  // compile-time indices into acc
+    // WHOLE: the tile lies inside the output (all of its pixels and 256
+    // channels), the 16-byte path applies and the epilogue stores y, so the
+    // stores need no per-lane tests.
+    auto round = [&](auto i_c, auto jp_c, auto whole_c) {  // compile-time indices into acc
       constexpr int i = decltype(i_c)::value, jp = decltype(jp_c)::value;
+      constexpr bool WHOLE = decltype(whole_c)::value;
+      const int ep_k = WHOLE ? int(kEpiStore) : epi;
 #pragma unroll
       for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
@@ -463,12 +468,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_patch_kernel(const GemmParam
         const int trow = wm * 128 + i * 32 + rr;  // row of the tile: pixel (trow / BW, trow % BW)
         const int64_t oh = cur.oh0 + trow / BW, ow = cur.ow0 + trow % BW;
         const int64_t col = int64_t(cur.n0) + wn * 128 + 64 * jp + cl;
-        if (oh >= OH || ow >= OW || col >= N) continue;
+        if (!WHOLE && (oh >= OH || ow >= OW || col >= N)) continue;
         const int64_t idx = ((int64_t(cur.f) * OH + oh) * OW + ow) * p.ldc + col;
-        if (vec && col + 8 <= N) {
-          if (epi == kEpiAccFirst || epi == kEpiAccMid) {
+        if (WHOLE || (vec && col + 8 <= N)) {
+          if (ep_k == kEpiAccFirst || ep_k == kEpiAccMid) {
             float4* dst = reinterpret_cast<float4*>(accbuf + idx);
-            if (epi == kEpiAccMid) {
+            if (ep_k == kEpiAccMid) {
               const float4 a0 = dst[0], a1 = dst[1];
               v[0] += a0.x; v[1] += a0.y; v[2] += a0.z; v[3] += a0.w;
               v[4] += a1.x; v[5] += a1.y; v[6] += a1.z; v[7] += a1.w;
@@ -476,7 +481,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_patch_kernel(const GemmParam
             dst[0] = make_float4(v[0], v[1], v[2], v[3]);
             dst[1] = make_float4(v[4], v[5], v[6], v[7]);
           } else {
-            if (epi == kEpiAccLast) {
+            if (ep_k == kEpiAccLast) {
               const float4* src = reinterpret_cast<const float4*>(accbuf + idx);
               const float4 a0 = src[0], a1 = src[1];
               v[0] = a0.x + v[0]; v[1] = a0.y + v[1]; v[2] = a0.z + v[2]; v[3] = a0.w + v[3];
@@ -506,14 +511,20 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_patch_kernel(const GemmParam
         }
       }
     };
-    round(ic<0>{}, ic<0>{});
-    round(ic<0>{}, ic<1>{});
-    round(ic<1>{}, ic<0>{});
-    round(ic<1>{}, ic<1>{});
-    round(ic<2>{}, ic<0>{});
-    round(ic<2>{}, ic<1>{});
-    round(ic<3>{}, ic<0>{});
-    round(ic<3>{}, ic<1>{});
+    auto rounds = [&](auto whole_c) {
+      round(ic<0>{}, ic<0>{}, whole_c);
+      round(ic<0>{}, ic<1>{}, whole_c);
+      round(ic<1>{}, ic<0>{}, whole_c);
+      round(ic<1>{}, ic<1>{}, whole_c);
+      round(ic<2>{}, ic<0>{}, whole_c);
+      round(ic<2>{}, ic<1>{}, whole_c);
+      round(ic<3>{}, ic<0>{}, whole_c);
+      round(ic<3>{}, ic<1>{}, whole_c);
+    };
+    if (vec && epi == kEpiStore && cur.oh0 + BH <= OH && cur.ow0 + BW <= OW && int64_t(cur.n0) + 256 <= N)
+      rounds(std::true_type{});
+    else
+      rounds(std::false_type{});
     if (!nx) break;
     cur = ng;
   }
