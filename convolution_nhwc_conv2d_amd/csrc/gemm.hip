@@ -416,30 +416,41 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_kernel(const GemmParams p) {
   // a K split stores its fp32 partial sums to its own slice (epilogue later)
   float* __restrict__ partbuf = split ? p.part + int64_t(blockIdx.z) * M * p.ldc : nullptr;
   const int epi = split ? -1 : p.epi;
+  // EPI: the epilogue kind when fixed at compile time (-2: read epi).  WHOLE:
+  // the tile lies inside M x N, so no element needs a bounds test.
+  auto store_tile = [&](auto epi_c, auto whole_c) {
+    constexpr int EPI = decltype(epi_c)::value;
+    constexpr bool WHOLE = decltype(whole_c)::value;
+    const int ep_k = EPI > -2 ? EPI : epi;
 #pragma unroll
-  for (int i = 0; i < FM; ++i)
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < FN; ++j)
+      for (int j = 0; j < FN; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t row = m0 + wm * WM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-        const int64_t col = n0 + wn * WN + j * 32 + (lane & 31);
-        if (row < M && col < N) {
-          const int64_t idx = row * p.ldc + col;
-          const float v = acc[i][j][r];
-          if (epi < 0) {
-            partbuf[idx] = v;
-          } else if (epi == kEpiStore) {
-            out[idx] = from_f32<E, BF16>(v);
-          } else if (epi == kEpiAccFirst) {
-            accbuf[idx] = v;
-          } else if (epi == kEpiAccMid) {
-            accbuf[idx] = accbuf[idx] + v;
-          } else {
-            out[idx] = from_f32<E, BF16>(accbuf[idx] + v);
+        for (int r = 0; r < 16; ++r) {
+          const int64_t row = m0 + wm * WM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+          const int64_t col = n0 + wn * WN + j * 32 + (lane & 31);
+          if (WHOLE || (row < M && col < N)) {
+            const int64_t idx = row * p.ldc + col;
+            const float v = acc[i][j][r];
+            if (ep_k < 0) {
+              partbuf[idx] = v;
+            } else if (ep_k == kEpiStore) {
+              out[idx] = from_f32<E, BF16>(v);
+            } else if (ep_k == kEpiAccFirst) {
+              accbuf[idx] = v;
+            } else if (ep_k == kEpiAccMid) {
+              accbuf[idx] = accbuf[idx] + v;
+            } else {
+              out[idx] = from_f32<E, BF16>(accbuf[idx] + v);
+            }
           }
         }
-      }
+  };
+  const bool whole = m0 + BM <= M && n0 + BN <= N;
+  if (whole && epi < 0) store_tile(std::integral_constant<int, -1>{}, std::true_type{});
+  else if (whole && epi == kEpiStore) store_tile(std::integral_constant<int, kEpiStore>{}, std::true_type{});
+  else store_tile(std::integral_constant<int, -2>{}, std::false_type{});
 }
 
 // y (or the fp32 accumulator) from the K-split partial slices: the slices are
