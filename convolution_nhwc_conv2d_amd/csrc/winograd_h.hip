@@ -415,35 +415,41 @@ __global__ __launch_bounds__(256) void wino_h_output_kernel(const float* __restr
     }
   }
   const float inv_a = scales[2], inv_b = scales[3];
+  // WHOLE: the tile lies inside the output, so its stores need no bounds tests
+  auto finish = [&](auto whole_c) {
+    constexpr bool WHOLE = decltype(whole_c)::value;
 #pragma unroll
-  for (int i = 0; i < kWinoHM; ++i) {
-    const int64_t oh = ty * kWinoHM + i;
-    float res[VEC][kWinoHM];
+    for (int i = 0; i < kWinoHM; ++i) {
+      const int64_t oh = ty * kWinoHM + i;
+      float res[VEC][kWinoHM];
 #pragma unroll
-    for (int v = 0; v < VEC; ++v) {
-      cmatvec(kWino4AT, t1[v][i], res[v]);  // Y[i][j]
+      for (int v = 0; v < VEC; ++v) {
+        cmatvec(kWino4AT, t1[v][i], res[v]);  // Y[i][j]
 #pragma unroll
-      for (int j = 0; j < kWinoHM; ++j)
-        res[v][j] = (hits[v] >> (i * kT + j)) & 1u ? (res[v][j] * inv_a) * inv_b : 0.0f;  // exact
-    }
-    if (oh < OH) {
+        for (int j = 0; j < kWinoHM; ++j)
+          res[v][j] = (hits[v] >> (i * kT + j)) & 1u ? (res[v][j] * inv_a) * inv_b : 0.0f;  // exact
+      }
+      if (WHOLE || oh < OH) {
 #pragma unroll
-      for (int j = 0; j < kWinoHM; ++j) {
-        const int64_t ow = tx * kWinoHM + j;
-        if (ow < OW) {
-          uint16_t* dst = y + ((im * OH + oh) * OW + ow) * O + o;
-          // y is written once and not read here again: stream it past the caches
-          if constexpr (VEC == 2) {
-            const uint32_t q = uint32_t(from_f32<uint16_t, BF16>(res[0][j])) |
-                               (uint32_t(from_f32<uint16_t, BF16>(res[1][j])) << 16);
-            __builtin_nontemporal_store(q, reinterpret_cast<uint32_t*>(dst));
-          } else {
-            __builtin_nontemporal_store(from_f32<uint16_t, BF16>(res[0][j]), dst);
+        for (int j = 0; j < kWinoHM; ++j) {
+          const int64_t ow = tx * kWinoHM + j;
+          if (WHOLE || ow < OW) {
+            uint16_t* dst = y + ((im * OH + oh) * OW + ow) * O + o;
+            // y is written once and not read here again: stream it past the caches
+            if constexpr (VEC == 2) {
+              const uint32_t q = uint32_t(from_f32<uint16_t, BF16>(res[0][j])) |
+                                 (uint32_t(from_f32<uint16_t, BF16>(res[1][j])) << 16);
+              __builtin_nontemporal_store(q, reinterpret_cast<uint32_t*>(dst));
+            } else {
+              __builtin_nontemporal_store(from_f32<uint16_t, BF16>(res[0][j]), dst);
+            }
           }
         }
       }
     }
-  }
+  };
+  if (ty * kWinoHM + kWinoHM <= OH && tx * kWinoHM + kWinoHM <= OW) finish(std::true_type{});
+  else finish(std::false_type{});
 }
 
 inline unsigned blocks_for(int64_t total) { return unsigned((total + 255) / 256); }
