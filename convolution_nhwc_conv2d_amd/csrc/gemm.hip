@@ -593,7 +593,7 @@ int gemm_launch(const GemmParams& p, void* stream) {
                        p.kchunk <= 0 || p.kchunk % gemm_config_bk(p.config) != 0 ||
                        (p.ksplit - 1) * p.kchunk >= p.K))
     return hipErrorInvalidValue;
-  // segmented or K-chunk-major dense A: the 256-row tiles only
+  // segmented A or K-chunk-major operands: the 256-row tiles only
   if ((p.a_seg_len != 0 || p.a_seg_jump != 0 || p.a_kstep != 0 || p.b_kstep != 0) &&
       p.config != kCfgH_256x256 && p.config != kCfgH_256x128L)
     return hipErrorInvalidValue;
